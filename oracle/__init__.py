@@ -1,0 +1,201 @@
+"""ctypes view of the plain C oracle (``q4k_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(``gemm_q4_super_block_amd``) never imports it and has no CPU fallback.
+
+All arrays are numpy; results are fp64.  See ``q4k_oracle.h`` for what each
+function computes and which page passage it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def lib():
+    """Load liboracle.so, compiling it first only if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        L.oracle_f16_to_f64.restype = ctypes.c_double
+        L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_bf16_to_f64.restype = ctypes.c_double
+        L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_silu.restype = ctypes.c_double
+        L.oracle_silu.argtypes = [ctypes.c_double]
+        L.oracle_quant.restype = ctypes.c_int
+        L.oracle_quant.argtypes = [_u8p, ctypes.c_int]
+        L.oracle_unpack_scales.restype = None
+        L.oracle_unpack_scales.argtypes = [_u8p, _u8p, _u8p]
+        L.oracle_dequant_block.restype = None
+        L.oracle_dequant_block.argtypes = [_u8p, _f32p]
+        L.oracle_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
+        L.oracle_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
+        L.oracle_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
+        L.oracle_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
+                                       _f64p, _f64p]
+        L.oracle_gemm.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _f64p, _f64p]
+        L.oracle_gemm_cols.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _i64p, _i64,
+                                       _f64p, _f64p]
+        L.oracle_swiglu_mlp.argtypes = [_u8p, _u8p, _u8p, _f32p, _i64, _i64,
+                                        _f64p, _f64p, _f64p, _f64p, _f64p, _f64p,
+                                        _f64p]
+        for name in ("oracle_dequant_f32", "oracle_dequant_bf16", "oracle_gemv",
+                     "oracle_gemv_rows", "oracle_gemm", "oracle_gemm_cols",
+                     "oracle_swiglu_mlp"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("oracle: %s rejected its arguments" % what)
+
+
+def f16_to_f64(bits: int) -> float:
+    return lib().oracle_f16_to_f64(int(bits))
+
+
+def f32_to_bf16(x: float) -> int:
+    return lib().oracle_f32_to_bf16(float(x))
+
+
+def bf16_to_f64(bits: int) -> float:
+    return lib().oracle_bf16_to_f64(int(bits))
+
+
+def silu(t: float) -> float:
+    return lib().oracle_silu(float(t))
+
+
+def quant(qs: np.ndarray, i: int) -> int:
+    qs = _c(qs, np.uint8)
+    assert qs.size == 128
+    return lib().oracle_quant(_p(qs, _u8p), int(i))
+
+
+def unpack_scales(s: np.ndarray):
+    s = _c(s, np.uint8)
+    assert s.size == 12
+    sc = np.zeros(8, np.uint8)
+    mn = np.zeros(8, np.uint8)
+    lib().oracle_unpack_scales(_p(s, _u8p), _p(sc, _u8p), _p(mn, _u8p))
+    return sc, mn
+
+
+def dequant_block(blk: np.ndarray) -> np.ndarray:
+    blk = _c(blk, np.uint8)
+    assert blk.size == 144
+    w = np.zeros(256, np.float32)
+    lib().oracle_dequant_block(_p(blk, _u8p), _p(w, _f32p))
+    return w
+
+
+def dequant_f32(w: np.ndarray, n: int, k: int) -> np.ndarray:
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * 144
+    out = np.zeros((n, k), np.float32)
+    _check(lib().oracle_dequant_f32(_p(w, _u8p), n, k, _p(out, _f32p)), "dequant_f32")
+    return out
+
+
+def dequant_bf16(w: np.ndarray, n: int, k: int) -> np.ndarray:
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * 144
+    out = np.zeros((n, k), np.uint16)
+    _check(lib().oracle_dequant_bf16(_p(w, _u8p), n, k, _p(out, _u16p)), "dequant_bf16")
+    return out
+
+
+def gemv(w: np.ndarray, x: np.ndarray, n: int, k: int):
+    """y, a = oracle GEMV; x is fp32 [m, k] (or [k]); returns fp64 [m, n]."""
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32).reshape(-1, k)
+    m = x.shape[0]
+    y = np.zeros((m, n), np.float64)
+    a = np.zeros((m, n), np.float64)
+    _check(lib().oracle_gemv(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(y, _f64p),
+                             _p(a, _f64p)), "gemv")
+    return y, a
+
+
+def gemv_rows(w: np.ndarray, x: np.ndarray, n: int, k: int, rows):
+    """Oracle GEMV restricted to output columns ``rows``; returns [m, len(rows)]."""
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32).reshape(-1, k)
+    rows = _c(rows, np.int64)
+    m = x.shape[0]
+    y = np.zeros((m, rows.size), np.float64)
+    a = np.zeros((m, rows.size), np.float64)
+    _check(lib().oracle_gemv_rows(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(rows, _i64p),
+                                  rows.size, _p(y, _f64p), _p(a, _f64p)), "gemv_rows")
+    return y, a
+
+
+def gemm(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int):
+    """Y, A = oracle GEMM with X bf16 bits [m, k]; returns fp64 [m, n]."""
+    w = _c(w, np.uint8)
+    x = _c(x_bf16, np.uint16).reshape(-1, k)
+    m = x.shape[0]
+    y = np.zeros((m, n), np.float64)
+    a = np.zeros((m, n), np.float64)
+    _check(lib().oracle_gemm(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(y, _f64p),
+                             _p(a, _f64p)), "gemm")
+    return y, a
+
+
+def gemm_cols(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int, cols):
+    """Oracle GEMM restricted to output columns ``cols``; returns [m, len(cols)]."""
+    w = _c(w, np.uint8)
+    x = _c(x_bf16, np.uint16).reshape(-1, k)
+    cols = _c(cols, np.int64)
+    m = x.shape[0]
+    y = np.zeros((m, cols.size), np.float64)
+    a = np.zeros((m, cols.size), np.float64)
+    _check(lib().oracle_gemm_cols(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(cols, _i64p),
+                                  cols.size, _p(y, _f64p), _p(a, _f64p)), "gemm_cols")
+    return y, a
+
+
+def swiglu_mlp(w_gate, w_up, w_down, x, d_model: int, d_ff: int):
+    """Oracle SwiGLU MLP at one token.  Returns a dict of fp64 arrays:
+    g, ag, u, au, h (length d_ff) and out, aout (length d_model)."""
+    wg = _c(w_gate, np.uint8)
+    wu = _c(w_up, np.uint8)
+    wd = _c(w_down, np.uint8)
+    x = _c(x, np.float32).reshape(d_model)
+    r = {name: np.zeros(d_ff, np.float64) for name in ("g", "ag", "u", "au", "h")}
+    r["out"] = np.zeros(d_model, np.float64)
+    r["aout"] = np.zeros(d_model, np.float64)
+    _check(lib().oracle_swiglu_mlp(
+        _p(wg, _u8p), _p(wu, _u8p), _p(wd, _u8p), _p(x, _f32p), d_model, d_ff,
+        _p(r["g"], _f64p), _p(r["ag"], _f64p), _p(r["u"], _f64p), _p(r["au"], _f64p),
+        _p(r["h"], _f64p), _p(r["out"], _f64p), _p(r["aout"], _f64p)), "swiglu_mlp")
+    return r

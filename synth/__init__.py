@@ -1,0 +1,73 @@
+"""Seeded synthetic inputs for the Q4_K linear layer.
+
+This module is shared by the tests, the smoke check and the benchmark, on both
+sides of every parity check (the HIP path and the oracle).  It holds none of
+the method's arithmetic: it never decodes a block, never dequantizes and never
+multiplies a weight.  It only draws bytes and numbers.
+
+Distributions (the workload of the pages: 4-bit quants uniform in 0..15,
+6-bit sub-block scales and mins uniform in 0..63, fp16 super-block scales
+d and dmin = |N(0,1)| * 0.01, activations N(0,1)):
+
+* A super-block is 144 bytes: fp16 ``d`` at byte 0, fp16 ``dmin`` at byte 2,
+  then 12 scale bytes and 128 quant bytes.  The 140 scale and quant bytes are
+  drawn uniformly from 0..255.  Every bit of them is then an independent fair
+  coin, so *any* 6-bit field is uniform in 0..63 and any 4-bit field uniform
+  in 0..15 -- whatever packing a reader applies.  The generator therefore
+  needs no knowledge of how the scales are packed.
+* ``d`` and ``dmin`` are |N(0,1)| * 0.01 drawn in fp64 and rounded to fp16
+  (round to nearest even, numpy's conversion).  About 0.5% of them land in
+  the fp16 subnormal range; they are kept.
+* Activations are fp32 N(0,1); bf16 activations are the fp32 draw rounded to
+  bf16 (round to nearest even, torch's conversion).
+
+Random streams come from numpy's PCG64 seeded with ``SeedSequence([seed,
+stream])``, so every tensor of a case has its own independent stream and a
+case is reproducible from ``seed`` alone.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+QK = 256            # weights per super-block
+BLOCK_BYTES = 144   # bytes per super-block
+
+# stream ids: one per tensor role, so cases never share draws
+W, X, W_GATE, W_UP, W_DOWN = 0, 1, 2, 3, 4
+
+
+def rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(stream)])))
+
+
+def q4k_weights(n: int, k: int, seed: int = 0, stream: int = W,
+                scale: float = 0.01) -> np.ndarray:
+    """Random Q4_K matrix W [n, k] as uint8 [n, (k/256)*144] (row-major blocks)."""
+    if k % QK:
+        raise ValueError("k must be a multiple of 256")
+    nb = n * (k // QK)
+    g = rng(seed, stream)
+    blocks = np.empty((nb, BLOCK_BYTES), np.uint8)
+    d = (np.abs(g.standard_normal(nb)) * scale).astype(np.float16)
+    dmin = (np.abs(g.standard_normal(nb)) * scale).astype(np.float16)
+    blocks[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    blocks[:, 2:4] = dmin.view(np.uint8).reshape(nb, 2)
+    blocks[:, 4:] = g.integers(0, 256, size=(nb, BLOCK_BYTES - 4), dtype=np.uint8)
+    return blocks.reshape(n, (k // QK) * BLOCK_BYTES)
+
+
+def normal_f32(shape, seed: int = 0, stream: int = X) -> np.ndarray:
+    """fp32 N(0,1) array."""
+    return rng(seed, stream).standard_normal(shape, dtype=np.float32)
+
+
+def bf16_bits(x_f32: np.ndarray) -> np.ndarray:
+    """Round an fp32 array to bf16 (nearest even) and return the uint16 bits."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x_f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def normal_bf16(shape, seed: int = 0, stream: int = X) -> np.ndarray:
+    """bf16 bits of fp32 N(0,1) draws."""
+    return bf16_bits(normal_f32(shape, seed, stream))
