@@ -1,0 +1,233 @@
+// k_gemm.hip -- prefill GEMM Y = X W^T on Q4_K weights with bf16 MFMA.
+//
+// The tile GEMM of the prefill shape ("Writing an ESIMD Fused Kernel From
+// Reverse-Engineered Assembly", "SLM-Tiled GEMM and Graph Recording": a
+// shared-memory tiled GEMM; the PR page "CPU kernel parity ..." pairs each
+// decode kernel with a tile kernel for prompt processing).  The Q4_K scale
+// changes every 32 weights along K, so it cannot be folded into an output
+// epilogue: each weight tile is dequantized before the contraction.
+//
+// Design for gfx950:
+//   * workgroup = 4 waves, tile BM x BN with BN = 128 weight rows; waves are
+//     arranged WAVES_M x WAVES_N, each owning (32*TI) x (32*TJ) outputs as
+//     TI x TJ accumulators of v_mfma_f32_32x32x16_bf16.
+//   * K advances 64 weights per step = one quant group of one super-block
+//     (32 low nibbles of sub-block 2g, 32 high nibbles of 2g+1).
+//   * W tile: each of the 256 threads loads the block header and 16 quant
+//     bytes of one row, dequantizes 32 weights to bf16 (round to nearest
+//     even of the exact fp32 weight) and writes them to LDS; the tile is
+//     double-buffered, one barrier per step.
+//   * X fragments go straight from global memory into MFMA operand layout:
+//     a 16-byte load per lane per K16 slice, no LDS pass.  Within a 64-wide
+//     step lane half h and slice kk hold physical k = 32h + 8kk + (0..7) for
+//     both operands (the MFMA sums over k, so any common assignment is the
+//     same contraction); a lane therefore reads 64 contiguous bytes of its X
+//     row per step.
+//   * optional split-K over blockIdx.z accumulates with fp32 atomics into a
+//     zeroed Y (used when the output tile count cannot fill 256 CUs).
+#include <hip/hip_runtime.h>
+
+#include "q4k_device.h"
+#include "q4k_launch.h"
+
+namespace q4k {
+namespace {
+
+typedef float f16x_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBN = 128;       // weight rows per tile
+constexpr int kBK = 64;        // weights per K step (one quant group)
+constexpr int kLdsStride = 72; // bf16 per LDS row: 64 + 8 pad (144 B rows)
+
+template <int WAVES_M, int WAVES_N, int TI, int TJ>
+__global__ __launch_bounds__(256) void k_gemm_q4k(const uint8_t* __restrict__ w,
+                                                  const uint16_t* __restrict__ x,
+                                                  float* __restrict__ y, int m, int n, int k,
+                                                  int steps_per_split, int atomic_out) {
+  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  static_assert(WAVES_N * 32 * TJ == kBN, "the tile fill covers 128 weight rows");
+  constexpr int BM = WAVES_M * 32 * TI;
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][kBN * kLdsStride];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int half = lane >> 5;
+  const int m0 = blockIdx.y * BM;
+  const int n0 = blockIdx.x * kBN;
+  const int kb_count = k >> 8;
+  const int steps = k / kBK;
+  const int s_begin = blockIdx.z * steps_per_split;
+  const int s_end = min(steps, s_begin + steps_per_split);
+  if (s_begin >= s_end) return;  // uniform over the workgroup, before any barrier
+
+  // Tile-fill role: weight row f_row of the tile, 16-byte half f_hh of the group.
+  const int f_row = t >> 1;
+  const int f_hh = t & 1;
+  const uint8_t* f_base =
+      w + static_cast<size_t>(min(n0 + f_row, n - 1)) * kb_count * kBlockBytes;
+
+  // A-operand role: rows of X this lane feeds (clamped; clamped rows are not stored).
+  const uint16_t* a_ptr[TI];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int row = min(m0 + wm * 32 * TI + 32 * i + (lane & 31), m - 1);
+    a_ptr[i] = x + static_cast<size_t>(row) * k + 32 * half;
+  }
+
+  f16x_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto load_w = [&](int s, uint4& hd, uint4& q) {
+    const uint8_t* p = f_base + static_cast<size_t>(s >> 2) * kBlockBytes;
+    hd = load16(p);
+    q = load16(p + 16 + 32 * (s & 3) + 16 * f_hh);
+  };
+  auto store_w = [&](int buf, int s, const uint4& hd, const uint4& q) {
+    const GroupScales sc = group_scales(hd, s & 3);
+    uint32_t lo8[8], hi8[8];
+    dequant16_bf16(q, sc, lo8, hi8);
+    uint16_t* dst = &ws[buf][f_row * kLdsStride + 16 * f_hh];
+    *reinterpret_cast<uint4*>(dst) = make_uint4(lo8[0], lo8[1], lo8[2], lo8[3]);
+    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(lo8[4], lo8[5], lo8[6], lo8[7]);
+    *reinterpret_cast<uint4*>(dst + 32) = make_uint4(hi8[0], hi8[1], hi8[2], hi8[3]);
+    *reinterpret_cast<uint4*>(dst + 40) = make_uint4(hi8[4], hi8[5], hi8[6], hi8[7]);
+  };
+  auto load_x = [&](int s, uint4 (&xr)[TI][4]) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const uint16_t* p = a_ptr[i] + static_cast<size_t>(s) * kBK;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xr[i][c] = *reinterpret_cast<const uint4*>(p + 8 * c);
+    }
+  };
+
+  uint4 hd, q;
+  uint4 xa[TI][4];
+  load_w(s_begin, hd, q);
+  load_x(s_begin, xa);
+  store_w(0, s_begin, hd, q);
+  __syncthreads();
+
+  int buf = 0;
+  for (int s = s_begin; s < s_end; ++s) {
+    const bool more = s + 1 < s_end;
+    uint4 xn[TI][4];
+    if (more) {
+      load_w(s + 1, hd, q);
+      load_x(s + 1, xn);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8_t bfr[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int nrow = wn * 32 * TJ + 32 * j + (lane & 31);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&ws[buf][nrow * kLdsStride + 32 * half + 8 * kk]);
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, xa[i][kk]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (more) store_w(buf ^ 1, s + 1, hd, q);
+    __syncthreads();
+    buf ^= 1;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xa[i][c] = xn[i][c];
+    }
+  }
+
+  // Accumulator r of a 32x32 tile holds row 8*(r/4) + 4*half + r%4, column lane%32.
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int col = n0 + wn * 32 * TJ + 32 * j + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 32 * TI + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (row < m && col < n) {
+          float* dst = y + static_cast<size_t>(row) * n + col;
+          if (atomic_out) {
+            unsafeAtomicAdd(dst, acc[i][j][r]);
+          } else {
+            *dst = acc[i][j][r];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Zero fill for split-K outputs (a kernel, not a memset node, so that a
+// captured graph replays it faithfully).
+__global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ y, size_t count) {
+  const size_t i = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i + 4 <= count) {
+    *reinterpret_cast<f4_t*>(y + i) = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  } else {
+    for (size_t j = i; j < count; ++j) y[j] = 0.0f;
+  }
+}
+
+template <int WAVES_M, int WAVES_N, int TI, int TJ>
+hipError_t launch(const uint8_t* w, const uint16_t* x, float* y, int m, int n, int k,
+                  int splits_wanted, hipStream_t stream) {
+  constexpr int BM = WAVES_M * 32 * TI;
+  const int tiles_m = (m + BM - 1) / BM;
+  const int tiles_n = (n + kBN - 1) / kBN;
+  const int steps = k / kBK;
+  int splits = splits_wanted < 1 ? 1 : splits_wanted;
+  if (splits > steps) splits = steps;
+  const int per = (steps + splits - 1) / splits;
+  splits = (steps + per - 1) / per;
+  if (splits > 1) {
+    const size_t count = static_cast<size_t>(m) * n;
+    const size_t grid = (count / 4 + 256) / 256;
+    hipLaunchKernelGGL(k_zero_f32, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, y,
+                       count);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_gemm_q4k<WAVES_M, WAVES_N, TI, TJ>), dim3(tiles_n, tiles_m, splits),
+                     dim3(256), 0, stream, w, x, y, m, n, k, per, splits > 1 ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Split K until the grid reaches one workgroup per CU (256 on MI355X).
+int splits_for(int tiles, int steps) {
+  int s = 1;
+  while (tiles * s * 2 <= 256 && s * 2 <= steps / 8) s *= 2;
+  return s;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                       int64_t k, hipStream_t stream) {
+  const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
+  const int steps = ki / kBK;
+  const int tiles_n = (ni + kBN - 1) / kBN;
+  if (mi <= 32) {
+    // Small batch: one 32-row slice, the four waves split the 128 weight rows.
+    return launch<1, 4, 1, 1>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
+  }
+  const int tiles = ((mi + 255) / 256) * tiles_n;
+  return launch<4, 1, 2, 4>(w, x, y, mi, ni, ki, splits_for(tiles, steps), stream);
+}
+
+}  // namespace q4k

@@ -1,0 +1,215 @@
+// q4k_api.hip -- the extern "C" boundary of libq4k (declared in include/q4k.h).
+//
+// Validates arguments on the host (before anything touches the device),
+// checks the device once per device id, then enqueues the kernels on the
+// caller's stream.  Conventions follow the C API described on the
+// "xpu-kernels" page, sections "Use from C" and "API": int status codes, a
+// last-error string, an init call, int64 sizes, stream-taking entry points.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/q4k.h"
+#include "q4k_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return Q4K_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 unusable
+char g_device_name[kMaxDevices][64];
+
+int check_device() {
+  int dev = -1;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(Q4K_ERR_DEVICE, "no HIP device is visible");
+  }
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(Q4K_ERR_DEVICE, "cannot query the current HIP device");
+  }
+  int st = g_device_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(Q4K_ERR_DEVICE, "cannot read the properties of device %d", dev);
+    }
+    snprintf(g_device_name[dev], sizeof g_device_name[dev], "%s", p.gcnArchName);
+    st = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_device_state[dev].store(st, std::memory_order_release);
+  }
+  if (st != 1) {
+    return fail(Q4K_ERR_DEVICE, "device %d is %s; libq4k is built for gfx950 only", dev,
+                g_device_name[dev]);
+  }
+  return Q4K_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges)?
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool valid_k(int64_t k) { return k >= 256 && k % 256 == 0 && k <= INT32_MAX; }
+
+size_t q4k_bytes(int64_t rows, int64_t k) {
+  return static_cast<size_t>(rows) * static_cast<size_t>(k / 256) * 144u;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    return fail(Q4K_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4k_version(void) { return 100; }  // 0.1.0
+
+int q4k_init(void) {
+  const int rc = check_device();
+  return rc == Q4K_OK ? ok() : rc;
+}
+
+const char* q4k_device_name(void) {
+  const std::string saved = g_last_error;  // a query leaves the last error alone
+  (void)check_device();
+  g_last_error = saved;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices ||
+      g_device_name[dev][0] == 0) {
+    (void)hipGetLastError();
+    return "none";
+  }
+  return g_device_name[dev];
+}
+
+const char* q4k_last_error(void) { return g_last_error.c_str(); }
+
+int q4k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (!w || !x || !y) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: null pointer");
+  if (m < 1 || m > Q4K_GEMV_MAX_M)
+    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: m=%lld outside 1..%d", (long long)m,
+                Q4K_GEMV_MAX_M);
+  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: n=%lld", (long long)n);
+  if (!valid_k(k))
+    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: k=%lld is not a positive multiple of 256",
+                (long long)k);
+  if (!aligned16(w) || !aligned16(x) || !aligned16(y))
+    return fail(Q4K_ERR_ALIGN, "q4k_gemv: w, x and y must be 16-byte aligned");
+  const size_t ny = static_cast<size_t>(m * n) * 4;
+  if (overlap(y, ny, x, static_cast<size_t>(m * k) * 4) || overlap(y, ny, w, q4k_bytes(n, k)))
+    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: y overlaps an input");
+  if (int rc = check_device()) return rc;
+  return launched(q4k::launch_gemv(static_cast<const uint8_t*>(w), x, y, m, n, k,
+                                   static_cast<hipStream_t>(stream)),
+                  "q4k_gemv");
+}
+
+int q4k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (!w || !x_bf16 || !y) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: null pointer");
+  if (m < 1 || m > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: m=%lld", (long long)m);
+  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: n=%lld", (long long)n);
+  if (!valid_k(k))
+    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: k=%lld is not a positive multiple of 256",
+                (long long)k);
+  if (!aligned16(w) || !aligned16(x_bf16) || !aligned16(y))
+    return fail(Q4K_ERR_ALIGN, "q4k_gemm: w, x and y must be 16-byte aligned");
+  const size_t ny = static_cast<size_t>(m) * static_cast<size_t>(n) * 4;
+  if (overlap(y, ny, x_bf16, static_cast<size_t>(m) * static_cast<size_t>(k) * 2) ||
+      overlap(y, ny, w, q4k_bytes(n, k)))
+    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: y overlaps an input");
+  if (int rc = check_device()) return rc;
+  return launched(q4k::launch_gemm(static_cast<const uint8_t*>(w), x_bf16, y, m, n, k,
+                                   static_cast<hipStream_t>(stream)),
+                  "q4k_gemm");
+}
+
+int q4k_swiglu_mlp(const void* w_gate, const void* w_up, const void* w_down, const float* x,
+                   float* h, float* out, int64_t d_model, int64_t d_ff, void* stream) {
+  if (!w_gate || !w_up || !w_down || !x || !h || !out)
+    return fail(Q4K_ERR_INVALID_ARG, "q4k_swiglu_mlp: null pointer");
+  if (!valid_k(d_model) || !valid_k(d_ff))
+    return fail(Q4K_ERR_INVALID_ARG,
+                "q4k_swiglu_mlp: d_model=%lld and d_ff=%lld must be positive multiples of 256",
+                (long long)d_model, (long long)d_ff);
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(x) ||
+      !aligned16(h) || !aligned16(out))
+    return fail(Q4K_ERR_ALIGN, "q4k_swiglu_mlp: all pointers must be 16-byte aligned");
+  const size_t nh = static_cast<size_t>(d_ff) * 4, no = static_cast<size_t>(d_model) * 4;
+  const size_t nw = q4k_bytes(d_ff, d_model);
+  if (overlap(h, nh, x, no) || overlap(h, nh, w_gate, nw) || overlap(h, nh, w_up, nw) ||
+      overlap(h, nh, w_down, nw) || overlap(out, no, x, no) || overlap(out, no, h, nh) ||
+      overlap(out, no, w_gate, nw) || overlap(out, no, w_up, nw) || overlap(out, no, w_down, nw))
+    return fail(Q4K_ERR_INVALID_ARG, "q4k_swiglu_mlp: h or out overlaps another buffer");
+  if (int rc = check_device()) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = q4k::launch_gateup_swiglu(static_cast<const uint8_t*>(w_gate),
+                                           static_cast<const uint8_t*>(w_up), x, h, d_model,
+                                           d_ff, s);
+  if (e != hipSuccess) return launched(e, "q4k_swiglu_mlp (gate/up)");
+  e = q4k::launch_gemv(static_cast<const uint8_t*>(w_down), h, out, 1, d_model, d_ff, s);
+  return launched(e, "q4k_swiglu_mlp (down)");
+}
+
+static int dequant_checks(const char* what, const void* w, const void* out, int64_t n,
+                          int64_t k, size_t elem) {
+  if (!w || !out) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
+  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
+  if (!valid_k(k))
+    return fail(Q4K_ERR_INVALID_ARG, "%s: k=%lld is not a positive multiple of 256", what,
+                (long long)k);
+  if (!aligned16(w) || !aligned16(out))
+    return fail(Q4K_ERR_ALIGN, "%s: w and out must be 16-byte aligned", what);
+  if (overlap(out, static_cast<size_t>(n) * static_cast<size_t>(k) * elem, w, q4k_bytes(n, k)))
+    return fail(Q4K_ERR_INVALID_ARG, "%s: out overlaps w", what);
+  return check_device();
+}
+
+int q4k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k, void* stream) {
+  if (int rc = dequant_checks("q4k_dequantize_f32", w, out, n, k, 4)) return rc;
+  return launched(q4k::launch_dequant_f32(static_cast<const uint8_t*>(w), out, n, k,
+                                          static_cast<hipStream_t>(stream)),
+                  "q4k_dequantize_f32");
+}
+
+int q4k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k, void* stream) {
+  if (int rc = dequant_checks("q4k_dequantize_bf16", w, out, n, k, 2)) return rc;
+  return launched(q4k::launch_dequant_bf16(static_cast<const uint8_t*>(w), out, n, k,
+                                           static_cast<hipStream_t>(stream)),
+                  "q4k_dequantize_bf16");
+}
+
+}  // extern "C"

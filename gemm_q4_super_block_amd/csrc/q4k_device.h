@@ -1,0 +1,145 @@
+// q4k_device.h -- gfx950 device routines that decode Q4_K super-blocks.
+//
+// Shared by every kernel of libq4k (GEMV, gate/up SwiGLU, GEMM tile fill,
+// diagnostic dequant) so that all of them read the format the same way.
+//
+// Format (Q4_K as read by the library; the pages -- "Writing an ESIMD Fused
+// Kernel From Reverse-Engineered Assembly", "Getting Q4_K Right" -- name the
+// super-block, its 6-bit sub-block scales and mins and a quant-to-weight
+// "y-offset mapping", but print no layout):
+//   144 bytes = 16-byte header + 128 quant bytes, 256 weights.
+//   header dword 0: d (fp16, bits 0..15), dmin (fp16, bits 16..31)
+//   header dwords 1..3: scale bytes s[0..11]
+//   quant group g (bytes 32g .. 32g+31): low nibble of byte 32g+r is weight
+//   64g+r (sub-block 2g), high nibble is weight 64g+32+r (sub-block 2g+1).
+//   w = d*sc[j]*q - dmin*mn[j].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4k {
+
+constexpr int kQK = 256;          // weights per super-block
+constexpr int kBlockBytes = 144;  // bytes per super-block
+
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// A byte 0000qqqq read as an OCP fp8 e4m3 value is q * 2^-9 exactly: codes
+// 0..7 are the subnormals q * 2^-9 and codes 8..15 are (1 + (q-8)/8) * 2^-6
+// = q * 2^-9.  gfx950 converts two such bytes to fp32 in one instruction, so
+// nibbles are widened with the scale 2^-9 folded into the sub-block scale.
+constexpr float kNibbleUnscale = 512.0f;
+
+__device__ __forceinline__ f2_t fp8x2_lo(uint32_t v) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v), false);
+}
+__device__ __forceinline__ f2_t fp8x2_hi(uint32_t v) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v), true);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+// Scales of the two sub-blocks that quant group g feeds: 2g (low nibbles) and
+// 2g+1 (high nibbles).  a = d*sc*2^9 multiplies an fp8-widened nibble, b =
+// dmin*mn is subtracted.  All four products are exact in fp32 (an fp16 value
+// times a 6-bit integer, times a power of two).
+struct GroupScales {
+  float a_lo, a_hi, b_lo, b_hi;
+};
+
+__device__ __forceinline__ GroupScales group_scales(uint4 h, int g) {
+  // Per-byte 6-bit fields: bytes 0..3 of each word are sub-blocks 0..3 (lo)
+  // or 4..7 (hi).
+  const uint32_t sc_lo = h.y & 0x3F3F3F3Fu;
+  const uint32_t mn_lo = h.z & 0x3F3F3F3Fu;
+  const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+  const uint32_t mn_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+  const int sh = (g & 1) * 16;
+  const uint32_t sc = (g < 2 ? sc_lo : sc_hi) >> sh;
+  const uint32_t mn = (g < 2 ? mn_lo : mn_hi) >> sh;
+  const float d = half_bits_to_float(h.x & 0xFFFFu) * kNibbleUnscale;
+  const float dmin = half_bits_to_float(h.x >> 16);
+  GroupScales s;
+  s.a_lo = d * static_cast<float>(sc & 0xFFu);
+  s.a_hi = d * static_cast<float>((sc >> 8) & 0xFFu);
+  s.b_lo = dmin * static_cast<float>(mn & 0xFFu);
+  s.b_hi = dmin * static_cast<float>((mn >> 8) & 0xFFu);
+  return s;
+}
+
+// Dequantize one quant dword (4 bytes = 4 low-nibble weights of sub-block 2g
+// and 4 high-nibble weights of sub-block 2g+1) to fp32.  fma(a, q*2^-9, -b)
+// rounds the exact d*sc*q - dmin*mn once, so the result is bit-identical to
+// any correctly rounded evaluation.
+__device__ __forceinline__ void dequant_dword(uint32_t v, const GroupScales& s, float lo[4],
+                                              float hi[4]) {
+  const uint32_t l = v & 0x0F0F0F0Fu;
+  const uint32_t h = (v >> 4) & 0x0F0F0F0Fu;
+  const f2_t l01 = fp8x2_lo(l), l23 = fp8x2_hi(l);
+  const f2_t h01 = fp8x2_lo(h), h23 = fp8x2_hi(h);
+  lo[0] = __builtin_fmaf(s.a_lo, l01.x, -s.b_lo);
+  lo[1] = __builtin_fmaf(s.a_lo, l01.y, -s.b_lo);
+  lo[2] = __builtin_fmaf(s.a_lo, l23.x, -s.b_lo);
+  lo[3] = __builtin_fmaf(s.a_lo, l23.y, -s.b_lo);
+  hi[0] = __builtin_fmaf(s.a_hi, h01.x, -s.b_hi);
+  hi[1] = __builtin_fmaf(s.a_hi, h01.y, -s.b_hi);
+  hi[2] = __builtin_fmaf(s.a_hi, h23.x, -s.b_hi);
+  hi[3] = __builtin_fmaf(s.a_hi, h23.y, -s.b_hi);
+}
+
+// Round two fp32 values to bf16 (nearest even, v_cvt_pk_bf16_f32) and pack
+// them: first value in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f2_t v = {a, b};
+  const bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Dequantize 16 quant bytes of group g (one 16-byte load) to bf16: lo8[0..7]
+// are the 16 low-nibble weights (sub-block 2g) as 8 packed pairs, hi8[0..7]
+// the 16 high-nibble weights (sub-block 2g+1).  This is the GEMM's LDS fill
+// and the bf16 diagnostic export.
+__device__ __forceinline__ void dequant16_bf16(uint4 q, const GroupScales& s, uint32_t lo8[8],
+                                               uint32_t hi8[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo[4], hi[4];
+    dequant_dword(w[i], s, lo, hi);
+    lo8[2 * i + 0] = pack_bf16x2(lo[0], lo[1]);
+    lo8[2 * i + 1] = pack_bf16x2(lo[2], lo[3]);
+    hi8[2 * i + 0] = pack_bf16x2(hi[0], hi[1]);
+    hi8[2 * i + 1] = pack_bf16x2(hi[2], hi[3]);
+  }
+}
+
+__device__ __forceinline__ uint4 load16(const uint8_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Sum of a float over the 64 lanes of a wave (every lane gets the total).
+// Within a row of 16 lanes: DPP quad_perm xor-1 and xor-2, then row_ror 4
+// and 8; across the four rows: two lane swizzles through the LDS crossbar.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x124>(v);  // row_ror 4
+  v += dpp_mov<0x128>(v);  // row_ror 8
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+}  // namespace q4k

@@ -1,0 +1,31 @@
+// q4k_launch.h -- host-side launchers of the libq4k kernels (internal).
+//
+// Each launcher enqueues on `stream` and returns the HIP status of the
+// launch.  Arguments are validated by the C ABI (q4k_api.hip) beforehand:
+// k % 256 == 0, sizes fit in int32, pointers 16-byte aligned.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4k {
+
+// Shipped launch shapes (pinned by tests/test_abi.py).
+constexpr int kGemvRowsPerWave = 4;    // decode GEMV, batch 1: rows of W per wave
+constexpr int kGateUpRowsPerWave = 2;  // gate/up SwiGLU: row pairs per wave
+
+hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                       int64_t k, hipStream_t stream);
+
+hipError_t launch_gateup_swiglu(const uint8_t* w_gate, const uint8_t* w_up, const float* x,
+                                float* h, int64_t d_model, int64_t d_ff, hipStream_t stream);
+
+hipError_t launch_dequant_f32(const uint8_t* w, float* out, int64_t n, int64_t k,
+                              hipStream_t stream);
+hipError_t launch_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64_t k,
+                               hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                       int64_t k, hipStream_t stream);
+
+}  // namespace q4k

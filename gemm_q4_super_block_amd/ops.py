@@ -1,0 +1,97 @@
+"""torch-facing wrappers over the libq4k C ABI (argument marshalling only).
+
+PyTorch provides device memory and the current stream; every computation runs
+in libq4k's HIP kernels.  Weights are ``torch.uint8`` tensors holding raw Q4_K
+super-blocks, shape ``[n, (k // 256) * 144]``.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import Q4K_BLOCK_BYTES, Q4K_QK, check
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _q4k_shape(w: torch.Tensor):
+    if w.dtype != torch.uint8 or w.dim() != 2 or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("Q4_K weights must be a contiguous CUDA uint8 tensor [n, k/256*144]")
+    n, row_bytes = w.shape
+    if row_bytes % Q4K_BLOCK_BYTES:
+        raise ValueError("row length %d is not a whole number of 144-byte blocks" % row_bytes)
+    return n, (row_bytes // Q4K_BLOCK_BYTES) * Q4K_QK
+
+
+def _dev_tensor(t: torch.Tensor, dtype, what: str) -> torch.Tensor:
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous CUDA %s tensor" % (what, dtype))
+    return t
+
+
+def gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x W^T for fp32 x [k] or [m, k] (m <= 32); returns fp32 [n] or [m, n]."""
+    n, k = _q4k_shape(w)
+    _dev_tensor(x, torch.float32, "x")
+    squeeze = x.dim() == 1
+    x2 = x.view(1, -1) if squeeze else x
+    if x2.dim() != 2 or x2.shape[1] != k:
+        raise ValueError("x has shape %s, expected [..., %d]" % (tuple(x.shape), k))
+    m = x2.shape[0]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _dev_tensor(y, torch.float32, "out")
+    check(_lib.q4k_gemv(w.data_ptr(), x2.data_ptr(), y.data_ptr(), m, n, k, _stream(w.device)))
+    return y.view(n) if squeeze else y
+
+
+def gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W^T for bf16 X [m, k]; returns fp32 [m, n]."""
+    n, k = _q4k_shape(w)
+    _dev_tensor(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x has shape %s, expected [m, %d]" % (tuple(x.shape), k))
+    m = x.shape[0]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _dev_tensor(y, torch.float32, "out")
+    check(_lib.q4k_gemm(w.data_ptr(), x.data_ptr(), y.data_ptr(), m, n, k, _stream(w.device)))
+    return y
+
+
+def swiglu_mlp(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+               x: torch.Tensor, h: torch.Tensor | None = None,
+               out: torch.Tensor | None = None):
+    """out = W_down (silu(W_gate x) * (W_up x)) at one token; returns (out, h)."""
+    d_ff, d_model = _q4k_shape(w_gate)
+    if _q4k_shape(w_up) != (d_ff, d_model) or _q4k_shape(w_down) != (d_model, d_ff):
+        raise ValueError("gate/up must be [d_ff, d_model] and down [d_model, d_ff]")
+    _dev_tensor(x, torch.float32, "x")
+    if x.numel() != d_model:
+        raise ValueError("x must have d_model = %d elements" % d_model)
+    if h is None:
+        h = torch.empty(d_ff, dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty(d_model, dtype=torch.float32, device=x.device)
+    _dev_tensor(h, torch.float32, "h")
+    _dev_tensor(out, torch.float32, "out")
+    check(_lib.q4k_swiglu_mlp(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(),
+                              x.data_ptr(), h.data_ptr(), out.data_ptr(), d_model, d_ff,
+                              _stream(x.device)))
+    return out, h
+
+
+def dequantize_f32(w: torch.Tensor) -> torch.Tensor:
+    """Dequantized W as fp32 [n, k]."""
+    n, k = _q4k_shape(w)
+    out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    check(_lib.q4k_dequantize_f32(w.data_ptr(), out.data_ptr(), n, k, _stream(w.device)))
+    return out
+
+
+def dequantize_bf16(w: torch.Tensor) -> torch.Tensor:
+    """Dequantized W as bf16 [n, k] (nearest-even rounding of the fp32 weight)."""
+    n, k = _q4k_shape(w)
+    out = torch.empty((n, k), dtype=torch.bfloat16, device=w.device)
+    check(_lib.q4k_dequantize_bf16(w.data_ptr(), out.data_ptr(), n, k, _stream(w.device)))
+    return out

@@ -1,0 +1,138 @@
+/*
+ * q4k.h -- C ABI of libq4k: the linear layer of LLM inference computed
+ * directly on Q4_K block-quantized weights, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what is computed, by page title and section:
+ *   [P1] "Writing an ESIMD Fused Kernel From Reverse-Engineered Assembly":
+ *        "Getting Q4_K Right" (Q4_K dequantization fused into a dot product),
+ *        "Building ESIMD Infrastructure" (the MUL_MAT + MUL_MAT + SWIGLU MLP
+ *        fusion), "SLM-Tiled GEMM and Graph Recording" (a shared-memory tiled
+ *        GEMM for the prefill shape).
+ *   [P2] "xpu-kernels -- fused kernels for Intel Arc (Xe2) ...": "Use from C"
+ *        and "API" (int status codes, a last-error string, an init call,
+ *        int64 sizes, entry points that enqueue on the caller's stream).
+ *   [P3] "CPU kernel parity: decode and tile kernels at llama.cpp speed ..."
+ *        (daScript PR page): the decode (GEMV) and tile (prefill) kernel
+ *        split; "Validation" (every kernel bit-exact against the reference
+ *        decode).
+ *
+ * Q4_K super-block (the pages name it and its 6-bit sub-block scales and
+ * mins but print no byte layout; this is the layout the library reads):
+ *   144 bytes encode 256 weights = 8 sub-blocks of 32.
+ *     bytes 0..1    d     fp16, little-endian: multiplies the 6-bit scales
+ *     bytes 2..3    dmin  fp16, little-endian: multiplies the 6-bit mins
+ *     bytes 4..15   s[12] eight 6-bit scales sc[0..7] and eight 6-bit mins
+ *                   mn[0..7]: for j < 4, sc[j] = s[j] & 63, mn[j] =
+ *                   s[j+4] & 63; for j >= 4, sc[j] = (s[j+4] & 15) |
+ *                   (s[j-4] >> 6) << 4 and mn[j] = (s[j+4] >> 4) |
+ *                   (s[j] >> 6) << 4
+ *     bytes 16..143 qs[128] 4-bit quants: in group g = 0..3, the low nibble
+ *                   of qs[32g + r] is weight 64g + r and its high nibble is
+ *                   weight 64g + 32 + r (r = 0..31)
+ *   weight i = d * sc[i/32] * q_i - dmin * mn[i/32], rounded once to fp32.
+ * A matrix W [n, k] (k a multiple of 256) is n rows of k/256 consecutive
+ * super-blocks, row-major: block b of row r starts at byte (r*k/256 + b)*144.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers on the current HIP device (memory from
+ *     hipMalloc or torch's CUDA allocator); the caller owns all memory.  The
+ *     library allocates, frees and synchronizes nothing on these calls.
+ *   - Calls enqueue asynchronously on `stream` (a hipStream_t; NULL = the
+ *     null stream) and return once the work is enqueued.
+ *   - Sizes are int64; byte offsets are computed in 64 bits.
+ *   - Arguments are validated before anything touches the device; on a
+ *     non-zero return nothing was enqueued and q4k_last_error() holds the
+ *     reason (thread-local, valid until this thread's next call).
+ *   - Outputs must not overlap inputs.
+ */
+#ifndef LIBQ4K_Q4K_H
+#define LIBQ4K_Q4K_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define Q4K_OK 0
+#define Q4K_ERR_INVALID_ARG (-1) /* null pointer, size out of range, k % 256 */
+#define Q4K_ERR_ALIGN (-2)       /* a pointer is not 16-byte aligned */
+#define Q4K_ERR_DEVICE (-3)      /* no HIP device, or it is not gfx950 */
+#define Q4K_ERR_LAUNCH (-4)      /* the HIP runtime rejected a launch */
+
+/* Weights per super-block, bytes per super-block, largest GEMV batch. */
+#define Q4K_QK 256
+#define Q4K_BLOCK_BYTES 144
+#define Q4K_GEMV_MAX_M 32
+
+/* Checks that a HIP device is present and is gfx950, for the current device.
+ * Idempotent and cheap after the first call per device; the compute entry
+ * points call it themselves.  Returns Q4K_OK or Q4K_ERR_DEVICE. [P2 "API":
+ * an explicit init call.] */
+int q4k_init(void);
+
+/* gcnArchName of the current device ("gfx950:sramecc+:xnack-" or similar),
+ * or "none".  The string is owned by the library. [P2 "API".] */
+const char* q4k_device_name(void);
+
+/* Message for the last non-zero return on the calling thread ("" if none).
+ * Owned by the library. [P2 "API": a last-error string.] */
+const char* q4k_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int q4k_version(void);
+
+/* Decode GEMV at batch m (decode step, or a small batch of tokens).
+ *   y[i, j] = sum_c W[j, c] * x[i, c]   for i < m, j < n, c < k.
+ *   w: Q4_K matrix [n, k] (layout above), 16-byte aligned.
+ *   x: fp32 [m, k] row-major, 16-byte aligned.
+ *   y: fp32 [m, n] row-major, 16-byte aligned.
+ *   1 <= m <= Q4K_GEMV_MAX_M, n >= 1, k >= 256 with k % 256 == 0.
+ * The dequantization is fused into an fp32 FMA dot product; each output
+ * lies within 1e-4 * sum_c |W[j,c] x[i,c]| of the exact value.
+ * [P1 "Getting Q4_K Right"; P3 decode kernels.] */
+int q4k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
+             int64_t k, void* stream);
+
+/* Prefill GEMM.
+ *   Y[i, j] = sum_c X[i, c] * W[j, c]   for i < m, j < n  (Y = X W^T).
+ *   w: Q4_K matrix [n, k], 16-byte aligned.
+ *   x_bf16: bf16 bit patterns [m, k] row-major, 16-byte aligned.
+ *   y: fp32 [m, n] row-major, 16-byte aligned.
+ *   m >= 1, n >= 1, k >= 256 with k % 256 == 0.
+ * Weight tiles are dequantized to bf16 (round to nearest even of the fp32
+ * weight) in LDS and contracted on bf16 MFMA with fp32 accumulation; each
+ * output lies within 1e-2 * sum_c |W[j,c] X[i,c]| of the exact value.
+ * [P1 "SLM-Tiled GEMM and Graph Recording"; P3 tile kernels.] */
+int q4k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m,
+             int64_t n, int64_t k, void* stream);
+
+/* SwiGLU MLP at one token (M = 1).
+ *   h   = silu(W_gate x) * (W_up x),  silu(t) = t / (1 + exp(-t))
+ *   out = W_down h
+ *   w_gate, w_up: Q4_K [d_ff, d_model];  w_down: Q4_K [d_model, d_ff].
+ *   x: fp32 [d_model];  h: fp32 [d_ff] (caller-owned scratch, left valid);
+ *   out: fp32 [d_model].  All 16-byte aligned.
+ *   d_model and d_ff: positive multiples of 256.
+ * Gate and up share one read of x and h is formed in registers; the down
+ * projection is a second launch on the same stream (it needs all of h).
+ * [P1 "Building ESIMD Infrastructure": MUL_MAT + MUL_MAT + SWIGLU.] */
+int q4k_swiglu_mlp(const void* w_gate, const void* w_up, const void* w_down,
+                   const float* x, float* h, float* out, int64_t d_model,
+                   int64_t d_ff, void* stream);
+
+/* Diagnostic dequantization of W [n, k] to fp32 / to bf16 bit patterns,
+ * row-major [n, k], through the same device routine the GEMM fills LDS with.
+ * The fp32 result is the exact weight rounded once to nearest even; the bf16
+ * result is that fp32 value rounded to nearest even.  out 16-byte aligned.
+ * [P3 "Validation": bit-exact against the reference decode.] */
+int q4k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k,
+                       void* stream);
+int q4k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBQ4K_Q4K_H */
