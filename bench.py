@@ -1,0 +1,354 @@
+"""Benchmark of the Q4_K linear layer on one MI355X.
+
+One *step* is one pass of the whole hot path over the workload's synthetic
+inputs, each kernel on cold weights:
+  * decode GEMV, W 4096 x 4096 Q4_K, fp32 x (the headline configuration);
+  * small-batch GEMV and GEMM, W 14336 x 4096, M in {1, 2, 4, 8, 16, 32};
+  * SwiGLU MLP at one token: gate/up 14336 x 4096, down 4096 x 14336;
+  * prefill GEMM, X bf16 [512, 4096], W 4096 x 4096 and 14336 x 4096;
+  * the bf16 dequantization export of the 4096 x 4096 matrix.
+Every kernel rotates over copies of its working set totalling >= 576 MB (past
+the 256 MB MALL and the 4 MB L2 per XCD), so each launch reads cold HBM.
+
+Timing: W warm-up steps, then K steps bracketed by a device synchronize.  The
+K launches of one kernel run back to back on the launch stream between two
+HIP events; the per-launch average is that kernel's duration (launch gaps
+included).  ``value`` is the decode GEMV's effective HBM bandwidth
+(algorithmic bytes / average duration).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+COLD_BYTES = 576 << 20         # rotating working set per kernel: over twice the 256 MB MALL
+
+D_MODEL, D_FF = 4096, 14336
+SWEEP_M = (1, 2, 4, 8, 16, 32)
+
+
+def q4k_bytes(n, k):
+    return n * (k // 256) * 144
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the CPU oracle (used for profiler runs)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="approximate CPU time budget for the oracle baseline")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run one device copy of 256 MiB (counter calibration)")
+    p.add_argument("--only", default="",
+                   help="comma list of kernels to run (gemv,sweep_gemv,sweep_gemm,mlp,gemm,dequant)")
+    p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
+    return p.parse_args()
+
+
+class Rotor:
+    """R device copies of a set of host arrays; copy i is used at launch i % R."""
+
+    def __init__(self, torch, arrays, bytes_per_set):
+        import numpy as np
+        self.count = max(1, -(-COLD_BYTES // max(1, bytes_per_set)))
+        base = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in arrays]
+        self.sets = [base]
+        for _ in range(self.count - 1):
+            self.sets.append([t.clone() for t in base])
+
+    def __getitem__(self, i):
+        return self.sets[i % self.count]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
+              "(the path shards by output rows, see DESIGN.md)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemm_q4_super_block_amd as q4k
+    from gemm_q4_super_block_amd import _lib
+    import synth
+
+    only = set(filter(None, args.only.split(",")))
+    want = lambda name: not only or name in only  # noqa: E731
+
+    torch.cuda.set_device(0)
+    q4k.load_library()
+    _lib.check(_lib.q4k_init())
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    dev_name = _lib.q4k_device_name()
+
+    kernels = []  # (name, launch(i), algorithmic bytes, flop)
+
+    # ---- decode GEMV 4096 x 4096
+    if want("gemv"):
+        n = k = D_MODEL
+        w = synth.q4k_weights(n, k, seed=0)
+        x = synth.normal_f32(k, seed=0)
+        nbytes = q4k_bytes(n, k) + 4 * k + 4 * n
+        rot = Rotor(torch, [w, x, np.zeros(n, np.float32)], nbytes)
+
+        def run_gemv(i, rot=rot, n=n, k=k):
+            wd, xd, yd = rot[i]
+            _lib.check(_lib.q4k_gemv(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), 1, n, k, sp))
+        kernels.append(("gemv_4096x4096", run_gemv, nbytes, 2 * n * k, rot))
+
+    # ---- small-batch sweep, W 14336 x 4096
+    if want("sweep_gemv") or want("sweep_gemm"):
+        n, k = D_FF, D_MODEL
+        w = synth.q4k_weights(n, k, seed=0)
+        for m in SWEEP_M:
+            xf = synth.normal_f32((m, k), seed=0)
+            if want("sweep_gemv"):
+                nbytes = q4k_bytes(n, k) + 4 * m * k + 4 * m * n
+                rot = Rotor(torch, [w, xf, np.zeros((m, n), np.float32)], nbytes)
+
+                def run(i, rot=rot, m=m, n=n, k=k):
+                    wd, xd, yd = rot[i]
+                    _lib.check(_lib.q4k_gemv(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
+                kernels.append(("sweep_gemv_m%d" % m, run, nbytes, 2 * m * n * k, rot))
+            if want("sweep_gemm"):
+                xb = synth.bf16_bits(xf)
+                nbytes = q4k_bytes(n, k) + 2 * m * k + 4 * m * n
+                rot = Rotor(torch, [w, xb.view(np.int16), np.zeros((m, n), np.float32)], nbytes)
+
+                def run(i, rot=rot, m=m, n=n, k=k):
+                    wd, xd, yd = rot[i]
+                    _lib.check(_lib.q4k_gemm(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
+                kernels.append(("sweep_gemm_m%d" % m, run, nbytes, 2 * m * n * k, rot))
+
+    # ---- SwiGLU MLP at one token
+    if want("mlp"):
+        wg = synth.q4k_weights(D_FF, D_MODEL, seed=0, stream=synth.W_GATE)
+        wu = synth.q4k_weights(D_FF, D_MODEL, seed=0, stream=synth.W_UP)
+        wdn = synth.q4k_weights(D_MODEL, D_FF, seed=0, stream=synth.W_DOWN)
+        x = synth.normal_f32(D_MODEL, seed=0)
+        nbytes = 3 * q4k_bytes(D_FF, D_MODEL) + 4 * D_MODEL + 2 * 4 * D_FF + 4 * D_MODEL
+        rot = Rotor(torch, [wg, wu, wdn, x, np.zeros(D_FF, np.float32),
+                            np.zeros(D_MODEL, np.float32)], nbytes)
+
+        def run_mlp(i, rot=rot):
+            g, u, d, xd, hd, od = rot[i]
+            _lib.check(_lib.q4k_swiglu_mlp(g.data_ptr(), u.data_ptr(), d.data_ptr(), xd.data_ptr(),
+                                           hd.data_ptr(), od.data_ptr(), D_MODEL, D_FF, sp))
+        kernels.append(("swiglu_mlp_4096_14336", run_mlp, nbytes, 2 * 3 * D_FF * D_MODEL, rot))
+
+    # ---- prefill GEMM, M = 512
+    if want("gemm"):
+        m, k = 512, D_MODEL
+        xb = synth.normal_bf16((m, k), seed=0)
+        for n in (D_MODEL, D_FF):
+            w = synth.q4k_weights(n, k, seed=0)
+            nbytes = q4k_bytes(n, k) + 2 * m * k + 4 * m * n
+            rot = Rotor(torch, [w, xb.view(np.int16), np.zeros((m, n), np.float32)], nbytes)
+
+            def run(i, rot=rot, m=m, n=n, k=k):
+                wd, xd, yd = rot[i]
+                _lib.check(_lib.q4k_gemm(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
+            kernels.append(("gemm_512x%dx4096" % n, run, nbytes, 2 * m * n * k, rot))
+
+    # ---- dequant export (bf16) of the 4096 x 4096 matrix
+    if want("dequant"):
+        n = k = D_MODEL
+        w = synth.q4k_weights(n, k, seed=0)
+        nbytes = q4k_bytes(n, k) + 2 * n * k
+        rot = Rotor(torch, [w, np.zeros((n, k), np.uint16).view(np.int16)], nbytes)
+
+        def run_dq(i, rot=rot, n=n, k=k):
+            wd, od = rot[i]
+            _lib.check(_lib.q4k_dequantize_bf16(wd.data_ptr(), od.data_ptr(), n, k, sp))
+        kernels.append(("dequant_bf16_4096x4096", run_dq, nbytes, 0, rot))
+
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copy probe: 268435456 bytes copied device to device", file=sys.stderr)
+
+    torch.cuda.synchronize()
+    # warm-up
+    for s in range(args.warmup):
+        for _, run, *_ in kernels:
+            run(s)
+    torch.cuda.synchronize()
+
+    # timed region: K steps; each kernel's K launches run back to back between two events
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in kernels]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for (name, run, *_), (e0, e1) in zip(kernels, events):
+        e0.record(stream)
+        for s in range(args.steps):
+            run(args.warmup + s)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {}
+    total_ms = 0.0
+    for (name, run, nbytes, flop, rot), (e0, e1) in zip(kernels, events):
+        ms = e0.elapsed_time(e1)
+        total_ms += ms
+        us = ms * 1e3 / args.steps
+        r = {"us": round(us, 3), "copies": rot.count}
+        if nbytes:
+            r["gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+            r["hbm_frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+        if flop:
+            r["tflops"] = round(flop / (us * 1e-6) / 1e12, 2)
+        if name.startswith("gemm_") or name.startswith("sweep_gemm"):
+            r["mfma_frac"] = round(r["tflops"] / BF16_PEAK_TFLOPS, 4)
+        per[name] = r
+
+    check = None if args.no_check else spot_check(kernels, args, np, torch)
+
+    head = per.get("gemv_4096x4096")
+    gemm = per.get("gemm_512x4096x4096")
+    value = head["gbs"] if head else None
+    cpu = None if args.no_cpu_baseline or not head else cpu_baseline(args, np)
+    crossover = None
+    if all(("sweep_gemv_m%d" % m) in per and ("sweep_gemm_m%d" % m) in per for m in SWEEP_M):
+        crossover = next((m for m in SWEEP_M
+                          if per["sweep_gemm_m%d" % m]["us"] < per["sweep_gemv_m%d" % m]["us"]), None)
+
+    out = {
+        "metric": "Q4_K GEMV eff. HBM GB/s (% of peak); M=512 GEMM TFLOP/s (% MFMA peak)",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_k weights, f32 activations and accumulation (GEMV); bf16 MFMA, f32 acc (GEMM)",
+        "data": "synthetic (seeded; Q4_K fields uniform, d/dmin |N(0,1)|*0.01, activations N(0,1))",
+        "config": {
+            "workload": "decode GEMV y = W x, W 4096 x 4096 Q4_K (9,437,184 B), x/y fp32, "
+                        "cold weights (%d rotating copies)" % (head["copies"] if head else 0),
+            "prefill_gemm": "Y = X W^T, X bf16 [512, 4096], W 4096 x 4096 Q4_K",
+            "mlp": "SwiGLU 4096 -> 14336 -> 4096 at one token",
+            "sweep": "W 14336 x 4096, M in %s" % (list(SWEEP_M),),
+        },
+        "percent_of_peak": {
+            "gemv_hbm": round(100 * head["hbm_frac"], 2) if head else None,
+            "gemm_m512_mfma_bf16": round(100 * gemm["mfma_frac"], 2) if gemm else None,
+        },
+        "gemm_m512_tflops": gemm["tflops"] if gemm else None,
+        "roofline": None,
+        "roofline_gemm": None,
+        "cpu_baseline": cpu,
+        "kernels": per,
+        "sweep_crossover_m": crossover,
+        "parity_spot_check": check,
+        "device": dev_name,
+        "wall_s": round(wall, 3),
+    }
+    if head:
+        out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": head["hbm_frac"], "traffic": traffic("gemv_4096x4096"),
+                           "kernel": "k_gemv_q4k<1,4,false>", "bytes_per_launch": 9469952}
+    if gemm:
+        out["roofline_gemm"] = {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": gemm["mfma_frac"],
+                                "traffic": traffic("gemm_512x4096x4096"),
+                                "kernel": "k_gemm_q4k<4,1,2,4> (+ split-K zero fill)",
+                                "flop_per_launch": 2 * 512 * 4096 * 4096}
+    print(json.dumps(out))
+
+
+def traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        return t.get(name)
+    except (OSError, ValueError):
+        return None
+
+
+def spot_check(kernels, args, np, torch):
+    """Check the last launch of each kernel against the oracle on sampled outputs."""
+    import oracle
+    import synth
+    res = {}
+    last = args.warmup + args.steps - 1
+    for name, run, nbytes, flop, rot in kernels:
+        t = rot[last]
+        if name == "gemv_4096x4096":
+            w, x, y = (a.cpu().numpy() for a in t)
+            rows = np.arange(0, 4096, 37)
+            yr, a = oracle.gemv_rows(w, x, 4096, 4096, rows)
+            res[name] = float((np.abs(y[rows] - yr[0]) / (1e-4 * a[0])).max())
+        elif name.startswith("gemm_512"):
+            w, xb, y = (a.cpu().numpy() for a in t)
+            n = y.shape[1]
+            cols = np.arange(0, n, n // 16)
+            yr, a = oracle.gemm_cols(w, xb.view(np.uint16), n, 4096, cols)
+            res[name] = float((np.abs(y[:, cols] - yr) / (1e-2 * a)).max())
+        elif name == "swiglu_mlp_4096_14336":
+            g, u, d, x, h, o = (a.cpu().numpy() for a in t)
+            yr, a = oracle.gemv(d.reshape(4096, -1), h, 4096, D_FF)
+            res[name + "_down_stage"] = float((np.abs(o - yr[0]) / (1e-4 * a[0])).max())
+    return {"max_err_over_tol": res}
+
+
+def cpu_baseline(args, np):
+    """The oracle's decode GEMV on the same 4096 x 4096 inputs, single-threaded, timed."""
+    import oracle
+    import synth
+    n = k = D_MODEL
+    w = synth.q4k_weights(n, k, seed=0)
+    x = synth.normal_f32(k, seed=0)
+    oracle.gemv(w[:16], x, 16, k)  # load and warm the library
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gemv(w, x, n, k)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds:
+            break
+    per = el / passes
+    nbytes = q4k_bytes(n, k) + 4 * k + 4 * n
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full passes of the oracle decode GEMV (4096 x 4096 Q4_K, fp64 dot) "
+                      "in %.1f s, %.3f s per pass; host %s, %d CPUs visible"
+                      % (passes, el, per, cpu_model, len(os.sched_getaffinity(0)))}
+
+
+if __name__ == "__main__":
+    main()
