@@ -16,7 +16,8 @@
 //   * W tile: each of the 256 threads loads the block header and 16 quant
 //     bytes of one row, dequantizes 32 weights to bf16 (round to nearest
 //     even of the exact fp32 weight) and writes them to LDS; the tile is
-//     double-buffered, one barrier per step.
+//     double-buffered, one barrier per step, and the loads run two steps
+//     ahead of the MFMAs that consume them.
 //   * X fragments go straight from global memory into MFMA operand layout:
 //     a 16-byte load per lane per K16 slice, no LDS pass.  Within a 64-wide
 //     step lane half h and slice kk hold physical k = 32h + 8kk + (0..7) for
@@ -39,11 +40,11 @@ constexpr int kBN = 128;       // weight rows per tile
 constexpr int kBK = 64;        // weights per K step (one quant group)
 constexpr int kLdsStride = 72; // bf16 per LDS row: 64 + 8 pad (144 B rows)
 
-template <int WAVES_M, int WAVES_N, int TI, int TJ>
-__global__ __launch_bounds__(256) void k_gemm_q4k(const uint8_t* __restrict__ w,
-                                                  const uint16_t* __restrict__ x,
-                                                  float* __restrict__ y, int m, int n, int k,
-                                                  int steps_per_split, int atomic_out) {
+template <int WAVES_M, int WAVES_N, int TI, int TJ, int MINB>
+__global__ __launch_bounds__(256, MINB) void k_gemm_q4k(const uint8_t* __restrict__ w,
+                                                        const uint16_t* __restrict__ x,
+                                                        float* __restrict__ y, int m, int n, int k,
+                                                        int steps_per_split, int atomic_out) {
   static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
   static_assert(WAVES_N * 32 * TJ == kBN, "the tile fill covers 128 weight rows");
   constexpr int BM = WAVES_M * 32 * TI;
@@ -85,10 +86,22 @@ __global__ __launch_bounds__(256) void k_gemm_q4k(const uint8_t* __restrict__ w,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // Loads past the last step re-read the last step (results unused) so the
+  // pipeline needs no branches.
   auto load_w = [&](int s, uint4& hd, uint4& q) {
-    const uint8_t* p = f_base + static_cast<size_t>(s >> 2) * kBlockBytes;
+    const int sc = min(s, s_end - 1);
+    const uint8_t* p = f_base + static_cast<size_t>(sc >> 2) * kBlockBytes;
     hd = load16(p);
-    q = load16(p + 16 + 32 * (s & 3) + 16 * f_hh);
+    q = load16(p + 16 + 32 * (sc & 3) + 16 * f_hh);
+  };
+  auto load_x = [&](int s, uint4 (&xr)[TI][4]) {
+    const int sc = min(s, s_end - 1);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const uint16_t* p = a_ptr[i] + static_cast<size_t>(sc) * kBK;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xr[i][c] = *reinterpret_cast<const uint4*>(p + 8 * c);
+    }
   };
   auto store_w = [&](int buf, int s, const uint4& hd, const uint4& q) {
     const GroupScales sc = group_scales(hd, s & 3);
@@ -100,55 +113,51 @@ __global__ __launch_bounds__(256) void k_gemm_q4k(const uint8_t* __restrict__ w,
     *reinterpret_cast<uint4*>(dst + 32) = make_uint4(hi8[0], hi8[1], hi8[2], hi8[3]);
     *reinterpret_cast<uint4*>(dst + 40) = make_uint4(hi8[4], hi8[5], hi8[6], hi8[7]);
   };
-  auto load_x = [&](int s, uint4 (&xr)[TI][4]) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const uint16_t* p = a_ptr[i] + static_cast<size_t>(s) * kBK;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) xr[i][c] = *reinterpret_cast<const uint4*>(p + 8 * c);
-    }
-  };
-
-  uint4 hd, q;
-  uint4 xa[TI][4];
-  load_w(s_begin, hd, q);
-  load_x(s_begin, xa);
-  store_w(0, s_begin, hd, q);
-  __syncthreads();
-
-  int buf = 0;
-  for (int s = s_begin; s < s_end; ++s) {
-    const bool more = s + 1 < s_end;
-    uint4 xn[TI][4];
-    if (more) {
-      load_w(s + 1, hd, q);
-      load_x(s + 1, xn);
-    }
+  auto mfma_step = [&](int buf, const uint4 (&xr)[TI][4]) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8_t bfr[TJ];
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int nrow = wn * 32 * TJ + 32 * j + (lane & 31);
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&ws[buf][nrow * kLdsStride + 32 * half + 8 * kk]);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(
+            &ws[buf][nrow * kLdsStride + 32 * half + 8 * kk]);
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, xa[i][kk]);
+        const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, xr[i][kk]);
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (more) store_w(buf ^ 1, s + 1, hd, q);
+  };
+
+  // Software pipeline, unrolled by two so that no register that a load is
+  // still writing is ever copied (a copy would force a wait on the load):
+  // at step s the MFMAs read LDS buffer s%2 and X registers set s%2, while
+  // the weights of step s+1 are dequantized into the other LDS buffer and the
+  // X fragments of step s+2 and raw weights of step s+2 are fetched.
+  uint4 xA[TI][4], xB[TI][4], hA, qA, hB, qB;
+  load_w(s_begin, hA, qA);
+  load_x(s_begin, xA);
+  load_x(s_begin + 1, xB);
+  store_w(0, s_begin, hA, qA);
+  load_w(s_begin + 1, hB, qB);
+  load_w(s_begin + 2, hA, qA);
+  __syncthreads();
+  for (int s = s_begin; s < s_end; s += 2) {
+    mfma_step(0, xA);
+    load_x(s + 2, xA);
+    if (s + 1 < s_end) store_w(1, s + 1, hB, qB);
+    load_w(s + 3, hB, qB);
     __syncthreads();
-    buf ^= 1;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) xa[i][c] = xn[i][c];
-    }
+    if (s + 1 >= s_end) break;
+    mfma_step(1, xB);
+    load_x(s + 3, xB);
+    if (s + 2 < s_end) store_w(0, s + 2, hA, qA);
+    load_w(s + 4, hA, qA);
+    __syncthreads();
   }
 
   // Accumulator r of a 32x32 tile holds row 8*(r/4) + 4*half + r%4, column lane%32.
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ y, size_t 
   }
 }
 
-template <int WAVES_M, int WAVES_N, int TI, int TJ>
+template <int WAVES_M, int WAVES_N, int TI, int TJ, int MINB>
 hipError_t launch(const uint8_t* w, const uint16_t* x, float* y, int m, int n, int k,
                   int splits_wanted, hipStream_t stream) {
   constexpr int BM = WAVES_M * 32 * TI;
@@ -203,7 +212,7 @@ hipError_t launch(const uint8_t* w, const uint16_t* x, float* y, int m, int n, i
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_gemm_q4k<WAVES_M, WAVES_N, TI, TJ>), dim3(tiles_n, tiles_m, splits),
+  hipLaunchKernelGGL((k_gemm_q4k<WAVES_M, WAVES_N, TI, TJ, MINB>), dim3(tiles_n, tiles_m, splits),
                      dim3(256), 0, stream, w, x, y, m, n, k, per, splits > 1 ? 1 : 0);
   return hipGetLastError();
 }
@@ -224,10 +233,11 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
   const int tiles_n = (ni + kBN - 1) / kBN;
   if (mi <= 32) {
     // Small batch: one 32-row slice, the four waves split the 128 weight rows.
-    return launch<1, 4, 1, 1>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
+    return launch<1, 4, 1, 1, 2>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
   }
-  const int tiles = ((mi + 255) / 256) * tiles_n;
-  return launch<4, 1, 2, 4>(w, x, y, mi, ni, ki, splits_for(tiles, steps), stream);
+  // 128 x 128 tiles, two workgroups per CU.
+  const int tiles = ((mi + 127) / 128) * tiles_n;
+  return launch<4, 1, 1, 4, 2>(w, x, y, mi, ni, ki, splits_for(tiles, steps), stream);
 }
 
 }  // namespace q4k
