@@ -55,6 +55,12 @@ def parse():
     p.add_argument("--only", default="",
                    help="comma list of kernels to run (gemv,sweep_gemv,sweep_gemm,mlp,gemm,dequant)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
+    p.add_argument("--summarize-profile", nargs="+", metavar="DIR",
+                   help="summarize rocprofv3 output directories (kernel trace, then optional "
+                        "FETCH_SIZE and WRITE_SIZE counter runs) instead of benchmarking")
+    p.add_argument("--profile-command", default="", help="command line recorded in the summary")
+    p.add_argument("--out", default="", help="summary output file (markdown)")
+    p.add_argument("--workload-hint", default="", help="the --only value the profiled run used")
     return p.parse_args()
 
 
@@ -75,6 +81,9 @@ class Rotor:
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
               "(the path shards by output rows, see DESIGN.md)" % args.gpus, file=sys.stderr)
@@ -179,12 +188,14 @@ def main():
         kernels.append(("dequant_bf16_4096x4096", run_dq, nbytes, 0, rot))
 
     if args.copy_probe:
+        # one elementwise kernel that reads 256 MiB and writes 256 MiB: the reference
+        # dispatch for scaling the FETCH_SIZE / WRITE_SIZE counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.add(src, 1, out=dst)
         torch.cuda.synchronize()
-        print("copy probe: 268435456 bytes copied device to device", file=sys.stderr)
+        print("copy probe: elementwise kernel read and wrote 268435456 bytes", file=sys.stderr)
 
     torch.cuda.synchronize()
     # warm-up
@@ -280,15 +291,144 @@ def main():
     print(json.dumps(out))
 
 
+KERNEL_SOURCES = ("k_gemv.hip", "k_gemm.hip", "k_dequant.hip", "q4k_device.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gemm_q4_super_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def traffic(name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    try:
-        with open(path) as f:
-            t = json.load(f)
-        return t.get(name)
-    except (OSError, ValueError):
-        return None
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by the
+    elementwise-kernel calibration) for workload `name`, from the summaries in profiles/,
+    or None if none covers it or the kernel sources changed since it was taken."""
+    import glob
+    current = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.startswith("traffic_json: "):
+                        t = json.loads(line[len("traffic_json: "):])
+                        if t.get("source_hash") == current and name in t.get("bytes_per_launch", {}):
+                            return t["bytes_per_launch"][name]
+        except (OSError, ValueError):
+            continue
+    return None
+
+
+# Dispatch signatures of the timed kernels -> workload.  Grid sizes (total work-items) and
+# LDS sizes follow from the launch code for these shapes.
+def dispatch_workload(name, threads, lds, hint=""):
+    if "k_gemv1_q4k<2, false>" in name:
+        if hint == "mlp":
+            return "swiglu_mlp_down_4096x14336"
+        return "gemv_4096x4096" if threads == 131072 else "sweep_gemv_14336x4096_m1"
+    if "k_gemv1_q4k<1, true>" in name:
+        return "swiglu_mlp_gateup_14336x4096"
+    if "k_gemm_q4k<4, 1, 1, 4, 2>" in name:
+        return {65536: "gemm_512x4096x4096", 114688: "gemm_512x14336x4096"}.get(threads, "gemm_other")
+    if "k_gemm_q4k<1, 4, 1, 1, 2>" in name:
+        return "sweep_gemm_14336x4096"
+    if "k_gemv_q4k<" in name:
+        return "sweep_gemv_14336x4096_batched"
+    if "k_dequant_q4k<true>" in name:
+        return "dequant_bf16_4096x4096"
+    if "k_zero_f32" in name:
+        return "split_k_zero_fill"
+    if "copy" in name.lower() or "elementwise" in name:
+        return "copy"
+    return "other"
+
+
+def _short_name(name):
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _dirs, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    return None
+
+
+def summarize_profile(args):
+    """Write a markdown summary of rocprofv3 runs: per-workload kernel durations from the
+    kernel trace; with counter runs, HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, KiB,
+    scaled by what the same counters read for the 256 MiB copy probe)."""
+    import statistics
+    dirs = args.summarize_profile
+    trace = _read_csv(_find(dirs[0], "kernel_trace.csv"))
+    groups = {}
+    for r in trace:
+        name = r["Kernel_Name"]
+        key = (_short_name(name), int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]),
+               int(r["Grid_Size_Z"]), int(r["LDS_Block_Size"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# rocprofv3 kernel summary", "", "Command:", "", "```", args.profile_command or "(not recorded)",
+             "```", "", "Kernel durations per dispatch (us), grouped by kernel and launch shape:", "",
+             "| workload | kernel | grid (threads) | LDS B | calls | median | mean | p10 | p90 |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    per_workload = {}
+    for key, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        kname, gx, gy, gz, lds = key
+        wl = dispatch_workload(kname, gx * gy * gz, lds, args.workload_hint)
+        v.sort()
+        med = statistics.median(v)
+        per_workload.setdefault(wl, med)
+        lines.append("| %s | `%s` | %dx%dx%d | %d | %d | %.3f | %.3f | %.3f | %.3f |" % (
+            wl, kname[:60], gx, gy, gz, lds, len(v), med, statistics.fmean(v), v[len(v) // 10],
+            v[(9 * len(v)) // 10]))
+    traffic_bytes = {}
+    if len(dirs) >= 3:
+        counters = {}
+        for d in dirs[1:3]:
+            for r in _read_csv(_find(d, "counter_collection.csv")):
+                kname = _short_name(r["Kernel_Name"])
+                gx = int(r["Grid_Size"]) if "Grid_Size" in r else 0
+                lds = int(r.get("LDS_Block_Size", 0))
+                counters.setdefault((kname, r["Counter_Name"], lds, gx), []).append(float(r["Counter_Value"]))
+        # calibration: the copy probe moves 256 MiB each way
+        cal = {}
+        for (kname, cname, lds, gx), vals in counters.items():
+            if "elementwise" in kname:
+                cal[cname] = max(cal.get(cname, 0.0), max(vals))
+        lines += ["", "HBM traffic per dispatch from counters (KiB), median over dispatches:", "",
+                  "| kernel | LDS B | grid | FETCH_SIZE | WRITE_SIZE |", "|---|---|---|---|---|"]
+        scale = {c: (262144.0 / cal[c] if cal.get(c) else None) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+        seen = {}
+        for (kname, cname, lds, gx), vals in counters.items():
+            seen.setdefault((kname, lds, gx), {})[cname] = statistics.median(vals)
+        for (kname, lds, gx), cs in sorted(seen.items()):
+            lines.append("| `%s` | %d | %d | %.1f | %.1f |" % (kname[:60], lds, gx, cs.get("FETCH_SIZE", -1),
+                                                            cs.get("WRITE_SIZE", -1)))
+            wl = dispatch_workload(kname, gx, lds, args.workload_hint)
+            if scale["FETCH_SIZE"] and scale["WRITE_SIZE"] and wl not in ("other", "copy"):
+                traffic_bytes.setdefault(wl, round((cs.get("FETCH_SIZE", 0) * scale["FETCH_SIZE"] +
+                                                    cs.get("WRITE_SIZE", 0) * scale["WRITE_SIZE"]) * 1024))
+        lines += ["", "Calibration: an elementwise kernel that reads and writes 256 MiB (262144 KiB each way) "
+                  "read FETCH_SIZE = %s KiB and WRITE_SIZE = %s KiB; scale factors (262144 / reading): %s." % (
+                      cal.get("FETCH_SIZE"), cal.get("WRITE_SIZE"), scale)]
+    if traffic_bytes:
+        lines += ["", "traffic_json: " + json.dumps({"source_hash": kernel_source_hash(),
+                                                     "bytes_per_launch": traffic_bytes})]
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
 
 
 def spot_check(kernels, args, np, torch):
