@@ -13,8 +13,13 @@ the 256 MB MALL and the 4 MB L2 per XCD), so each launch reads cold HBM.
 Timing: W warm-up steps, then K steps bracketed by a device synchronize.  The
 K launches of one kernel run back to back on the launch stream between two
 HIP events; the per-launch average is that kernel's duration (launch gaps
-included).  ``value`` is the decode GEMV's effective HBM bandwidth
-(algorithmic bytes / average duration).
+included).  The K launches are captured once into a HIP graph and the replay
+is timed, so that the host's per-launch cost (Python, ctypes, argument
+checks) does not throttle kernels of a few microseconds; the same launches
+enqueued one by one are timed as well and reported as ``eager_us``.
+``value`` is the decode GEMV's effective HBM bandwidth (algorithmic bytes /
+average duration).  The parity spot check reads the outputs the last graph
+replay wrote.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -55,6 +60,8 @@ def parse():
     p.add_argument("--only", default="",
                    help="comma list of kernels to run (gemv,sweep_gemv,sweep_gemm,mlp,gemm,dequant)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
+    p.add_argument("--eager-only", action="store_true",
+                   help="time only the eagerly enqueued launches (no HIP graph replay)")
     p.add_argument("--summarize-profile", nargs="+", metavar="DIR",
                    help="summarize rocprofv3 output directories (kernel trace, then optional "
                         "FETCH_SIZE and WRITE_SIZE counter runs) instead of benchmarking")
@@ -116,7 +123,7 @@ def main():
         nbytes = q4k_bytes(n, k) + 4 * k + 4 * n
         rot = Rotor(torch, [w, x, np.zeros(n, np.float32)], nbytes)
 
-        def run_gemv(i, rot=rot, n=n, k=k):
+        def run_gemv(i, sp, rot=rot, n=n, k=k):
             wd, xd, yd = rot[i]
             _lib.check(_lib.q4k_gemv(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), 1, n, k, sp))
         kernels.append(("gemv_4096x4096", run_gemv, nbytes, 2 * n * k, rot))
@@ -131,7 +138,7 @@ def main():
                 nbytes = q4k_bytes(n, k) + 4 * m * k + 4 * m * n
                 rot = Rotor(torch, [w, xf, np.zeros((m, n), np.float32)], nbytes)
 
-                def run(i, rot=rot, m=m, n=n, k=k):
+                def run(i, sp, rot=rot, m=m, n=n, k=k):
                     wd, xd, yd = rot[i]
                     _lib.check(_lib.q4k_gemv(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
                 kernels.append(("sweep_gemv_m%d" % m, run, nbytes, 2 * m * n * k, rot))
@@ -140,7 +147,7 @@ def main():
                 nbytes = q4k_bytes(n, k) + 2 * m * k + 4 * m * n
                 rot = Rotor(torch, [w, xb.view(np.int16), np.zeros((m, n), np.float32)], nbytes)
 
-                def run(i, rot=rot, m=m, n=n, k=k):
+                def run(i, sp, rot=rot, m=m, n=n, k=k):
                     wd, xd, yd = rot[i]
                     _lib.check(_lib.q4k_gemm(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
                 kernels.append(("sweep_gemm_m%d" % m, run, nbytes, 2 * m * n * k, rot))
@@ -155,7 +162,7 @@ def main():
         rot = Rotor(torch, [wg, wu, wdn, x, np.zeros(D_FF, np.float32),
                             np.zeros(D_MODEL, np.float32)], nbytes)
 
-        def run_mlp(i, rot=rot):
+        def run_mlp(i, sp, rot=rot):
             g, u, d, xd, hd, od = rot[i]
             _lib.check(_lib.q4k_swiglu_mlp(g.data_ptr(), u.data_ptr(), d.data_ptr(), xd.data_ptr(),
                                            hd.data_ptr(), od.data_ptr(), D_MODEL, D_FF, sp))
@@ -170,7 +177,7 @@ def main():
             nbytes = q4k_bytes(n, k) + 2 * m * k + 4 * m * n
             rot = Rotor(torch, [w, xb.view(np.int16), np.zeros((m, n), np.float32)], nbytes)
 
-            def run(i, rot=rot, m=m, n=n, k=k):
+            def run(i, sp, rot=rot, m=m, n=n, k=k):
                 wd, xd, yd = rot[i]
                 _lib.check(_lib.q4k_gemm(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
             kernels.append(("gemm_512x%dx4096" % n, run, nbytes, 2 * m * n * k, rot))
@@ -182,7 +189,7 @@ def main():
         nbytes = q4k_bytes(n, k) + 2 * n * k
         rot = Rotor(torch, [w, np.zeros((n, k), np.uint16).view(np.int16)], nbytes)
 
-        def run_dq(i, rot=rot, n=n, k=k):
+        def run_dq(i, sp, rot=rot, n=n, k=k):
             wd, od = rot[i]
             _lib.check(_lib.q4k_dequantize_bf16(wd.data_ptr(), od.data_ptr(), n, k, sp))
         kernels.append(("dequant_bf16_4096x4096", run_dq, nbytes, 0, rot))
@@ -198,32 +205,56 @@ def main():
         print("copy probe: elementwise kernel read and wrote 268435456 bytes", file=sys.stderr)
 
     torch.cuda.synchronize()
-    # warm-up
+    # warm-up (also sets each kernel's per-device launch attributes)
     for s in range(args.warmup):
         for _, run, *_ in kernels:
-            run(s)
+            run(s, sp)
     torch.cuda.synchronize()
 
-    # timed region: K steps; each kernel's K launches run back to back between two events
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in kernels]
+    # Timed region, two ways, each kernel's K launches back to back between two
+    # HIP events on the launch stream:
+    #   * graph (reported): the K launches are captured once into a HIP graph
+    #     and replayed, so host-side launch cost does not throttle short kernels;
+    #   * eager: the K launches are enqueued one by one from Python.
+    # The per-launch average (launch gaps included) is the kernel's duration.
+    graphs = []
+    if not args.eager_only:
+        cap = torch.cuda.Stream()
+        for name, run, *_ in kernels:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for s in range(args.steps):
+                    run(args.warmup + s, cap.cuda_stream)
+            graphs.append(g)
+        for g in graphs:  # first replay uploads the graph
+            g.replay()
+        torch.cuda.synchronize()
+    ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa: E731
+    eager_ev = [ev() for _ in kernels]
+    graph_ev = [ev() for _ in kernels]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for (name, run, *_), (e0, e1) in zip(kernels, events):
+    for (name, run, *_), (e0, e1) in zip(kernels, eager_ev):
         e0.record(stream)
         for s in range(args.steps):
-            run(args.warmup + s)
+            run(args.warmup + s, sp)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    for g, (e0, e1) in zip(graphs, graph_ev):
+        e0.record(stream)
+        g.replay()
         e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     per = {}
     total_ms = 0.0
-    for (name, run, nbytes, flop, rot), (e0, e1) in zip(kernels, events):
-        ms = e0.elapsed_time(e1)
+    for i, (name, run, nbytes, flop, rot) in enumerate(kernels):
+        eager_ms = eager_ev[i][0].elapsed_time(eager_ev[i][1])
+        ms = graph_ev[i][0].elapsed_time(graph_ev[i][1]) if graphs else eager_ms
         total_ms += ms
         us = ms * 1e3 / args.steps
-        r = {"us": round(us, 3), "copies": rot.count}
+        r = {"us": round(us, 3), "eager_us": round(eager_ms * 1e3 / args.steps, 3), "copies": rot.count}
         if nbytes:
             r["gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
             r["hbm_frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
@@ -281,7 +312,7 @@ def main():
     if head:
         out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": head["hbm_frac"], "traffic": traffic("gemv_4096x4096"),
-                           "kernel": "k_gemv_q4k<1,4,false>", "bytes_per_launch": 9469952}
+                           "kernel": "k_gemv_q4k<1,1,false,16>", "bytes_per_launch": 9469952}
     if gemm:
         out["roofline_gemm"] = {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": gemm["mfma_frac"],
@@ -325,11 +356,13 @@ def traffic(name):
 # Dispatch signatures of the timed kernels -> workload.  Grid sizes (total work-items) and
 # LDS sizes follow from the launch code for these shapes.
 def dispatch_workload(name, threads, lds, hint=""):
-    if "k_gemv1_q4k<2, false>" in name:
-        if hint == "mlp":
-            return "swiglu_mlp_down_4096x14336"
-        return "gemv_4096x4096" if threads == 131072 else "sweep_gemv_14336x4096_m1"
-    if "k_gemv1_q4k<1, true>" in name:
+    if "k_gemv_q4k<1, 1, false, 16>" in name:
+        return "gemv_4096x4096"
+    if "k_gemv_q4k<1, 2, false, 4>" in name:
+        return "sweep_gemv_14336x4096_m1"
+    if "k_gemv_q4k<1, 2, false, 8>" in name:
+        return "swiglu_mlp_down_4096x14336"
+    if "k_gemv_q4k<1, 1, true" in name:
         return "swiglu_mlp_gateup_14336x4096"
     if "k_gemm_q4k<4, 1, 1, 4, 2>" in name:
         return {65536: "gemm_512x4096x4096", 114688: "gemm_512x14336x4096"}.get(threads, "gemm_other")

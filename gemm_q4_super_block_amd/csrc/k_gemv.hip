@@ -7,19 +7,27 @@
 // of the MLP share one read of x with h = silu(g) * u formed in registers
 // ("Building ESIMD Infrastructure": MUL_MAT + MUL_MAT + SWIGLU).
 //
-// Work mapping (wave64, 4 waves per workgroup):
+// Work mapping (wave64):
 //   * lane = 4*b + g: b = 0..15 is a super-block slot, g = 0..3 a quant group.
-//     One step of the K loop covers 16 consecutive super-blocks of a row
-//     (4096 weights); a lane reads the block header (16 B) and the 32 quant
-//     bytes of its group (two 16-byte loads) -- weights 64g..64g+63 of the
-//     block: 32 low nibbles of sub-block 2g and 32 high nibbles of 2g+1.
-//   * a wave owns R consecutive weight rows (2R with the gate/up pair) and
-//     reuses each x value it loads for all of them.
+//     One K step covers 16 consecutive super-blocks of a row (4096 weights); a
+//     lane reads the block header (16 B) and the 32 quant bytes of its group
+//     (two 16-byte loads) -- weights 64g..64g+63 of the block: 32 low nibbles
+//     of sub-block 2g and 32 high nibbles of 2g+1.  A wave's load covers one
+//     row's 2304 contiguous bytes, which streams HBM as well as a flat copy.
+//   * a wave owns a set of R consecutive rows (2R with the gate/up pair) and
+//     reuses each staged x value for all of them; waves are persistent: each
+//     walks row sets with a stride of the whole grid, and the (row set, K step)
+//     items are pipelined -- the next item's weights are in flight while the
+//     current one is computed (two register sets, the loop unrolled by two).
+//   * x (MT activation rows, a chunk of K at a time) is staged once per
+//     workgroup in LDS, skewed by 16 bytes every 256 so that the lanes of a
+//     wave -- whose 64-float slices start 256 bytes apart -- hit distinct
+//     banks; the staging pass also forms the 32-wide sub-block sums of x.
 //   * per sub-block j the dot is refactored as
 //       sum_l (a_j q_l - b_j) x_l = a_j * sum_l q_l x_l - b_j * sum_l x_l,
 //     so the scales are applied twice per 32 weights, not per weight.
 //   * quants are widened with v_cvt_pk_f32_fp8 (a masked nibble byte is the
-//     fp8 value q * 2^-9), two per instruction.
+//     fp8 value q * 2^-9), two per instruction, once per weight whatever MT.
 //   * lanes reduce with DPP and two cross-row swizzles; lane 0 stores.
 #include <hip/hip_runtime.h>
 
@@ -37,214 +45,219 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 __device__ __forceinline__ float silu(float t) { return t / (1.0f + expf(-t)); }
 
+// Elements of K staged per pass: MT rows of x share roughly 64 KiB of LDS.
+// Always a multiple of one K step (4096 elements).
 template <int MT>
-constexpr int kChunkUnroll = MT == 1 ? 2 : 1;
-
-template <int MT, int R, bool GLU>
-__global__ __launch_bounds__(256) void k_gemv_q4k(const uint8_t* __restrict__ w,
-                                                  const uint8_t* __restrict__ w2,
-                                                  const float* __restrict__ x,
-                                                  float* __restrict__ y, int m, int n, int k) {
-  constexpr int NW = GLU ? 2 : 1;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int b = lane >> 2;
-  const int g = lane & 3;
-  const int kb_count = k >> 8;
-  const int row0 = (blockIdx.x * 4 + wave) * R;
-  if (row0 >= n) return;  // whole wave idle; the kernel has no barriers
-  const size_t row_bytes = static_cast<size_t>(kb_count) * kBlockBytes;
-
-  float acc[NW][R][MT];
-#pragma unroll
-  for (int t = 0; t < NW; ++t)
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int i = 0; i < MT; ++i) acc[t][r][i] = 0.0f;
-
-  for (int kb0 = 0; kb0 < kb_count; kb0 += 16) {
-    const bool active = kb0 + b < kb_count;
-    // Inactive lanes (ragged last step) read a valid block and see x = 0.
-    const int kb = active ? kb0 + b : kb_count - 1;
-
-    uint4 hd[NW][R], qa[NW][R], qb[NW][R];
-#pragma unroll
-    for (int t = 0; t < NW; ++t) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int row = min(row0 + r, n - 1);
-        const uint8_t* p = (t ? w2 : w) + row * row_bytes + static_cast<size_t>(kb) * kBlockBytes;
-        hd[t][r] = load16(p);
-        qa[t][r] = load16(p + 16 + 32 * g);
-        qb[t][r] = load16(p + 32 + 32 * g);
-      }
-    }
-
-    float pl[NW][R][MT], ph[NW][R][MT], sl[MT], sh[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      sl[i] = 0.0f;
-      sh[i] = 0.0f;
-#pragma unroll
-      for (int t = 0; t < NW; ++t)
-#pragma unroll
-        for (int r = 0; r < R; ++r) pl[t][r][i] = ph[t][r][i] = 0.0f;
-    }
-
-    const float* xb = x + static_cast<size_t>(kb) * kQK + 64 * g;
-    // Two 16-byte quant chunks per lane; batched variants keep one chunk's x
-    // live at a time (a rolled loop), batch 1 unrolls both for load depth.
-#pragma unroll(kChunkUnroll<MT>)
-    for (int hq = 0; hq < 2; ++hq) {
-      uint4 qv[NW][R];
-#pragma unroll
-      for (int t = 0; t < NW; ++t)
-#pragma unroll
-        for (int r = 0; r < R; ++r) qv[t][r] = hq ? qb[t][r] : qa[t][r];
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int c = 4 * hq + c4;
-        f4_t xl[MT], xh[MT];
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          if (active && i < m) {
-            xl[i] = *reinterpret_cast<const f4_t*>(xb + static_cast<size_t>(i) * k + 4 * c);
-            xh[i] = *reinterpret_cast<const f4_t*>(xb + static_cast<size_t>(i) * k + 32 + 4 * c);
-          } else {
-            xl[i] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            xh[i] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          }
-          sl[i] += (xl[i].x + xl[i].y) + (xl[i].z + xl[i].w);
-          sh[i] += (xh[i].x + xh[i].y) + (xh[i].z + xh[i].w);
-        }
-#pragma unroll
-        for (int t = 0; t < NW; ++t) {
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const uint32_t v = word(qv[t][r], c4);
-            const uint32_t lo = v & 0x0F0F0F0Fu;
-            const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
-            const f2_t l01 = fp8x2_lo(lo), l23 = fp8x2_hi(lo);
-            const f2_t h01 = fp8x2_lo(hi), h23 = fp8x2_hi(hi);
-#pragma unroll
-            for (int i = 0; i < MT; ++i) {
-              float a = pl[t][r][i];
-              a = __builtin_fmaf(l01.x, xl[i].x, a);
-              a = __builtin_fmaf(l01.y, xl[i].y, a);
-              a = __builtin_fmaf(l23.x, xl[i].z, a);
-              a = __builtin_fmaf(l23.y, xl[i].w, a);
-              pl[t][r][i] = a;
-              float e = ph[t][r][i];
-              e = __builtin_fmaf(h01.x, xh[i].x, e);
-              e = __builtin_fmaf(h01.y, xh[i].y, e);
-              e = __builtin_fmaf(h23.x, xh[i].z, e);
-              e = __builtin_fmaf(h23.y, xh[i].w, e);
-              ph[t][r][i] = e;
-            }
-          }
-        }
-      }
-    }
-
-#pragma unroll
-    for (int t = 0; t < NW; ++t) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const GroupScales s = group_scales(hd[t][r], g);
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          float a = acc[t][r][i];
-          a = __builtin_fmaf(s.a_lo, pl[t][r][i], a);
-          a = __builtin_fmaf(s.a_hi, ph[t][r][i], a);
-          a = __builtin_fmaf(-s.b_lo, sl[i], a);
-          a = __builtin_fmaf(-s.b_hi, sh[i], a);
-          acc[t][r][i] = a;
-        }
-      }
-    }
-  }
-
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row = row0 + r;
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      float v = wave_sum(acc[0][r][i]);
-      if constexpr (GLU) {
-        const float u = wave_sum(acc[NW - 1][r][i]);
-        v = silu(v) * u;
-      }
-      if (lane == 0 && row < n && i < m) y[static_cast<size_t>(i) * n + row] = v;
-    }
-  }
-}
-
-// ---------------------------------------------------------------- batch 1
-// x (up to kXChunk floats at a time) is staged once per workgroup in LDS,
-// skewed by 16 bytes every 256 bytes so that the lanes of a wave -- whose
-// 64-float slices start 256 bytes apart -- hit distinct banks; the staging
-// pass also forms the 32-wide sub-block sums of x.  Each wave prefetches the
-// next K step's weights before it computes the current one.
-constexpr int kXChunk = 16384;
+constexpr int kXChunk = MT == 1 ? 16384 : MT == 2 ? 8192 : 4096;
 
 __device__ __forceinline__ int xs_index(int i) { return i + ((i >> 6) << 2); }
 
-__host__ __device__ constexpr size_t gemv1_lds_bytes(int kc) {
-  return static_cast<size_t>(kc + kc / 16 + kc / 32) * sizeof(float);
+// Floats of LDS per staged activation row (skewed x) and per row of sums.
+__host__ __device__ constexpr int xs_stride(int kc) { return kc + kc / 16; }
+
+__host__ __device__ constexpr size_t gemv_lds_bytes(int mt, int kc) {
+  return static_cast<size_t>(mt) * (xs_stride(kc) + kc / 32) * sizeof(float);
 }
 
-template <int R, bool GLU>
-__global__ __launch_bounds__(256) void k_gemv1_q4k(const uint8_t* __restrict__ w,
-                                                   const uint8_t* __restrict__ w2,
-                                                   const float* __restrict__ x,
-                                                   float* __restrict__ y, int n, int k) {
+template <int R, int NW>
+struct WRegs {
+  uint4 hd[NW][R], qa[NW][R], qb[NW][R];
+};
+
+// MT activation rows per pass, R weight rows per wave (times NW = 2 weight
+// matrices for the gate/up pair), NWV waves per workgroup.
+template <int MT, int R, bool GLU, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict__ w,
+                                                       const uint8_t* __restrict__ w2,
+                                                       const float* __restrict__ x,
+                                                       float* __restrict__ y, int m, int n,
+                                                       int k) {
+  static_assert(!GLU || MT == 1, "the gate/up pair runs at batch 1");
   constexpr int NW = GLU ? 2 : 1;
+  constexpr int NT = 64 * NWV;
   extern __shared__ float smem[];
-  const int kc_max = min(k, kXChunk);
-  float* xs = smem;
-  float* ssum = smem + kc_max + kc_max / 16;
+  const int kc_max = min(k, kXChunk<MT>);
+  const int xst = xs_stride(kc_max);
+  const int sst = kc_max / 32;
+  float* xs = smem;             // [MT][xst]
+  float* ssum = smem + MT * xst;  // [MT][sst]
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   const int b = lane >> 2;
   const int g = lane & 3;
   const int kb_count = k >> 8;
-  const int steps = (kb_count + 15) >> 4;
   const size_t row_bytes = static_cast<size_t>(kb_count) * kBlockBytes;
-  const int row0 = (blockIdx.x * 4 + wave) * R;
+  const int nsets = (n + R - 1) / R;
+  const int gw = blockIdx.x * NWV + wave;
+  const int tw = gridDim.x * NWV;
+  const int my_sets = gw < nsets ? (nsets - 1 - gw) / tw + 1 : 0;
+  // With at most one row set per wave the accumulators stay in registers
+  // across K chunks (the gate/up pair needs the full dot before silu);
+  // otherwise each chunk's partial dot is added into y.
+  const bool single = tw >= nsets;
 
-  auto load_w = [&](int s, uint4 (&hd)[NW][R], uint4 (&qa)[NW][R], uint4 (&qb)[NW][R]) {
-    const int kb = min(s * 16 + b, kb_count - 1);
-#pragma unroll
-    for (int u = 0; u < NW; ++u) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int row = min(row0 + r, n - 1);
-        const uint8_t* p = (u ? w2 : w) + row * row_bytes + static_cast<size_t>(kb) * kBlockBytes;
-        hd[u][r] = load16(p);
-        qa[u][r] = load16(p + 16 + 32 * g);
-        qb[u][r] = load16(p + 32 + 32 * g);
-      }
-    }
-  };
-
-  uint4 hd[NW][R], qa[NW][R], qb[NW][R];
-  load_w(0, hd, qa, qb);  // in flight while x is staged
-
-  float acc[NW][R];
+  float acc[NW][R][MT];
 #pragma unroll
   for (int u = 0; u < NW; ++u)
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[u][r] = 0.0f;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[u][r][i] = 0.0f;
 
-  for (int c0 = 0; c0 < k; c0 += kXChunk) {
-    const int kc = min(kXChunk, k - c0);
-    if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
-    for (int i0 = 16 * t; i0 < kc; i0 += 16 * 256) {
-      const f4_t* src = reinterpret_cast<const f4_t*>(x + c0 + i0);
-      const f4_t v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
-      f4_t* dst = reinterpret_cast<f4_t*>(xs + xs_index(i0));
+  for (int c0 = 0; c0 < k; c0 += kXChunk<MT>) {
+    const int kc = min(kXChunk<MT>, k - c0);
+    const int s_begin = c0 >> 12;
+    const int ns = (kc + 4095) >> 12;  // K steps in this chunk
+    const int jobs = my_sets * ns;
+    const bool last_chunk = c0 + kc >= k;
+
+    auto issue = [&](int j, WRegs<R, NW>& B) {
+      const int si = j / ns;
+      const int st = s_begin + (j - si * ns);
+      const int row0 = (gw + si * tw) * R;
+      const int kb = min(st * 16 + b, kb_count - 1);
+#pragma unroll
+      for (int u = 0; u < NW; ++u) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = min(row0 + r, n - 1);
+          const uint8_t* p =
+              (u ? w2 : w) + row * row_bytes + static_cast<size_t>(kb) * kBlockBytes;
+          B.hd[u][r] = load16(p);
+          B.qa[u][r] = load16(p + 16 + 32 * g);
+          B.qb[u][r] = load16(p + 32 + 32 * g);
+        }
+      }
+    };
+
+    auto compute = [&](int j, const WRegs<R, NW>& B) {
+      const int si = j / ns;
+      const int sl = j - si * ns;
+      const int st = s_begin + sl;
+      // Lanes past the last super-block (ragged last step) read block 0 of
+      // the chunk and x slot 0 -- valid memory -- and add nothing.
+      const bool active = st * 16 + b < kb_count;
+      const int kb_local = active ? st * 16 + b - (c0 >> 8) : 0;
+      const int xo = xs_index(kb_local * kQK + 64 * g);
+      float pl[NW][R][MT], ph[NW][R][MT];
+#pragma unroll
+      for (int u = 0; u < NW; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int i = 0; i < MT; ++i) pl[u][r][i] = ph[u][r][i] = 0.0f;
+      // At batch 1, x is read one 4-float slice ahead of its use; batches
+      // read at use (their many accumulators leave no registers to spare).
+      // A scheduling fence per slice keeps the compiler from hoisting all the
+      // reads of a step (and spilling).
+      constexpr bool kAhead = MT == 1;
+      f4_t xl_n[MT], xh_n[MT];
+      if constexpr (kAhead) {
+        xl_n[0] = *reinterpret_cast<const f4_t*>(xs + xo);
+        xh_n[0] = *reinterpret_cast<const f4_t*>(xs + xo + 32);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        f4_t xl[MT], xh[MT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          if constexpr (kAhead) {
+            xl[i] = xl_n[i];
+            xh[i] = xh_n[i];
+            if (c < 7) {
+              xl_n[i] = *reinterpret_cast<const f4_t*>(xs + i * xst + xo + 4 * c + 4);
+              xh_n[i] = *reinterpret_cast<const f4_t*>(xs + i * xst + xo + 36 + 4 * c);
+            }
+          } else {
+            xl[i] = *reinterpret_cast<const f4_t*>(xs + i * xst + xo + 4 * c);
+            xh[i] = *reinterpret_cast<const f4_t*>(xs + i * xst + xo + 32 + 4 * c);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < NW; ++u) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint32_t v = c < 4 ? word(B.qa[u][r], c) : word(B.qb[u][r], c - 4);
+            const uint32_t lo = v & 0x0F0F0F0Fu;
+            const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+            const f2_t l01 = fp8x2_lo(lo), l23 = fp8x2_hi(lo);
+            const f2_t h01 = fp8x2_lo(hi), h23 = fp8x2_hi(hi);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+              float a = pl[u][r][i];
+              a = __builtin_fmaf(l01.x, xl[i].x, a);
+              a = __builtin_fmaf(l01.y, xl[i].y, a);
+              a = __builtin_fmaf(l23.x, xl[i].z, a);
+              a = __builtin_fmaf(l23.y, xl[i].w, a);
+              pl[u][r][i] = a;
+              float e = ph[u][r][i];
+              e = __builtin_fmaf(h01.x, xh[i].x, e);
+              e = __builtin_fmaf(h01.y, xh[i].y, e);
+              e = __builtin_fmaf(h23.x, xh[i].z, e);
+              e = __builtin_fmaf(h23.y, xh[i].w, e);
+              ph[u][r][i] = e;
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u = 0; u < NW; ++u) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const GroupScales sc = group_scales(B.hd[u][r], g);
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const float slo = ssum[i * sst + kb_local * 8 + 2 * g];
+            const float shi = ssum[i * sst + kb_local * 8 + 2 * g + 1];
+            float a = sc.a_lo * pl[u][r][i];
+            a = __builtin_fmaf(sc.a_hi, ph[u][r][i], a);
+            a = __builtin_fmaf(-sc.b_lo, slo, a);
+            a = __builtin_fmaf(-sc.b_hi, shi, a);
+            acc[u][r][i] += active ? a : 0.0f;
+          }
+        }
+      }
+      if (sl != ns - 1 || (single && !last_chunk)) return;
+      // Row set finished (for this chunk): reduce, store, reset.
+      const int row0 = (gw + si * tw) * R;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          float v = wave_sum(acc[0][r][i]);
+          if constexpr (GLU) v = silu(v) * wave_sum(acc[NW - 1][r][i]);
+          if (lane == 0 && row < n && i < m) {
+            float* dst = y + static_cast<size_t>(i) * n + row;
+            if (single || c0 == 0) {
+              *dst = v;
+            } else {
+              *dst += v;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < NW; ++u) acc[u][r][i] = 0.0f;
+        }
+      }
+    };
+
+    WRegs<R, NW> bufA, bufB;
+    if (jobs > 0) issue(0, bufA);  // in flight while x is staged
+    if (c0 > 0) __syncthreads();   // every wave is done with the previous chunk
+    for (int idx = 16 * t; idx < MT * kc; idx += 16 * NT) {
+      const int i = idx / kc;
+      const int e = idx - i * kc;
+      f4_t v0 = {0, 0, 0, 0}, v1 = v0, v2 = v0, v3 = v0;
+      if (i < m) {
+        const f4_t* src = reinterpret_cast<const f4_t*>(x + static_cast<size_t>(i) * k + c0 + e);
+        v0 = src[0];
+        v1 = src[1];
+        v2 = src[2];
+        v3 = src[3];
+      }
+      f4_t* dst = reinterpret_cast<f4_t*>(xs + i * xst + xs_index(e));
       dst[0] = v0;
       dst[1] = v1;
       dst[2] = v2;
@@ -252,109 +265,76 @@ __global__ __launch_bounds__(256) void k_gemv1_q4k(const uint8_t* __restrict__ w
       float s = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)) +
                 ((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w));
       s += dpp_mov<0xB1>(s);  // thread t ^ 1 holds the other 16 floats of the sub-block
-      if ((t & 1) == 0) ssum[i0 >> 5] = s;
+      if ((t & 1) == 0) ssum[i * sst + (e >> 5)] = s;
     }
     __syncthreads();
 
-    const int s_begin = c0 >> 12;
-    const int s_end = min(steps, (c0 + kc + 4095) >> 12);
-    for (int s = s_begin; s < s_end; ++s) {
-      uint4 nhd[NW][R], nqa[NW][R], nqb[NW][R];
-      const bool more = s + 1 < steps;
-      if (more) load_w(s + 1, nhd, nqa, nqb);
-      const bool active = s * 16 + b < kb_count;
-      const int kb_local = active ? s * 16 + b - (c0 >> 8) : 0;
-      const float* xb = xs + xs_index(kb_local * kQK + 64 * g);
-      const float sl = active ? ssum[kb_local * 8 + 2 * g] : 0.0f;
-      const float sh = active ? ssum[kb_local * 8 + 2 * g + 1] : 0.0f;
-      float pl[NW][R], ph[NW][R];
-#pragma unroll
-      for (int u = 0; u < NW; ++u)
-#pragma unroll
-        for (int r = 0; r < R; ++r) pl[u][r] = ph[u][r] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const f4_t xl = active ? *reinterpret_cast<const f4_t*>(xb + 4 * c) : f4_t{0, 0, 0, 0};
-        const f4_t xh = active ? *reinterpret_cast<const f4_t*>(xb + 32 + 4 * c) : f4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < NW; ++u) {
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const uint32_t v = c < 4 ? word(qa[u][r], c) : word(qb[u][r], c - 4);
-            const uint32_t lo = v & 0x0F0F0F0Fu;
-            const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
-            const f2_t l01 = fp8x2_lo(lo), l23 = fp8x2_hi(lo);
-            const f2_t h01 = fp8x2_lo(hi), h23 = fp8x2_hi(hi);
-            float a = pl[u][r];
-            a = __builtin_fmaf(l01.x, xl.x, a);
-            a = __builtin_fmaf(l01.y, xl.y, a);
-            a = __builtin_fmaf(l23.x, xl.z, a);
-            a = __builtin_fmaf(l23.y, xl.w, a);
-            pl[u][r] = a;
-            float e = ph[u][r];
-            e = __builtin_fmaf(h01.x, xh.x, e);
-            e = __builtin_fmaf(h01.y, xh.y, e);
-            e = __builtin_fmaf(h23.x, xh.z, e);
-            e = __builtin_fmaf(h23.y, xh.w, e);
-            ph[u][r] = e;
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NW; ++u) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const GroupScales sc = group_scales(hd[u][r], g);
-          float a = acc[u][r];
-          a = __builtin_fmaf(sc.a_lo, pl[u][r], a);
-          a = __builtin_fmaf(sc.a_hi, ph[u][r], a);
-          a = __builtin_fmaf(-sc.b_lo, sl, a);
-          a = __builtin_fmaf(-sc.b_hi, sh, a);
-          acc[u][r] = a;
-          hd[u][r] = nhd[u][r];
-          qa[u][r] = nqa[u][r];
-          qb[u][r] = nqb[u][r];
-        }
-      }
+    for (int j = 0; j < jobs; j += 2) {
+      if (j + 1 < jobs) issue(j + 1, bufB);
+      compute(j, bufA);
+      if (j + 1 >= jobs) break;
+      if (j + 2 < jobs) issue(j + 2, bufA);
+      compute(j + 1, bufB);
     }
   }
-
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float v = wave_sum(acc[0][r]);
-    if constexpr (GLU) v = silu(v) * wave_sum(acc[NW - 1][r]);
-    if (lane == 0 && row0 + r < n) y[row0 + r] = v;
-  }
 }
 
-template <int R, bool GLU>
-hipError_t launch1(const uint8_t* w, const uint8_t* w2, const float* x, float* y, int n, int k,
-                   hipStream_t stream) {
-  const size_t lds = gemv1_lds_bytes(min(k, kXChunk));
-  // LDS above 64 KiB needs an opt-in per kernel and device (set once per device).
-  static std::atomic<uint64_t> attr_set{0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
-  const uint64_t bit = 1ull << (dev & 63);
-  if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv1_q4k<R, GLU>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(gemv1_lds_bytes(kXChunk)));
+// Per-device launch facts, read once: CU count and LDS per CU; per kernel,
+// the workgroups per CU that registers and wave slots allow (LDS above 64 KiB
+// needs an opt-in per kernel and device).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+std::atomic<int> g_lds_per_cu[kMaxDevices];
+
+hipError_t device_facts(int dev, int* cus, int* lds_per_cu) {
+  int c = g_cu_count[dev].load(std::memory_order_acquire);
+  int l = g_lds_per_cu[dev].load(std::memory_order_acquire);
+  if (c == 0 || l == 0) {
+    hipError_t e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    attr_set.fetch_or(bit, std::memory_order_acq_rel);
+    e = hipDeviceGetAttribute(&l, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e != hipSuccess) return e;
+    g_cu_count[dev].store(c, std::memory_order_release);
+    g_lds_per_cu[dev].store(l, std::memory_order_release);
   }
-  const int grid = (n + 4 * R - 1) / (4 * R);
-  hipLaunchKernelGGL((k_gemv1_q4k<R, GLU>), dim3(grid), dim3(256), lds, stream, w, w2, x, y, n, k);
-  return hipGetLastError();
+  *cus = c;
+  *lds_per_cu = l;
+  return hipSuccess;
 }
 
-template <int MT, int R, bool GLU>
+template <int MT, int R, bool GLU, int NWV>
 hipError_t launch(const uint8_t* w, const uint8_t* w2, const float* x, float* y, int m, int n,
                   int k, hipStream_t stream) {
-  const int rows_per_block = 4 * R;
-  const int grid = (n + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((k_gemv_q4k<MT, R, GLU>), dim3(grid), dim3(256), 0, stream, w, w2, x, y, m,
-                     n, k);
+  static std::atomic<int> resident[kMaxDevices];  // workgroups per CU, LDS aside
+  const auto kern = &k_gemv_q4k<MT, R, GLU, NWV>;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int cus = 0, lds_per_cu = 0;
+  e = device_facts(dev, &cus, &lds_per_cu);
+  if (e != hipSuccess) return e;
+  int occ = resident[dev].load(std::memory_order_acquire);
+  if (occ == 0) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(gemv_lds_bytes(MT, kXChunk<MT>)));
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * NWV, 0);
+    if (e != hipSuccess) return e;
+    occ = occ < 1 ? 1 : occ;
+    resident[dev].store(occ, std::memory_order_release);
+  }
+  const size_t lds = gemv_lds_bytes(MT, min(k, kXChunk<MT>));
+  const int by_lds = static_cast<int>(static_cast<size_t>(lds_per_cu) / lds);
+  const int per_cu = max(1, min(occ, by_lds));
+  const int nsets = (n + R - 1) / R;
+  const int need = (nsets + NWV - 1) / NWV;
+  // The gate/up pair keeps its dots in registers across K chunks, so above
+  // one chunk every wave gets at most one row set.
+  const bool one_set = GLU && k > kXChunk<MT>;
+  const int grid = one_set ? need : min(need, per_cu * cus);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NWV), lds, stream, w, w2, x, y, m, n, k);
   return hipGetLastError();
 }
 
@@ -367,15 +347,23 @@ hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, in
     const int mm = static_cast<int>(m - i0 < 8 ? m - i0 : 8);
     const float* xs = x + i0 * k;
     float* ys = y + i0 * n;
+    const int ni = static_cast<int>(n), ki = static_cast<int>(k);
     hipError_t e;
     if (mm == 1) {
-      e = launch1<kGemvRowsPerWave, false>(w, w, xs, ys, (int)n, (int)k, stream);
+      if (n * k <= kGemvSmallWeights) {
+        // Few rows per CU: short dots, many waves, x staged once per 16 waves.
+        e = launch<1, 1, false, 16>(w, w, xs, ys, mm, ni, ki, stream);
+      } else if (k >= 8192) {
+        e = launch<1, kGemvRowsPerWave, false, 8>(w, w, xs, ys, mm, ni, ki, stream);
+      } else {
+        e = launch<1, kGemvRowsPerWave, false, 4>(w, w, xs, ys, mm, ni, ki, stream);
+      }
     } else if (mm == 2) {
-      e = launch<2, 2, false>(w, w, xs, ys, mm, (int)n, (int)k, stream);
+      e = launch<2, 2, false, 4>(w, w, xs, ys, mm, ni, ki, stream);
     } else if (mm <= 4) {
-      e = launch<4, 2, false>(w, w, xs, ys, mm, (int)n, (int)k, stream);
+      e = launch<4, 2, false, 4>(w, w, xs, ys, mm, ni, ki, stream);
     } else {
-      e = launch<8, 1, false>(w, w, xs, ys, mm, (int)n, (int)k, stream);
+      e = launch<8, 1, false, 8>(w, w, xs, ys, mm, ni, ki, stream);
     }
     if (e != hipSuccess) return e;
   }
@@ -384,7 +372,8 @@ hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, in
 
 hipError_t launch_gateup_swiglu(const uint8_t* w_gate, const uint8_t* w_up, const float* x,
                                 float* h, int64_t d_model, int64_t d_ff, hipStream_t stream) {
-  return launch1<kGateUpRowsPerWave, true>(w_gate, w_up, x, h, (int)d_ff, (int)d_model, stream);
+  return launch<1, kGateUpRowsPerWave, true, 8>(w_gate, w_up, x, h, 1, static_cast<int>(d_ff),
+                                                static_cast<int>(d_model), stream);
 }
 
 }  // namespace q4k
