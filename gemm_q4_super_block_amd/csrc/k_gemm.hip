@@ -217,6 +217,234 @@ hipError_t launch(const uint8_t* w, const uint16_t* x, float* y, int m, int n, i
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------ large tiles
+// 256 x 128 output tiles for large N at M >= 256 (each weight tile is then
+// dequantized M/256 times instead of M/128 times):
+//   * 8 waves, 4 (M) x 2 (N), 64 x 64 outputs each as 2 x 2 accumulators of
+//     v_mfma_f32_32x32x16_bf16; two waves per SIMD, so one wave's LDS fragment
+//     reads overlap the other's MFMAs.
+//   * all global -> LDS traffic is direct (global_load_lds_dwordx4, no VGPR
+//     staging): X through a 3-slot ring, the raw 16-byte header and 32 quant
+//     bytes of each weight row through a 3-slot ring one step further ahead.
+//     The copies are issued from inline assembly so the compiler neither
+//     tracks nor waits for them; the waits are explicit: at the end of step s
+//     the copies issued at step s-1 have landed (every wave issues exactly
+//     kXCopies + 1 copies per step), then one barrier.
+//   * the raw tile of step s+1 is dequantized (bf16, round to nearest even of
+//     the exact fp32 weight) into one of two bf16 LDS tiles during step s.
+//   * LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by row, so
+//     the 32 rows a fragment read touches hit distinct banks.
+//   * each workgroup starts its K loop at a different step: X rows are 8 KiB
+//     apart, and workgroups walking K in lockstep would all hit the same L2
+//     channel.
+//   * when the tile grid allows, workgroup b (XCD b % 8) takes one M-tile
+//     per group of XCDs, so each XCD's L2 holds one 2 MiB slice of X.
+constexpr int kLBM = 256, kLBN = 128;
+constexpr int kXCopies = kLBM * 128 / 1024 / 8;  // X copies (1 KiB each) per wave per step
+constexpr int kLXSlot = kLBM * 128;              // bytes per X slot
+constexpr int kLRSlot = kLBN * 64;               // bytes per raw-weight slot (64 B per row)
+constexpr int kLBSlot = kLBN * 128;              // bytes per bf16 weight slot
+constexpr int kLRot = 7;                         // K start step = blockIdx * 7 mod steps
+
+__device__ __forceinline__ int swz(int r) { return ((r & 15) >> 1) ^ ((r & 1) << 2); }
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// One 16-byte-per-lane global -> LDS copy: lane i's 16 bytes go to
+// lds_uniform + 16 i.  M0 is saved and restored around the copy.
+__device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds_uniform) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_uniform)
+      : "memory");
+}
+
+__global__ __launch_bounds__(512, 1) void k_gemm_q4k_256x128(const uint8_t* __restrict__ w,
+                                                             const uint16_t* __restrict__ x,
+                                                             float* __restrict__ y, int m, int n,
+                                                             int k, int tiles_m, int tiles_n,
+                                                             int xcd_map) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * kLXSlot + 3 * kLRSlot + 2 * kLBSlot];
+  uint8_t* const xs = smem;
+  uint8_t* const rs = smem + 3 * kLXSlot;
+  uint8_t* const bs = smem + 3 * kLXSlot + 3 * kLRSlot;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int half = lane >> 5;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  int tm, tn;
+  if (xcd_map) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per_m = 8 / tiles_m;
+    tm = xcd / per_m;
+    tn = (xcd % per_m) * (tiles_n / per_m) + slot;
+  } else {
+    tm = blockIdx.x % tiles_m;
+    tn = blockIdx.x / tiles_m;
+  }
+  const int m0 = tm * kLBM, n0 = tn * kLBN;
+  const int kb_count = k >> 8;
+  const int steps = k >> 6;
+  const int rot = (static_cast<int>(blockIdx.x) * kLRot) % steps;
+  // Physical K step of logical step s (steps past the end repeat the last one).
+  auto phys = [&](int s) {
+    const int e = min(s, steps - 1) + rot;
+    return e < steps ? e : e - steps;
+  };
+
+  // X copies: copy q of this wave fills tile rows 8 (wave kXCopies + q) .. +7,
+  // lane -> (row, LDS chunk lane % 8) holding X chunk (lane % 8) ^ swz(row).
+  const uint16_t* xsrc[kXCopies];
+#pragma unroll
+  for (int q = 0; q < kXCopies; ++q) {
+    const int row = 8 * (wave * kXCopies + q) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    xsrc[q] = x + static_cast<size_t>(min(m0 + row, m - 1)) * k + 8 * c;
+  }
+  // Raw-weight copy: wave fills rows 16 wave .. +15, lane -> (row, part):
+  // part 0 header, 1 and 2 the two 16-byte halves of the quant group, 3 a
+  // second header read that pads the row to 64 bytes.
+  const int wrow = 16 * wave + (lane >> 2);
+  const int wpart = lane & 3;
+  const uint8_t* wsrc = w + static_cast<size_t>(min(n0 + wrow, n - 1)) * kb_count * kBlockBytes;
+  const uint32_t xs_l = lds_address(xs), rs_l = lds_address(rs);
+
+  auto copy_x = [&](int s, int slot) {
+    const int ps = phys(s);
+#pragma unroll
+    for (int q = 0; q < kXCopies; ++q)
+      copy16_to_lds(xsrc[q] + static_cast<size_t>(ps) * kBK,
+                    __builtin_amdgcn_readfirstlane(xs_l + slot * kLXSlot +
+                                                   (wave * kXCopies + q) * 1024));
+  };
+  auto copy_w = [&](int s, int slot) {
+    const int ps = phys(s);
+    const int off = (wpart == 1 || wpart == 2) ? 16 + 32 * (ps & 3) + 16 * (wpart - 1) : 0;
+    copy16_to_lds(wsrc + static_cast<size_t>(ps >> 2) * kBlockBytes + off,
+                  __builtin_amdgcn_readfirstlane(rs_l + slot * kLRSlot + wave * 1024));
+  };
+
+  // Dequant role: thread t -> weight row t / 4, quarter t % 4 of the quant
+  // group (8 bytes: 8 low-nibble and 8 high-nibble weights).
+  const int drow = t >> 2, dq = t & 3;
+  auto read_raw = [&](int slot, uint4& hd, uint2& qv) {
+    const uint8_t* rp = rs + slot * kLRSlot + drow * 64;
+    hd = *reinterpret_cast<const uint4*>(rp);
+    qv = *reinterpret_cast<const uint2*>(rp + 16 + 8 * dq);
+  };
+  auto dequant = [&](int s, const uint4& hd, const uint2& qv, int slot) {
+    const GroupScales sc = group_scales(hd, phys(s) & 3);
+    float lo[8], hi[8];
+    dequant_dword(qv.x, sc, lo, hi);
+    dequant_dword(qv.y, sc, lo + 4, hi + 4);
+    uint8_t* rowp = bs + slot * kLBSlot + drow * 128;
+    const int f = swz(drow);
+    *reinterpret_cast<uint4*>(rowp + ((dq ^ f) << 4)) =
+        make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                   pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7]));
+    *reinterpret_cast<uint4*>(rowp + (((4 + dq) ^ f) << 4)) =
+        make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
+                   pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7]));
+  };
+
+  f16x_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // A/B fragment of a K16 slice kk: lane -> row lane % 32, 16-byte chunk 2 kk + lane / 32.
+  auto mfma_step = [&](int xslot, int bslot) {
+    const uint8_t* xb = xs + xslot * kLXSlot;
+    const uint8_t* wb = bs + bslot * kLBSlot;
+    bf16x8_t af[4][2], bf[4][2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = 2 * kk + half;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + 32 * i + (lane & 31);
+        af[kk][i] = *reinterpret_cast<const bf16x8_t*>(xb + r * 128 + ((c ^ swz(r)) << 4));
+        const int rn = wn * 64 + 32 * i + (lane & 31);
+        bf[kk][i] = *reinterpret_cast<const bf16x8_t*>(wb + rn * 128 + ((c ^ swz(rn)) << 4));
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bf[kk][j], acc[i][j], 0, 0, 0);
+  };
+
+  // Prologue: raw W(0), X(0), raw W(1), X(1), raw W(2) issued; W(0), X(0),
+  // W(1) must land (X(1) and W(2): kXCopies + 1 copies may remain).
+  static_assert(kXCopies + 1 == 5, "the explicit waits below count 5 copies per step");
+  copy_w(0, 0);
+  copy_x(0, 0);
+  copy_w(1, 1);
+  copy_x(1, 1);
+  copy_w(2, 2);
+  asm volatile("s_waitcnt vmcnt(5)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  {
+    uint4 hd;
+    uint2 qv;
+    read_raw(0, hd, qv);
+    dequant(0, hd, qv, 0);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // Step s: X slot s % 3, raw slot (s + 1) % 3, bf16 slot s % 2.
+  int xa = 0, ra = 1, ba = 0;
+  for (int s = 0; s < steps; ++s) {
+    copy_x(s + 2, xa == 0 ? 2 : xa - 1);  // slot (s + 2) % 3, last read at step s - 1
+    copy_w(s + 3, ra == 0 ? 2 : ra - 1);  // slot (s + 3) % 3, last read at step s - 1
+    uint4 hd;
+    uint2 qv;
+    read_raw(ra, hd, qv);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(xa, ba);
+    if (s + 1 < steps) dequant(s + 1, hd, qv, ba ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // copies of step s - 1 (X(s + 1), raw W(s + 2)) landed; LDS writes done
+    asm volatile("s_waitcnt vmcnt(5)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    xa = xa == 2 ? 0 : xa + 1;
+    ra = ra == 2 ? 0 : ra + 1;
+    ba ^= 1;
+  }
+  // No copy into this workgroup's LDS may outlive it.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + 32 * j + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (row < m && col < n) y[static_cast<size_t>(row) * n + col] = acc[i][j][r];
+      }
+    }
+  }
+}
+
 // Split K until the grid reaches one workgroup per CU (256 on MI355X).
 int splits_for(int tiles, int steps) {
   int s = 1;
@@ -234,6 +462,14 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
   if (mi <= 32) {
     // Small batch: one 32-row slice, the four waves split the 128 weight rows.
     return launch<1, 4, 1, 1, 2>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
+  }
+  const int big_m = (mi + kLBM - 1) / kLBM, big_n = (ni + kLBN - 1) / kLBN;
+  if (mi >= kLBM && big_m * big_n >= kGemmBigTiles) {
+    // Enough 256 x 128 tiles to fill most CUs without splitting K.
+    const bool xcd = 8 % big_m == 0 && big_n % (8 / big_m) == 0 && (big_m * big_n) % 8 == 0;
+    hipLaunchKernelGGL(k_gemm_q4k_256x128, dim3(big_m * big_n), dim3(512), 0, stream, w, x, y,
+                       mi, ni, ki, big_m, big_n, xcd ? 1 : 0);
+    return hipGetLastError();
   }
   // 128 x 128 tiles, two workgroups per CU.
   const int tiles = ((mi + 127) / 128) * tiles_n;

@@ -13,6 +13,9 @@ namespace q4k {
 // Shipped launch shapes (pinned by tests/test_abi.py).
 constexpr int kGemvRowsPerWave = 2;    // decode GEMV, batch 1: rows of W per wave
 constexpr int kGateUpRowsPerWave = 1;  // gate/up SwiGLU: row pairs per wave
+// Prefill GEMMs with M >= 256 and at least this many 256 x 128 output tiles
+// use the large-tile kernel.
+constexpr int kGemmBigTiles = 128;
 // Batch-1 matrices of at most this many weights run one row per wave.
 constexpr int64_t kGemvSmallWeights = int64_t(4096) * 4096;
 

@@ -246,6 +246,21 @@ def test_gemm_prefill_sampled(q4k, n):
     assert np.all(np.isfinite(Y))
 
 
+# Shapes that take the 256 x 128 large-tile kernel (M >= 256, >= 128 tiles):
+# ragged M and N with the linear tile order (130 tiles), and an XCD-ordered
+# grid (128 tiles) at the smallest K (4 steps, every K rotation in play).
+@pytest.mark.parametrize("m,n,k", [(300, 8200, 512), (512, 8192, 256), (257, 16383, 768)])
+def test_gemm_large_tile_kernel(q4k, m, n, k):
+    w = synth.q4k_weights(n, k, seed=m + k)
+    xb = synth.normal_bf16((m, k), seed=m + k)
+    Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, n - 129, n - 2, n - 1],
+                                     np.random.default_rng(n).integers(0, n, 55)]))
+    Yr, A = oracle.gemm_cols(w, xb, n, k, cols)
+    assert_within(Y[:, cols], Yr, A, GEMM_TOL, "gemm %dx%dx%d" % (m, n, k))
+    assert np.all(np.isfinite(Y))
+
+
 @pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
 def test_gemm_sweep_shape_sampled(q4k, m):
     n, k = 14336, 4096
