@@ -357,11 +357,9 @@ def traffic(name):
 # LDS sizes follow from the launch code for these shapes.
 def dispatch_workload(name, threads, lds, hint=""):
     if "k_gemv_q4k<1, 1, false, 16>" in name:
-        return "gemv_4096x4096"
-    if "k_gemv_q4k<1, 2, false, 4>" in name:
+        return "swiglu_mlp_down_4096x14336" if hint == "mlp" else "gemv_4096x4096"
+    if "k_gemv_q4k<1, 1, false, 8>" in name:
         return "sweep_gemv_14336x4096_m1"
-    if "k_gemv_q4k<1, 2, false, 8>" in name:
-        return "swiglu_mlp_down_4096x14336"
     if "k_gemv_q4k<1, 1, true" in name:
         return "swiglu_mlp_gateup_14336x4096"
     if "k_gemm_q4k_256x128" in name:

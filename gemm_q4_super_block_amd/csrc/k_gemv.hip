@@ -243,29 +243,48 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
       }
     };
 
-    WRegs<R, NW> bufA, bufB;
-    if (jobs > 0) issue(0, bufA);  // in flight while x is staged
-    if (c0 > 0) __syncthreads();   // every wave is done with the previous chunk
-    for (int idx = 16 * t; idx < MT * kc; idx += 16 * NT) {
+    // x staging, 16 floats per thread and pass.  The first pass's x loads are
+    // issued before the first weights: loads complete in order, so x (a few
+    // L2 hits) then lands first and the staging barrier does not wait for the
+    // weights of every wave of the workgroup.
+    auto load_x16 = [&](int idx, f4_t (&v)[4]) {
       const int i = idx / kc;
       const int e = idx - i * kc;
-      f4_t v0 = {0, 0, 0, 0}, v1 = v0, v2 = v0, v3 = v0;
+      v[0] = v[1] = v[2] = v[3] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
       if (i < m) {
         const f4_t* src = reinterpret_cast<const f4_t*>(x + static_cast<size_t>(i) * k + c0 + e);
-        v0 = src[0];
-        v1 = src[1];
-        v2 = src[2];
-        v3 = src[3];
+        v[0] = src[0];
+        v[1] = src[1];
+        v[2] = src[2];
+        v[3] = src[3];
       }
+    };
+    auto store_x16 = [&](int idx, const f4_t (&v)[4]) {
+      const int i = idx / kc;
+      const int e = idx - i * kc;
       f4_t* dst = reinterpret_cast<f4_t*>(xs + i * xst + xs_index(e));
-      dst[0] = v0;
-      dst[1] = v1;
-      dst[2] = v2;
-      dst[3] = v3;
-      float s = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)) +
-                ((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w));
+      dst[0] = v[0];
+      dst[1] = v[1];
+      dst[2] = v[2];
+      dst[3] = v[3];
+      float s = ((v[0].x + v[0].y) + (v[0].z + v[0].w)) + ((v[1].x + v[1].y) + (v[1].z + v[1].w)) +
+                ((v[2].x + v[2].y) + (v[2].z + v[2].w)) + ((v[3].x + v[3].y) + (v[3].z + v[3].w));
       s += dpp_mov<0xB1>(s);  // thread t ^ 1 holds the other 16 floats of the sub-block
       if ((t & 1) == 0) ssum[i * sst + (e >> 5)] = s;
+    };
+    // Every pass covers whole sub-blocks (MT * kc is a multiple of 32), so a
+    // thread and its partner t ^ 1 take the same passes.
+    const bool first = 16 * t < MT * kc;
+    f4_t v0[4];
+    if (first) load_x16(16 * t, v0);
+    WRegs<R, NW> bufA, bufB;
+    if (jobs > 0) issue(0, bufA);
+    if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
+    if (first) store_x16(16 * t, v0);
+    for (int idx = 16 * t + 16 * NT; idx < MT * kc; idx += 16 * NT) {
+      f4_t v[4];
+      load_x16(idx, v);
+      store_x16(idx, v);
     }
     __syncthreads();
 
@@ -350,13 +369,12 @@ hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, in
     const int ni = static_cast<int>(n), ki = static_cast<int>(k);
     hipError_t e;
     if (mm == 1) {
-      if (n * k <= kGemvSmallWeights) {
-        // Few rows per CU: short dots, many waves, x staged once per 16 waves.
-        e = launch<1, 1, false, 16>(w, w, xs, ys, mm, ni, ki, stream);
-      } else if (k >= 8192) {
-        e = launch<1, kGemvRowsPerWave, false, 8>(w, w, xs, ys, mm, ni, ki, stream);
+      // One row per wave; matrices with few rows per CU take 16 waves per
+      // workgroup (x staged once per 16 waves), taller ones 8.
+      if (n <= kGemvWideRows) {
+        e = launch<1, kGemvRowsPerWave, false, 16>(w, w, xs, ys, mm, ni, ki, stream);
       } else {
-        e = launch<1, kGemvRowsPerWave, false, 4>(w, w, xs, ys, mm, ni, ki, stream);
+        e = launch<1, kGemvRowsPerWave, false, 8>(w, w, xs, ys, mm, ni, ki, stream);
       }
     } else if (mm == 2) {
       e = launch<2, 2, false, 4>(w, w, xs, ys, mm, ni, ki, stream);

@@ -11,13 +11,13 @@
 namespace q4k {
 
 // Shipped launch shapes (pinned by tests/test_abi.py).
-constexpr int kGemvRowsPerWave = 2;    // decode GEMV, batch 1: rows of W per wave
+constexpr int kGemvRowsPerWave = 1;    // decode GEMV, batch 1: rows of W per wave
 constexpr int kGateUpRowsPerWave = 1;  // gate/up SwiGLU: row pairs per wave
 // Prefill GEMMs with M >= 256 and at least this many 256 x 128 output tiles
 // use the large-tile kernel.
 constexpr int kGemmBigTiles = 128;
-// Batch-1 matrices of at most this many weights run one row per wave.
-constexpr int64_t kGemvSmallWeights = int64_t(4096) * 4096;
+// Batch-1 matrices of at most this many rows run 16 waves per workgroup.
+constexpr int64_t kGemvWideRows = 8192;
 
 hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);

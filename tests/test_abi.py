@@ -111,8 +111,8 @@ def test_no_device_is_reported_cleanly():
 def test_shipped_launch_shapes_are_pinned():
     src = os.path.join(ROOT, "gemm_q4_super_block_amd", "csrc")
     launch = open(os.path.join(src, "q4k_launch.h")).read()
-    assert re.search(r"kGemvRowsPerWave = 2;", launch)
-    assert re.search(r"kGemvSmallWeights = int64_t\(4096\) \* 4096;", launch)
+    assert re.search(r"kGemvRowsPerWave = 1;", launch)
+    assert re.search(r"kGemvWideRows = 8192;", launch)
     assert re.search(r"kGateUpRowsPerWave = 1;", launch)
     gemm = open(os.path.join(src, "k_gemm.hip")).read()
     assert re.search(r"kBN = 128;", gemm) and re.search(r"kBK = 64;", gemm)
