@@ -362,8 +362,8 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "sweep_gemv_14336x4096_m1"
     if "k_gemv_q4k<1, 1, true" in name:
         return "swiglu_mlp_gateup_14336x4096"
-    if "k_gemm_q4k_256x128" in name:
-        return "gemm_512x14336x4096" if threads == 114688 else "gemm_other"
+    if "k_gemm_q4k_128x256" in name:
+        return "gemm_512x14336x4096" if threads == 57344 else "gemm_other"
     if "k_gemm_q4k<4, 1, 1, 4, 2>" in name:
         return "gemm_512x4096x4096" if threads == 65536 else "gemm_other"
     if "k_gemm_q4k<1, 4, 1, 1, 2>" in name:

@@ -219,33 +219,39 @@ hipError_t launch(const uint8_t* w, const uint16_t* x, float* y, int m, int n, i
 
 
 // ------------------------------------------------------------ large tiles
-// 256 x 128 output tiles for large N at M >= 256 (each weight tile is then
-// dequantized M/256 times instead of M/128 times):
-//   * 8 waves, 4 (M) x 2 (N), 64 x 64 outputs each as 2 x 2 accumulators of
-//     v_mfma_f32_32x32x16_bf16; two waves per SIMD, so one wave's LDS fragment
-//     reads overlap the other's MFMAs.
-//   * all global -> LDS traffic is direct (global_load_lds_dwordx4, no VGPR
-//     staging): X through a 3-slot ring, the raw 16-byte header and 32 quant
-//     bytes of each weight row through a 3-slot ring one step further ahead.
-//     The copies are issued from inline assembly so the compiler neither
-//     tracks nor waits for them; the waits are explicit: at the end of step s
-//     the copies issued at step s-1 have landed (every wave issues exactly
-//     kXCopies + 1 copies per step), then one barrier.
-//   * the raw tile of step s+1 is dequantized (bf16, round to nearest even of
-//     the exact fp32 weight) into one of two bf16 LDS tiles during step s.
-//   * LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by row, so
-//     the 32 rows a fragment read touches hit distinct banks.
-//   * each workgroup starts its K loop at a different step: X rows are 8 KiB
-//     apart, and workgroups walking K in lockstep would all hit the same L2
-//     channel.
-//   * when the tile grid allows, workgroup b (XCD b % 8) takes one M-tile
-//     per group of XCDs, so each XCD's L2 holds one 2 MiB slice of X.
-constexpr int kLBM = 256, kLBN = 128;
-constexpr int kXCopies = kLBM * 128 / 1024 / 8;  // X copies (1 KiB each) per wave per step
-constexpr int kLXSlot = kLBM * 128;              // bytes per X slot
-constexpr int kLRSlot = kLBN * 64;               // bytes per raw-weight slot (64 B per row)
-constexpr int kLBSlot = kLBN * 128;              // bytes per bf16 weight slot
-constexpr int kLRot = 7;                         // K start step = blockIdx * 7 mod steps
+// 128 x 256 output tiles for prefill GEMMs with many tiles (m=512, n=14336:
+// 224 tiles).  The weights never pass through LDS as bf16: each wave
+// dequantizes its MFMA B fragments straight into registers.
+//   * 4 waves = 2 (K parity) x 2 (N halves).  Every wave owns all 128 rows x
+//     128 columns (4 x 4 accumulators of v_mfma_f32_32x32x16_bf16, 256
+//     AGPRs) and, in each 64-wide K step (one quant group g), only the
+//     sub-block of its parity: low nibbles (sub-block 2g) or high nibbles
+//     (2g+1).  Every weight is dequantized once per workgroup; the two K
+//     halves are summed through LDS at the end.
+//   * within a step, lane half h of a wave holds the 16 quant bytes
+//     16h .. 16h+15 of its column; MFMA slice u (0, 1) uses bytes 8u .. 8u+7
+//     of that half, so slice u, lane half h covers k = 32 p + 16 h + 8 u + (0..7)
+//     for parity p.  The X fragment of the same lanes reads those k.
+//   * global -> LDS traffic is direct (global_load_lds_dwordx4), issued from
+//     inline assembly with explicit waits: X (128 rows x 64 k = 16 KiB per
+//     step) through a 5-slot ring, 5 steps ahead; whole 144-byte super-blocks
+//     of the 256 weight rows (36 KiB) through a 2-slot ring, issued at the
+//     last step of the super-block before the one that needs them.
+//   * LDS X rows are 128 bytes with XOR-swizzled 16-byte chunks (conflict-
+//     free fragment reads); weight rows keep their 144-byte record, whose
+//     36-dword stride spreads 16 consecutive rows over all 64 banks.
+//   * K starts at a super-block that depends on the N-tile only: the M-tiles
+//     that share a weight tile walk K in step, and the N-tiles that share X
+//     rows start at different offsets.  When the tile grid allows, all
+//     M-tiles of an N-tile run on one XCD, so its L2 serves their weight reads.
+constexpr int kWBM = 128, kWBN = 256;
+constexpr int kWXSlot = kWBM * 128;          // bytes per X slot (one step)
+constexpr int kWWSlot = kWBN * kBlockBytes;  // bytes per weight slot (one super-block)
+constexpr int kWXSlots = 5;
+constexpr int kWWOff = kWXSlots * kWXSlot;
+constexpr int kWLds = kWXSlots * kWXSlot + 2 * kWWSlot;  // 155648 bytes
+static_assert(kWLds <= 160 * 1024, "LDS budget of one workgroup");
+static_assert(2 * 2 * 32768 <= kWLds, "the K-half exchange reuses the rings");
 
 __device__ __forceinline__ int swz(int r) { return ((r & 15) >> 1) ^ ((r & 1) << 2); }
 
@@ -269,179 +275,286 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds_unifor
       : "memory");
 }
 
-__global__ __launch_bounds__(512, 1) void k_gemm_q4k_256x128(const uint8_t* __restrict__ w,
+// Wait until at most N copies of this wave are in flight, then barrier.
+template <int N>
+__device__ __forceinline__ void wait_copies_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// 8 weights of one MFMA slice: nibbles (shift 0: low, 4: high) of the 8
+// quant bytes d0, d1, as bf16 of fma(a, q*2^-9, -b).
+__device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t d0, uint32_t d1, int shift, float a,
+                                                  float b) {
+  const uint32_t l0 = (d0 >> shift) & 0x0F0F0F0Fu;
+  const uint32_t l1 = (d1 >> shift) & 0x0F0F0F0Fu;
+  const f2_t p0 = fp8x2_lo(l0), p1 = fp8x2_hi(l0), p2 = fp8x2_lo(l1), p3 = fp8x2_hi(l1);
+  return __builtin_bit_cast(
+      bf16x8_t,
+      make_uint4(pack_bf16x2(__builtin_fmaf(a, p0.x, -b), __builtin_fmaf(a, p0.y, -b)),
+                 pack_bf16x2(__builtin_fmaf(a, p1.x, -b), __builtin_fmaf(a, p1.y, -b)),
+                 pack_bf16x2(__builtin_fmaf(a, p2.x, -b), __builtin_fmaf(a, p2.y, -b)),
+                 pack_bf16x2(__builtin_fmaf(a, p3.x, -b), __builtin_fmaf(a, p3.y, -b))));
+}
+
+struct XFrag {
+  bf16x8_t a[2][4];  // [slice u][M block i]
+};
+
+// xcd_map: 1 = all M-tiles of an N-tile on one XCD (tiles_n % 8 == 0).
+__global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __restrict__ w,
                                                              const uint16_t* __restrict__ x,
                                                              float* __restrict__ y, int m, int n,
                                                              int k, int tiles_m, int tiles_n,
                                                              int xcd_map) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * kLXSlot + 3 * kLRSlot + 2 * kLBSlot];
-  uint8_t* const xs = smem;
-  uint8_t* const rs = smem + 3 * kLXSlot;
-  uint8_t* const bs = smem + 3 * kLXSlot + 3 * kLRSlot;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWLds];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int half = lane >> 5;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int h = lane >> 5;
+  const int c32 = lane & 31;
+  const int kp = wave >> 1;  // K parity: 0 = low nibbles, 1 = high nibbles
+  const int wn = wave & 1;   // N half
   int tm, tn;
   if (xcd_map) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int per_m = 8 / tiles_m;
-    tm = xcd / per_m;
-    tn = (xcd % per_m) * (tiles_n / per_m) + slot;
+    tm = slot % tiles_m;
+    tn = xcd * (tiles_n / 8) + slot / tiles_m;
   } else {
     tm = blockIdx.x % tiles_m;
     tn = blockIdx.x / tiles_m;
   }
-  const int m0 = tm * kLBM, n0 = tn * kLBN;
-  const int kb_count = k >> 8;
-  const int steps = k >> 6;
-  const int rot = (static_cast<int>(blockIdx.x) * kLRot) % steps;
-  // Physical K step of logical step s (steps past the end repeat the last one).
-  auto phys = [&](int s) {
-    const int e = min(s, steps - 1) + rot;
-    return e < steps ? e : e - steps;
+  const int m0 = tm * kWBM, n0 = tn * kWBN;
+  const int nsb = k >> 8;                     // super-blocks along K
+  const int nst = k >> 6;                     // 64-wide steps
+  const uint32_t row_bytes = static_cast<uint32_t>(nsb) * kBlockBytes;
+  const int sb_rot = (tn * 7) % nsb;
+  // Super-block of logical super-block S (indices past the end repeat the last).
+  auto phys_sb = [&](int S) {
+    const int e = min(S, nsb - 1) + sb_rot;
+    return e < nsb ? e : e - nsb;
   };
 
-  // X copies: copy q of this wave fills tile rows 8 (wave kXCopies + q) .. +7,
-  // lane -> (row, LDS chunk lane % 8) holding X chunk (lane % 8) ^ swz(row).
-  const uint16_t* xsrc[kXCopies];
+  // X copy q of this wave fills tile rows 8 (4 wave + q) .. +7; lane ->
+  // (row, LDS chunk lane % 8) holding X chunk (lane % 8) ^ swz(row).
+  const uint16_t* xsrc[4];
 #pragma unroll
-  for (int q = 0; q < kXCopies; ++q) {
-    const int row = 8 * (wave * kXCopies + q) + (lane >> 3);
+  for (int q = 0; q < 4; ++q) {
+    const int row = 8 * (wave * 4 + q) + (lane >> 3);
     const int c = (lane & 7) ^ swz(row);
     xsrc[q] = x + static_cast<size_t>(min(m0 + row, m - 1)) * k + 8 * c;
   }
-  // Raw-weight copy: wave fills rows 16 wave .. +15, lane -> (row, part):
-  // part 0 header, 1 and 2 the two 16-byte halves of the quant group, 3 a
-  // second header read that pads the row to 64 bytes.
-  const int wrow = 16 * wave + (lane >> 2);
-  const int wpart = lane & 3;
-  const uint8_t* wsrc = w + static_cast<size_t>(min(n0 + wrow, n - 1)) * kb_count * kBlockBytes;
-  const uint32_t xs_l = lds_address(xs), rs_l = lds_address(rs);
-
+  // Weight copy i of this wave fills 16-byte unit P = 64 (9 wave + i) + lane
+  // of the slot: row P / 9, part P % 9 of its 144-byte super-block.
+  uint32_t woff[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int P = (wave * 9 + i) * 64 + lane;
+    const int col = (P * 7282) >> 16;  // P / 9 for P < 2304
+    woff[i] = static_cast<uint32_t>(min(n0 + col, n - 1)) * row_bytes + (P - col * 9) * 16;
+  }
+  const uint32_t lds0 = lds_address(smem);
   auto copy_x = [&](int s, int slot) {
-    const int ps = phys(s);
+    const int sc = min(s, nst - 1);
+    const int ps = 4 * phys_sb(sc >> 2) + (sc & 3);
 #pragma unroll
-    for (int q = 0; q < kXCopies; ++q)
-      copy16_to_lds(xsrc[q] + static_cast<size_t>(ps) * kBK,
-                    __builtin_amdgcn_readfirstlane(xs_l + slot * kLXSlot +
-                                                   (wave * kXCopies + q) * 1024));
+    for (int q = 0; q < 4; ++q)
+      copy16_to_lds(xsrc[q] + static_cast<size_t>(ps) * 64,
+                    __builtin_amdgcn_readfirstlane(lds0 + slot * kWXSlot + (wave * 4 + q) * 1024));
   };
-  auto copy_w = [&](int s, int slot) {
-    const int ps = phys(s);
-    const int off = (wpart == 1 || wpart == 2) ? 16 + 32 * (ps & 3) + 16 * (wpart - 1) : 0;
-    copy16_to_lds(wsrc + static_cast<size_t>(ps >> 2) * kBlockBytes + off,
-                  __builtin_amdgcn_readfirstlane(rs_l + slot * kLRSlot + wave * 1024));
-  };
-
-  // Dequant role: thread t -> weight row t / 4, quarter t % 4 of the quant
-  // group (8 bytes: 8 low-nibble and 8 high-nibble weights).
-  const int drow = t >> 2, dq = t & 3;
-  auto read_raw = [&](int slot, uint4& hd, uint2& qv) {
-    const uint8_t* rp = rs + slot * kLRSlot + drow * 64;
-    hd = *reinterpret_cast<const uint4*>(rp);
-    qv = *reinterpret_cast<const uint2*>(rp + 16 + 8 * dq);
-  };
-  auto dequant = [&](int s, const uint4& hd, const uint2& qv, int slot) {
-    const GroupScales sc = group_scales(hd, phys(s) & 3);
-    float lo[8], hi[8];
-    dequant_dword(qv.x, sc, lo, hi);
-    dequant_dword(qv.y, sc, lo + 4, hi + 4);
-    uint8_t* rowp = bs + slot * kLBSlot + drow * 128;
-    const int f = swz(drow);
-    *reinterpret_cast<uint4*>(rowp + ((dq ^ f) << 4)) =
-        make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                   pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7]));
-    *reinterpret_cast<uint4*>(rowp + (((4 + dq) ^ f) << 4)) =
-        make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
-                   pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7]));
-  };
-
-  f16x_t acc[2][2];
+  auto copy_w = [&](int S, int slot) {
+    const uint8_t* base = w + static_cast<size_t>(phys_sb(S)) * kBlockBytes;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 9; ++i)
+      copy16_to_lds(base + woff[i], __builtin_amdgcn_readfirstlane(
+                                        lds0 + kWWOff + slot * kWWSlot + (wave * 9 + i) * 1024));
+  };
+  // Fragments: X slices of the wave's parity; quant half h and header of its columns.
+  auto read_x = [&](int slot, XFrag& A) {
+    const uint8_t* xb = smem + slot * kWXSlot;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + c32;
+        const int ch = kp * 4 + 2 * h + u;
+        A.a[u][i] = *reinterpret_cast<const bf16x8_t*>(xb + r * 128 + ((ch ^ swz(r)) << 4));
+      }
+  };
+  auto read_q = [&](int slot, int g, uint4 (&Q)[4]) {
+    const uint8_t* wb = smem + kWWOff + slot * kWWSlot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = wn * 128 + 32 * j + c32;
+      Q[j] = *reinterpret_cast<const uint4*>(wb + col * kBlockBytes + 16 + 32 * g + 16 * h);
+    }
+  };
+  auto read_hdr = [&](int slot, uint4 (&H)[4]) {
+    const uint8_t* wb = smem + kWWOff + slot * kWWSlot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = wn * 128 + 32 * j + c32;
+      H[j] = *reinterpret_cast<const uint4*>(wb + col * kBlockBytes);
+    }
+  };
+  // sa[g][j], sb[g][j]: a = d*sc*2^9 and b = dmin*mn of sub-block 2g + kp of column block j.
+  auto scales = [&](const uint4 (&H)[4], float (&sa)[4][4], float (&sb)[4][4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 hd = H[j];
+      const uint32_t sc_lo = hd.y & 0x3F3F3F3Fu;
+      const uint32_t mn_lo = hd.z & 0x3F3F3F3Fu;
+      const uint32_t sc_hi = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+      const uint32_t mn_hi = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+      const float d = half_bits_to_float(hd.x & 0xFFFFu) * kNibbleUnscale;
+      const float dmin = half_bits_to_float(hd.x >> 16);
+      const int sh = 8 * kp;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t scw = (g < 2 ? sc_lo : sc_hi) >> (sh + 16 * (g & 1));
+        const uint32_t mnw = (g < 2 ? mn_lo : mn_hi) >> (sh + 16 * (g & 1));
+        sa[g][j] = d * static_cast<float>(scw & 0xFFu);
+        sb[g][j] = dmin * static_cast<float>(mnw & 0xFFu);
+      }
+    }
+  };
+  const int nshift = 4 * kp;
+  auto dequant = [&](const uint4 (&Q)[4], int u, const float (&a)[4], const float (&b)[4],
+                     bf16x8_t (&B)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      B[j] = dequant8_bf16(u ? Q[j].z : Q[j].x, u ? Q[j].w : Q[j].y, nshift, a[j], b[j]);
+  };
+  f16x_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // A/B fragment of a K16 slice kk: lane -> row lane % 32, 16-byte chunk 2 kk + lane / 32.
-  auto mfma_step = [&](int xslot, int bslot) {
-    const uint8_t* xb = xs + xslot * kLXSlot;
-    const uint8_t* wb = bs + bslot * kLBSlot;
-    bf16x8_t af[4][2], bf[4][2];
+  auto mfmas = [&](const XFrag& A, int u, const bf16x8_t (&B)[4]) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = 2 * kk + half;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + 32 * i + (lane & 31);
-        af[kk][i] = *reinterpret_cast<const bf16x8_t*>(xb + r * 128 + ((c ^ swz(r)) << 4));
-        const int rn = wn * 64 + 32 * i + (lane & 31);
-        bf[kk][i] = *reinterpret_cast<const bf16x8_t*>(wb + rn * 128 + ((c ^ swz(rn)) << 4));
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bf[kk][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[u][i], B[j], acc[i][j], 0, 0, 0);
   };
 
-  // Prologue: raw W(0), X(0), raw W(1), X(1), raw W(2) issued; W(0), X(0),
-  // W(1) must land (X(1) and W(2): kXCopies + 1 copies may remain).
-  static_assert(kXCopies + 1 == 5, "the explicit waits below count 5 copies per step");
+  // Copies per wave: X 4 per step, weights 9 per super-block.  Prologue:
+  // W(0), X(0..4), W(1); W(0) and X(0) land, then X(1).
   copy_w(0, 0);
-  copy_x(0, 0);
+#pragma unroll
+  for (int s = 0; s < kWXSlots; ++s) copy_x(s, s);
   copy_w(1, 1);
-  copy_x(1, 1);
-  copy_w(2, 2);
-  asm volatile("s_waitcnt vmcnt(5)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  {
-    uint4 hd;
-    uint2 qv;
-    read_raw(0, hd, qv);
-    dequant(0, hd, qv, 0);
+  wait_copies_barrier<4 * 4 + 9>();
+  XFrag A0, A1;
+  uint4 Q0[4], Q1[4], H[4];
+  float sa[4][4], sb[4][4];
+  read_hdr(0, H);
+  read_q(0, 0, Q0);
+  read_x(0, A0);
+  wait_copies_barrier<3 * 4 + 9>();
+  scales(H, sa, sb);
+  bf16x8_t B0[4];
+  dequant(Q0, 0, sa[0], sb[0], B0);
+
+  int xs = 0;  // X slot of step s
+  int ws = 0;  // weight slot of super-block S
+  // Step s (phase p = s % 4 of super-block S): issue X(s+5) and, at phase 3,
+  // W(S+2); read the fragments of step s+1; MFMAs of step s, the weights of
+  // slice 1 and of step s+1's slice 0 dequantized in between.  At the end of
+  // the step every copy issued up to step s-3 has landed (X(s+2), and from
+  // phase 2 on W(S+1)).
+  auto step = [&](int s, int p, XFrag& Ac, uint4 (&Qc)[4], XFrag& An, uint4 (&Qn)[4]) {
+    const int xn = xs == kWXSlots - 1 ? 0 : xs + 1;
+    const int ws1 = ws ^ 1;
+    copy_x(s + kWXSlots, xs);
+    if (p == 3) copy_w((s >> 2) + 2, ws);
+    read_x(xn, An);
+    if (p < 3) {
+      read_q(ws, p + 1, Qn);
+    } else {
+      read_q(ws1, 0, Qn);
+      read_hdr(ws1, H);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t B1[4];
+    dequant(Qc, 1, sa[p], sb[p], B1);
+    mfmas(Ac, 0, B0);
+    if (p < 3) {
+      dequant(Qn, 0, sa[p + 1], sb[p + 1], B0);
+    } else {
+      scales(H, sa, sb);
+      dequant(Qn, 0, sa[0], sb[0], B0);
+    }
+    mfmas(Ac, 1, B1);
+    // One MFMA, then five VALU instructions, so the dequantization runs
+    // under the matrix core.
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (p == 2)
+      wait_copies_barrier<3 * 4>();
+    else
+      wait_copies_barrier<3 * 4 + 9>();
+    __builtin_amdgcn_sched_barrier(0);
+    xs = xn;
+    if (p == 3) ws = ws1;
+  };
+  for (int s = 0; s < nst; s += 4) {
+    step(s, 0, A0, Q0, A1, Q1);
+    step(s + 1, 1, A1, Q1, A0, Q0);
+    step(s + 2, 2, A0, Q0, A1, Q1);
+    step(s + 3, 3, A1, Q1, A0, Q0);
+  }
+  // No copy into this workgroup's LDS may outlive it; the rings are reused below.
+  wait_copies_barrier<0>();
+
+  // Sum the K halves: parity 1 hands rows 0..63 to parity 0, parity 0 hands
+  // rows 64..127 to parity 1; each lane moves its own accumulator registers.
+  uint8_t* const ex_out = smem + (kp == 1 ? 0 : 65536) + wn * 32768;
+  const uint8_t* const ex_in = smem + (kp == 0 ? 0 : 65536) + wn * 32768;
+  auto put = [&](int il, const f16x_t (&row)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<f4_t*>(ex_out + ((il * 4 + j) * 4 + r4) * 1024 + lane * 16) =
+            f4_t{row[j][4 * r4], row[j][4 * r4 + 1], row[j][4 * r4 + 2], row[j][4 * r4 + 3]};
+  };
+  if (kp == 1) {
+    put(0, acc[0]);
+    put(1, acc[1]);
+  } else {
+    put(0, acc[2]);
+    put(1, acc[3]);
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  // Step s: X slot s % 3, raw slot (s + 1) % 3, bf16 slot s % 2.
-  int xa = 0, ra = 1, ba = 0;
-  for (int s = 0; s < steps; ++s) {
-    copy_x(s + 2, xa == 0 ? 2 : xa - 1);  // slot (s + 2) % 3, last read at step s - 1
-    copy_w(s + 3, ra == 0 ? 2 : ra - 1);  // slot (s + 3) % 3, last read at step s - 1
-    uint4 hd;
-    uint2 qv;
-    read_raw(ra, hd, qv);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(xa, ba);
-    if (s + 1 < steps) dequant(s + 1, hd, qv, ba ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    // copies of step s - 1 (X(s + 1), raw W(s + 2)) landed; LDS writes done
-    asm volatile("s_waitcnt vmcnt(5)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    xa = xa == 2 ? 0 : xa + 1;
-    ra = ra == 2 ? 0 : ra + 1;
-    ba ^= 1;
-  }
-  // No copy into this workgroup's LDS may outlive it.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
+  // Accumulator r of a 32x32 tile holds row 8*(r/4) + 4*h + r%4, column lane%32.
+  auto finish = [&](int il, int i, const f16x_t (&row)[4]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + 32 * j + c32;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + 32 * j + (lane & 31);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f4_t o = *reinterpret_cast<const f4_t*>(ex_in + ((il * 4 + j) * 4 + r4) * 1024 + lane * 16);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row < m && col < n) y[static_cast<size_t>(row) * n + col] = acc[i][j][r];
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const int row_g = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row_g < m && col < n) y[static_cast<size_t>(row_g) * n + col] = row[j][r] + o[e];
+        }
       }
     }
+  };
+  if (kp == 0) {
+    finish(0, 0, acc[0]);
+    finish(1, 1, acc[1]);
+  } else {
+    finish(0, 2, acc[2]);
+    finish(1, 3, acc[3]);
   }
 }
 
@@ -463,11 +576,11 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
     // Small batch: one 32-row slice, the four waves split the 128 weight rows.
     return launch<1, 4, 1, 1, 2>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
   }
-  const int big_m = (mi + kLBM - 1) / kLBM, big_n = (ni + kLBN - 1) / kLBN;
-  if (mi >= kLBM && big_m * big_n >= kGemmBigTiles) {
-    // Enough 256 x 128 tiles to fill most CUs without splitting K.
-    const bool xcd = 8 % big_m == 0 && big_n % (8 / big_m) == 0 && (big_m * big_n) % 8 == 0;
-    hipLaunchKernelGGL(k_gemm_q4k_256x128, dim3(big_m * big_n), dim3(512), 0, stream, w, x, y,
+  const int big_m = (mi + kWBM - 1) / kWBM, big_n = (ni + kWBN - 1) / kWBN;
+  if (mi >= 2 * kWBM && big_m * big_n >= kGemmBigTiles) {
+    // Enough 128 x 256 tiles to fill most CUs without splitting K.
+    const bool xcd = big_n % 8 == 0;
+    hipLaunchKernelGGL(k_gemm_q4k_128x256, dim3(big_m * big_n), dim3(256), 0, stream, w, x, y,
                        mi, ni, ki, big_m, big_n, xcd ? 1 : 0);
     return hipGetLastError();
   }

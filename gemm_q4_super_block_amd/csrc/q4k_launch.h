@@ -13,7 +13,7 @@ namespace q4k {
 // Shipped launch shapes (pinned by tests/test_abi.py).
 constexpr int kGemvRowsPerWave = 1;    // decode GEMV, batch 1: rows of W per wave
 constexpr int kGateUpRowsPerWave = 1;  // gate/up SwiGLU: row pairs per wave
-// Prefill GEMMs with M >= 256 and at least this many 256 x 128 output tiles
+// Prefill GEMMs with M >= 256 and at least this many 128 x 256 output tiles
 // use the large-tile kernel.
 constexpr int kGemmBigTiles = 128;
 // Batch-1 matrices of at most this many rows run 16 waves per workgroup.

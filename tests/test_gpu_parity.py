@@ -246,13 +246,15 @@ def test_gemm_prefill_sampled(q4k, n):
     assert np.all(np.isfinite(Y))
 
 
-# Shapes around the switch to the 256 x 128 large-tile kernel (M >= 256 and
-# >= 128 tiles): ragged M and N with the linear tile order (130 tiles), an
-# XCD-ordered grid (128 tiles) at the smallest K (4 steps, every K rotation in
-# play), 256 tiles with N one short of a multiple of 128, and two shapes just
-# below the switch (64 tiles, split-K 128 x 128 kernel).
-@pytest.mark.parametrize("m,n,k", [(300, 8200, 512), (512, 8192, 256), (257, 16383, 768),
-                                   (512, 4096, 4096), (384, 4000, 4096)])
+# Shapes around the switch to the 128 x 256 large-tile kernel (M >= 256 and
+# >= 128 tiles): an XCD-ordered grid of exactly 128 tiles at the smallest K (one
+# super-block), ragged M and N with 192 tiles and three super-blocks (every K
+# rotation in play), ragged M with the linear tile order (65 N-tiles), five
+# M-tiles on the XCD order, and three shapes below the switch (99, 64 and 48
+# tiles: the split-K 128 x 128 kernel).
+@pytest.mark.parametrize("m,n,k", [(512, 8192, 256), (257, 16383, 768), (300, 16640, 512),
+                                   (640, 12288, 1024), (300, 8200, 512), (512, 4096, 4096),
+                                   (384, 4000, 4096)])
 def test_gemm_large_tile_kernel(q4k, m, n, k):
     w = synth.q4k_weights(n, k, seed=m + k)
     xb = synth.normal_bf16((m, k), seed=m + k)
