@@ -16,6 +16,9 @@ constexpr int kGateUpRowsPerWave = 1;  // gate/up SwiGLU: row pairs per wave
 // Prefill GEMMs with M >= 256 and at least this many 128 x 256 output tiles
 // use the large-tile kernel.
 constexpr int kGemmBigTiles = 128;
+// Other prefill GEMMs (M > 32) with at least this many 64 x 128 output tiles
+// use the mid-tile kernel; smaller grids split K over 128 x 128 tiles.
+constexpr int kGemmMidTiles = 192;
 // Batch-1 matrices of at most this many rows run 16 waves per workgroup.
 constexpr int64_t kGemvWideRows = 8192;
 

@@ -246,24 +246,38 @@ def test_gemm_prefill_sampled(q4k, n):
     assert np.all(np.isfinite(Y))
 
 
-# Shapes around the switch to the 128 x 256 large-tile kernel (M >= 256 and
-# >= 128 tiles): an XCD-ordered grid of exactly 128 tiles at the smallest K (one
-# super-block), ragged M and N with 192 tiles and three super-blocks (every K
-# rotation in play), ragged M with the linear tile order (65 N-tiles), five
-# M-tiles on the XCD order, and three shapes below the switch (99, 64 and 48
-# tiles: the split-K 128 x 128 kernel).
+# Shapes around the kernel switches (M > 32):
+#   128 x 256 tiles (M >= 256, >= 128 tiles): an XCD-ordered grid of exactly 128
+#     tiles at the smallest K (one super-block); ragged M and N, 192 tiles, three
+#     super-blocks (every K rotation in play); ragged M with the linear order;
+#     five M-tiles on the XCD order.
+#   64 x 128 tiles (>= 192 tiles): ragged M and N (325 tiles), N not a multiple
+#     of 128 with 192 tiles, M = 65 (a one-row last M-tile), 256 tiles at K = 4096.
+#   128 x 128 tiles with split K (fewer tiles): 64 and 32 tiles.
 @pytest.mark.parametrize("m,n,k", [(512, 8192, 256), (257, 16383, 768), (300, 16640, 512),
-                                   (640, 12288, 1024), (300, 8200, 512), (512, 4096, 4096),
-                                   (384, 4000, 4096)])
-def test_gemm_large_tile_kernel(q4k, m, n, k):
+                                   (640, 12288, 1024), (300, 8200, 512), (384, 4000, 4096),
+                                   (65, 24576, 512), (512, 4096, 4096), (128, 4096, 1024),
+                                   (64, 4000, 2048)])
+def test_gemm_tile_kernels(q4k, m, n, k):
     w = synth.q4k_weights(n, k, seed=m + k)
     xb = synth.normal_bf16((m, k), seed=m + k)
     Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
-    cols = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, n - 129, n - 2, n - 1],
-                                     np.random.default_rng(n).integers(0, n, 55)]))
+    cols = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 255, 256, n - 129, n - 65, n - 2,
+                                      n - 1], np.random.default_rng(n).integers(0, n, 52)]))
     Yr, A = oracle.gemm_cols(w, xb, n, k, cols)
     assert_within(Y[:, cols], Yr, A, GEMM_TOL, "gemm %dx%dx%d" % (m, n, k))
     assert np.all(np.isfinite(Y))
+
+
+def test_gemm_mid_tile_kernel_full_output(q4k):
+    # 4 x 48 = 192 tiles of 64 x 128 (the smallest mid-tile grid), every output
+    # against the oracle; M = 200 leaves an 8-row last M-tile.
+    m, n, k = 200, 6144, 256
+    w = synth.q4k_weights(n, k, seed=77)
+    xb = synth.normal_bf16((m, k), seed=77)
+    Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
+    Yr, A = oracle.gemm(w, xb, n, k)
+    assert_within(Y, Yr, A, GEMM_TOL, "gemm 200x6144x256")
 
 
 @pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
