@@ -317,7 +317,7 @@ def main():
         out["roofline_gemm"] = {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": gemm["mfma_frac"],
                                 "traffic": traffic("gemm_512x4096x4096"),
-                                "kernel": "k_gemm_q4k_64x128",
+                                "kernel": "k_gemm_q4k_kslice<2, 2>",
                                 "flop_per_launch": 2 * 512 * 4096 * 4096}
     print(json.dumps(out))
 
@@ -364,8 +364,10 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "swiglu_mlp_gateup_14336x4096"
     if "k_gemm_q4k_128x256" in name:
         return "gemm_512x14336x4096" if threads == 57344 else "gemm_other"
-    if "k_gemm_q4k_64x128" in name:
+    if "k_gemm_q4k_kslice<2, 2>" in name:
         return "gemm_512x4096x4096" if threads == 131072 else "gemm_other"
+    if "k_gemm_q4k_kslice<1, 2>" in name:
+        return "sweep_gemm_14336x4096"
     if "k_gemm_q4k<4, 1, 1, 4, 2>" in name:
         return "gemm_other"
     if "k_gemm_q4k<1, 4, 1, 1, 2>" in name:

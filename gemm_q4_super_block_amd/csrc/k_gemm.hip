@@ -558,56 +558,67 @@ __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __re
   }
 }
 
-// ------------------------------------------------------------ mid tiles
-// 64 x 128 output tiles for shapes whose 128 x 256 tile grid cannot fill the
-// chip without splitting K (m=512, n=4096: 256 tiles).  Splitting K across
-// workgroups would need atomics (fp32 atomics at L2 are far slower than the
-// GEMM) or a second pass; here K is split four ways inside the workgroup.
-//   * 8 waves = 4 K slices x 2 N halves, two per SIMD.  Wave (kq, wn) owns all
-//     64 rows x 64 columns of its half (2 x 2 accumulators) and, in every
-//     64-wide K step, k = 32 p + 16 b + 8 h + (0..7) with p = kq / 2 (nibble
-//     parity), b = kq % 2 (byte half) and h the lane half: the low or high
-//     nibbles of quant bytes 16 b + 8 h .. +7.  Every weight is dequantized
-//     once per workgroup; the four K slices are summed through LDS at the end.
-//   * copies as in the 128 x 256 kernel: X (64 rows x 64 k = 8 KiB) through a
-//     9-slot ring, whole 144-byte super-blocks of the 128 weight rows (18 KiB)
-//     through a 4-slot ring issued three super-blocks ahead.
+// ------------------------------------------------------------ K-slice tiles
+// (32 TI) x (32 NJ TI) output tiles with K split four ways inside the
+// workgroup, for grids that the 128 x 256 tiles cannot fill without splitting
+// K across workgroups (m=512, n=4096: TI=NJ=2, 256 tiles of 64 x 128; m <= 32,
+// n=14336: TI=1, NJ=2, 224 tiles of 32 x 64).  Splitting K across workgroups would need fp32 atomics (about one per
+// L2 channel per clock, ~25 us for the m=512, n=4096 output) or a second pass.
+//   * 4 TI waves = 4 K slices x TI N halves.  Wave (kq, wn) owns all 32 TI
+//     rows x 32 NJ columns of its half (TI x NJ accumulators) and, in every 64-wide
+//     K step, k = 32 p + 16 b + 8 h + (0..7) with p = kq / 2 (nibble parity),
+//     b = kq % 2 (byte half) and h the lane half: the low or high nibbles of
+//     quant bytes 16 b + 8 h .. +7.  Every weight is dequantized once per
+//     workgroup; the four K slices are summed through LDS at the end.
+//   * copies as in the 128 x 256 kernel: X (32 TI rows x 64 k) through a
+//     9-slot ring, whole 144-byte super-blocks of the weight rows through a
+//     4-slot ring issued three super-blocks ahead; per wave one X copy per step
+//     and NJ + 1 weight copies per super-block.
 //   * the sub-block scales of a super-block are decoded once per workgroup
 //     (thread t: row t / 4, group t % 4) into LDS; waves read the (a, b) pairs
 //     of their parity.
 //   * quant bytes are read two steps ahead of their dequantization, which runs
 //     under the MFMAs of the step before their use.
-constexpr int kMBM = 64, kMBN = 128;
-constexpr int kMXSlot = kMBM * 128;            // 8 KiB
-constexpr int kMWSlot = kMBN * kBlockBytes;    // 18 KiB
-constexpr int kMXSlots = 9;
-constexpr int kMWOff = kMXSlots * kMXSlot;
-constexpr int kMSOff = kMWOff + 4 * kMWSlot;
-constexpr int kMSSlot = 4 * kMBN * 16;         // [parity][group pair][row] x (a, b, a', b')
-constexpr int kMLds = kMSOff + 2 * kMSSlot;    // 163840 bytes
-static_assert(kMLds <= 160 * 1024, "LDS budget of one workgroup");
-static_assert(8 * 16384 <= kMSOff, "the K-slice exchange reuses the rings");
-
-struct XFrag2 {
-  bf16x8_t a[2];  // [M block]
+template <int TI, int NJ>
+struct KSlice {
+  static constexpr int BM = 32 * TI, BN = 32 * NJ * TI, Threads = 256 * TI;
+  static constexpr int WCopies = NJ + 1;  // weight copies per wave per super-block
+  static constexpr int XSlot = BM * 128;
+  static constexpr int WSlot = BN * kBlockBytes;
+  static constexpr int XSlots = 9;
+  static constexpr int WOff = XSlots * XSlot;
+  static constexpr int SOff = WOff + 4 * WSlot;
+  static constexpr int SSlot = 4 * BN * 16;  // [parity][group pair][row] x (a, b, a', b')
+  static constexpr int Lds = SOff + 2 * SSlot;
+  static constexpr int ExWave = TI * NJ * 4 * 1024;  // one wave's partial tile
+  static_assert(Lds <= 160 * 1024, "LDS budget of one workgroup");
+  static_assert(4 * TI * ExWave <= SOff, "the K-slice exchange reuses the rings");
 };
 
-__global__ __launch_bounds__(512, 1) void k_gemm_q4k_64x128(const uint8_t* __restrict__ w,
-                                                            const uint16_t* __restrict__ x,
-                                                            float* __restrict__ y, int m, int n,
-                                                            int k, int tiles_m) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kMLds];
+template <int TI>
+struct XFragT {
+  bf16x8_t a[TI];  // [M block]
+};
+
+template <int TI, int NJ>
+__global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* __restrict__ w,
+                                                                 const uint16_t* __restrict__ x,
+                                                                 float* __restrict__ y, int m,
+                                                                 int n, int k, int tiles_m) {
+  using C = KSlice<TI, NJ>;
+  constexpr int kColsPerWave = 32 * NJ;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::Lds];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   const int h = lane >> 5;
   const int c32 = lane & 31;
   const int kq = wave & 3;
-  const int par = kq >> 1;  // nibble parity of this K slice
-  const int bh = kq & 1;    // byte half of this K slice
-  const int wn = wave >> 2; // N half
+  const int par = kq >> 1;   // nibble parity of this K slice
+  const int bh = kq & 1;     // byte half of this K slice
+  const int wn = wave >> 2;  // N half
   const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int m0 = tm * kMBM, n0 = tn * kMBN;
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int nsb = k >> 8, nst = k >> 6;
   const uint32_t row_bytes = static_cast<uint32_t>(nsb) * kBlockBytes;
   const int sb_rot = (tn * 7) % nsb;
@@ -622,13 +633,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_q4k_64x128(const uint8_t* __res
     const int c = (lane & 7) ^ swz(row);
     xsrc = x + static_cast<size_t>(min(m0 + row, m - 1)) * k + 8 * c;
   }
-  // Weight copies of this wave: 16-byte units 144 wave + {0, 64, 80} + lane of
-  // the slot (the third repeats 48 units of the second, same data and place).
-  constexpr int kUnit[3] = {0, 64, 80};
-  uint32_t woff[3];
+  // Weight copies of this wave: 16-byte units 72 NJ wave + {0, 64, 80} + lane
+  // (NJ = 2) or {0, 8} + lane (NJ = 1) of the slot; the last copy repeats some
+  // units of the one before, with the same data and place.
+  constexpr int kUnit[3] = {0, NJ == 2 ? 64 : 8, 80};
+  uint32_t woff[C::WCopies];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int U = 144 * wave + kUnit[i] + lane;
+  for (int i = 0; i < C::WCopies; ++i) {
+    const int U = 72 * NJ * wave + kUnit[i] + lane;
     const int col = (U * 7282) >> 16;  // U / 9 for U < 2304
     woff[i] = static_cast<uint32_t>(min(n0 + col, n - 1)) * row_bytes + (U - col * 9) * 16;
   }
@@ -637,49 +649,54 @@ __global__ __launch_bounds__(512, 1) void k_gemm_q4k_64x128(const uint8_t* __res
     const int sc = min(s, nst - 1);
     const int ps = 4 * phys_sb(sc >> 2) + (sc & 3);
     copy16_to_lds(xsrc + static_cast<size_t>(ps) * 64,
-                  __builtin_amdgcn_readfirstlane(lds0 + slot * kMXSlot + wave * 1024));
+                  __builtin_amdgcn_readfirstlane(lds0 + slot * C::XSlot + wave * 1024));
   };
   auto copy_w = [&](int S, int slot) {
     const uint8_t* base = w + static_cast<size_t>(phys_sb(S)) * kBlockBytes;
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-      copy16_to_lds(base + woff[i], __builtin_amdgcn_readfirstlane(
-                                        lds0 + kMWOff + slot * kMWSlot + (144 * wave + kUnit[i]) * 16));
+    for (int i = 0; i < C::WCopies; ++i)
+      copy16_to_lds(base + woff[i],
+                    __builtin_amdgcn_readfirstlane(lds0 + C::WOff + slot * C::WSlot +
+                                                   (72 * NJ * wave + kUnit[i]) * 16));
   };
-  auto read_x = [&](int slot, XFrag2& A) {
-    const uint8_t* xb = smem + slot * kMXSlot;
+  auto read_x = [&](int slot, XFragT<TI>& A) {
+    const uint8_t* xb = smem + slot * C::XSlot;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < TI; ++i) {
       const int r = 32 * i + c32;
       const int ch = 4 * par + 2 * bh + h;
       A.a[i] = *reinterpret_cast<const bf16x8_t*>(xb + r * 128 + ((ch ^ swz(r)) << 4));
     }
   };
-  auto read_q = [&](int slot, int g, uint2 (&Q)[2]) {
-    const uint8_t* wb = smem + kMWOff + slot * kMWSlot;
+  auto read_q = [&](int slot, int g, uint2 (&Q)[NJ]) {
+    const uint8_t* wb = smem + C::WOff + slot * C::WSlot;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = 64 * wn + 32 * j + c32;
+    for (int j = 0; j < NJ; ++j) {
+      const int col = kColsPerWave * wn + 32 * j + c32;
       const uint4 v = *reinterpret_cast<const uint4*>(wb + col * kBlockBytes + 16 + 32 * g + 16 * bh);
       Q[j] = h ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
     }
   };
   auto scales_store = [&](int wslot, int ss) {
     const int col = t >> 2, g = t & 3;
-    const uint4 hd = *reinterpret_cast<const uint4*>(smem + kMWOff + wslot * kMWSlot + col * kBlockBytes);
+    // (With NJ = 1 half the threads have no row; with NJ = 2 the test folds away,
+    // so the step stays one basic block for the scheduling hints below.)
+    if (C::Threads / 4 > C::BN && col >= C::BN) return;
+    const uint4 hd =
+        *reinterpret_cast<const uint4*>(smem + C::WOff + wslot * C::WSlot + col * kBlockBytes);
     const GroupScales gs = group_scales(hd, g);
-    uint8_t* sp = smem + kMSOff + ss * kMSSlot;
-    *reinterpret_cast<f2_t*>(sp + ((g >> 1) * kMBN + col) * 16 + (g & 1) * 8) = f2_t{gs.a_lo, gs.b_lo};
-    *reinterpret_cast<f2_t*>(sp + ((2 + (g >> 1)) * kMBN + col) * 16 + (g & 1) * 8) = f2_t{gs.a_hi, gs.b_hi};
+    uint8_t* sp = smem + C::SOff + ss * C::SSlot;
+    *reinterpret_cast<f2_t*>(sp + ((g >> 1) * C::BN + col) * 16 + (g & 1) * 8) = f2_t{gs.a_lo, gs.b_lo};
+    *reinterpret_cast<f2_t*>(sp + ((2 + (g >> 1)) * C::BN + col) * 16 + (g & 1) * 8) = f2_t{gs.a_hi, gs.b_hi};
   };
-  auto scales_load = [&](int ss, float (&sa)[4][2], float (&sb)[4][2]) {
-    const uint8_t* sp = smem + kMSOff + ss * kMSSlot;
+  auto scales_load = [&](int ss, float (&sa)[4][NJ], float (&sb)[4][NJ]) {
+    const uint8_t* sp = smem + C::SOff + ss * C::SSlot;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = 64 * wn + 32 * j + c32;
+    for (int j = 0; j < NJ; ++j) {
+      const int col = kColsPerWave * wn + 32 * j + c32;
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
-        const f4_t v = *reinterpret_cast<const f4_t*>(sp + ((par * 2 + gp) * kMBN + col) * 16);
+        const f4_t v = *reinterpret_cast<const f4_t*>(sp + ((par * 2 + gp) * C::BN + col) * 16);
         sa[2 * gp][j] = v.x;
         sb[2 * gp][j] = v.y;
         sa[2 * gp + 1][j] = v.z;
@@ -688,23 +705,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_q4k_64x128(const uint8_t* __res
     }
   };
   const int nshift = 4 * par;
-  auto dequant = [&](const uint2 (&Q)[2], const float (&a)[2], const float (&b)[2],
-                     bf16x8_t (&B)[2]) {
+  auto dequant = [&](const uint2 (&Q)[NJ], const float (&a)[NJ], const float (&b)[NJ],
+                     bf16x8_t (&B)[NJ]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) B[j] = dequant8_bf16(Q[j].x, Q[j].y, nshift, a[j], b[j]);
+    for (int j = 0; j < NJ; ++j) B[j] = dequant8_bf16(Q[j].x, Q[j].y, nshift, a[j], b[j]);
   };
-  f16x_t acc[2][2];
+  f16x_t acc[TI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  auto mfmas = [&](const XFrag2& A, const bf16x8_t (&B)[2]) {
+  auto mfmas = [&](const XFragT<TI>& A, const bf16x8_t (&B)[NJ]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[i], B[j], acc[i][j], 0, 0, 0);
   };
 
@@ -718,17 +735,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_q4k_64x128(const uint8_t* __res
 #pragma unroll
   for (int s = 5; s <= 8; ++s) copy_x(s, s);
   copy_w(2, 2);
-  wait_copies_barrier<8 + 2 * 3>();  // X(0), W(0) landed
-  XFrag2 A0, A1;
-  uint2 Q0[2], Q1[2];
-  float sa[4][2], sb[4][2];
+  constexpr int CW = C::WCopies;
+  wait_copies_barrier<8 + 2 * CW>();  // X(0), W(0) landed
+  XFragT<TI> A0, A1;
+  uint2 Q0[NJ], Q1[NJ];
+  float sa[4][NJ], sb[4][NJ];
   scales_store(0, 0);
   read_q(0, 0, Q0);
   read_q(0, 1, Q1);
   read_x(0, A0);
-  wait_copies_barrier<8 + 2 * 3>();
+  wait_copies_barrier<8 + 2 * CW>();
   scales_load(0, sa, sb);
-  bf16x8_t B0[2], B1[2];
+  bf16x8_t B0[NJ], B1[NJ];
   dequant(Q0, sa[0], sb[0], B0);
 
   int xs = 0;  // X slot of step s
@@ -737,11 +755,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_q4k_64x128(const uint8_t* __res
   // reads the X fragments of step s+1, the quant bytes of step s+2 (into Qb)
   // and at phase 2 decodes the scales of S+1; MFMAs of step s with Bc while
   // Bn = B(s+1) is dequantized from Qa, read one step earlier.
-  auto step = [&](int s, int p, XFrag2& Ac, XFrag2& An, uint2 (&Qa)[2], uint2 (&Qb)[2],
-                  bf16x8_t (&Bc)[2], bf16x8_t (&Bn)[2]) {
-    const int xn = xs == kMXSlots - 1 ? 0 : xs + 1;
+  auto step = [&](int s, int p, XFragT<TI>& Ac, XFragT<TI>& An, uint2 (&Qa)[NJ], uint2 (&Qb)[NJ],
+                  bf16x8_t (&Bc)[NJ], bf16x8_t (&Bn)[NJ]) {
+    const int xn = xs == C::XSlots - 1 ? 0 : xs + 1;
     const int ws1 = (ws + 1) & 3;
-    copy_x(s + kMXSlots, xs);
+    copy_x(s + C::XSlots, xs);
     if (p == 3) copy_w((s >> 2) + 3, (ws + 3) & 3);
     read_x(xn, An);
     read_q(p < 2 ? ws : ws1, (p + 2) & 3, Qb);
@@ -755,7 +773,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_q4k_64x128(const uint8_t* __res
       dequant(Qa, sa[0], sb[0], Bn);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NJ * TI; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     }
@@ -763,11 +781,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_q4k_64x128(const uint8_t* __res
     // End of step s: every copy issued up to step s-7 has landed (X(s+2));
     // at phase 1 up to step s-6 (W(S+1), read from phase 2 on).
     if (p == 1)
-      wait_copies_barrier<6 + 3>();
+      wait_copies_barrier<6 + CW>();
     else if (p == 2)
-      wait_copies_barrier<7 + 3>();
+      wait_copies_barrier<7 + CW>();
     else
-      wait_copies_barrier<7 + 2 * 3>();
+      wait_copies_barrier<7 + 2 * CW>();
     __builtin_amdgcn_sched_barrier(0);
     xs = xn;
     if (p == 3) ws = ws1;
@@ -780,38 +798,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_q4k_64x128(const uint8_t* __res
   }
   wait_copies_barrier<0>();
 
-  // Sum the K slices: wave w writes its 64 x 64 partial to region w; wave
-  // (kq, wn) then finishes quarter kq (M block kq / 2, accumulator registers
-  // 8 (kq % 2) .. +7) of N half wn from the four regions of that half.
-  uint8_t* const reg_out = smem + wave * 16384;
+  // Sum the K slices: wave w writes its partial tile (TI x NJ accumulators,
+  // one 1-KiB unit per 4 registers) to region w; wave (kq, wn) then finishes
+  // units kq U/4 .. (kq+1) U/4 - 1 (U = 4 TI NJ) of N half wn from the four
+  // regions of that half.
+  uint8_t* const reg_out = smem + wave * C::ExWave;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<f4_t*>(reg_out + ((i * 2 + j) * 4 + r4) * 1024 + lane * 16) =
+        *reinterpret_cast<f4_t*>(reg_out + ((i * NJ + j) * 4 + r4) * 1024 + lane * 16) =
             f4_t{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  const int qi = kq >> 1, qr = (kq & 1) * 2;
+  constexpr int kUnitsPerWave = TI * NJ;  // U / 4
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + 64 * wn + 32 * j + c32;
+  for (int uu = 0; uu < kUnitsPerWave; ++uu) {
+    const int u = kq * kUnitsPerWave + uu;
+    const int i = u / (NJ * 4), j = (u >> 2) % NJ, r4 = u & 3;
+    const int col = n0 + kColsPerWave * wn + 32 * j + c32;
+    f4_t v = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int r4 = qr + rr;
-      f4_t v = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int src = 0; src < 4; ++src)
+      v += *reinterpret_cast<const f4_t*>(smem + (wn * 4 + src) * C::ExWave + u * 1024 + lane * 16);
+    // Accumulator r of a 32x32 tile holds row 8*(r/4) + 4*h + r%4, column lane%32.
 #pragma unroll
-      for (int src = 0; src < 4; ++src)
-        v += *reinterpret_cast<const f4_t*>(smem + (wn * 4 + src) * 16384 +
-                                            ((qi * 2 + j) * 4 + r4) * 1024 + lane * 16);
-      // Accumulator r of a 32x32 tile holds row 8*(r/4) + 4*h + r%4, column lane%32.
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * r4 + e;
-        const int row = m0 + 32 * qi + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < m && col < n) y[static_cast<size_t>(row) * n + col] = v[e];
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * r4 + e;
+      const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < m && col < n) y[static_cast<size_t>(row) * n + col] = v[e];
     }
   }
 }
@@ -831,6 +847,14 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
   const int steps = ki / kBK;
   const int tiles_n = (ni + kBN - 1) / kBN;
   if (mi <= 32) {
+    using Small = KSlice<1, 2>;
+    const int small_n = (ni + Small::BN - 1) / Small::BN;
+    if (small_n >= kGemmSmallTiles) {
+      // One 32 x 64 tile per workgroup, K split inside the workgroup.
+      hipLaunchKernelGGL((k_gemm_q4k_kslice<1, 2>), dim3(small_n), dim3(Small::Threads), 0,
+                         stream, w, x, y, mi, ni, ki, 1);
+      return hipGetLastError();
+    }
     // Small batch: one 32-row slice, the four waves split the 128 weight rows.
     return launch<1, 4, 1, 1, 2>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
   }
@@ -842,11 +866,12 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
                        mi, ni, ki, big_m, big_n, xcd ? 1 : 0);
     return hipGetLastError();
   }
-  const int mid_m = (mi + kMBM - 1) / kMBM, mid_n = (ni + kMBN - 1) / kMBN;
+  using Mid = KSlice<2, 2>;
+  const int mid_m = (mi + Mid::BM - 1) / Mid::BM, mid_n = (ni + Mid::BN - 1) / Mid::BN;
   if (mid_m * mid_n >= kGemmMidTiles) {
     // Enough 64 x 128 tiles to fill most CUs without splitting K.
-    hipLaunchKernelGGL(k_gemm_q4k_64x128, dim3(mid_m * mid_n), dim3(512), 0, stream, w, x, y, mi,
-                       ni, ki, mid_m);
+    hipLaunchKernelGGL((k_gemm_q4k_kslice<2, 2>), dim3(mid_m * mid_n), dim3(Mid::Threads), 0,
+                       stream, w, x, y, mi, ni, ki, mid_m);
     return hipGetLastError();
   }
   // 128 x 128 tiles, two workgroups per CU.

@@ -19,6 +19,9 @@ constexpr int kGemmBigTiles = 128;
 // Other prefill GEMMs (M > 32) with at least this many 64 x 128 output tiles
 // use the mid-tile kernel; smaller grids split K over 128 x 128 tiles.
 constexpr int kGemmMidTiles = 192;
+// Batches of at most 32 rows with at least this many 64-row weight tiles use
+// the 32 x 64 K-slice kernel; smaller ones split K over 128-row tiles.
+constexpr int kGemmSmallTiles = 128;
 // Batch-1 matrices of at most this many rows run 16 waves per workgroup.
 constexpr int64_t kGemvWideRows = 8192;
 

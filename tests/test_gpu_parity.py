@@ -269,6 +269,30 @@ def test_gemm_tile_kernels(q4k, m, n, k):
     assert np.all(np.isfinite(Y))
 
 
+# Batches of at most 32 rows with >= 128 weight tiles of 64 rows run the 32 x 64
+# K-slice kernel: ragged N (one 8-row last tile) at one super-block of K, three
+# super-blocks with 17 rows, and every output of a 7-row batch.
+@pytest.mark.parametrize("m,n,k", [(5, 8200, 256), (17, 9000, 768), (32, 16384, 512)])
+def test_gemm_small_batch_kslice(q4k, m, n, k):
+    w = synth.q4k_weights(n, k, seed=m + n)
+    xb = synth.normal_bf16((m, k), seed=m + n)
+    Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
+    cols = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, n - 65, n - 64, n - 9, n - 1],
+                                     np.random.default_rng(n).integers(0, n, 54)]))
+    Yr, A = oracle.gemm_cols(w, xb, n, k, cols)
+    assert_within(Y[:, cols], Yr, A, GEMM_TOL, "gemm %dx%dx%d" % (m, n, k))
+    assert np.all(np.isfinite(Y))
+
+
+def test_gemm_small_batch_kslice_full_output(q4k):
+    m, n, k = 7, 8192, 256
+    w = synth.q4k_weights(n, k, seed=78)
+    xb = synth.normal_bf16((m, k), seed=78)
+    Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
+    Yr, A = oracle.gemm(w, xb, n, k)
+    assert_within(Y, Yr, A, GEMM_TOL, "gemm 7x8192x256")
+
+
 def test_gemm_mid_tile_kernel_full_output(q4k):
     # 4 x 48 = 192 tiles of 64 x 128 (the smallest mid-tile grid), every output
     # against the oracle; M = 200 leaves an 8-row last M-tile.
