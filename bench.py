@@ -58,7 +58,8 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one device copy of 256 MiB (counter calibration)")
     p.add_argument("--only", default="",
-                   help="comma list of kernels to run (gemv,sweep_gemv,sweep_gemm,mlp,gemm,dequant)")
+                   help="comma list of kernels to run "
+                        "(gemv,sweep_gemv,sweep_gemm,mlp,gemm,dequant,read_probe)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
     p.add_argument("--eager-only", action="store_true",
                    help="time only the eagerly enqueued launches (no HIP graph replay)")
@@ -69,6 +70,16 @@ def parse():
     p.add_argument("--out", default="", help="summary output file (markdown)")
     p.add_argument("--workload-hint", default="", help="the --only value the profiled run used")
     return p.parse_args()
+
+
+def read_probe_runner(_lib, rot, nbytes, torch):
+    """Launch the streaming read probe over the first array of each rotating copy: the
+    plain-read ceiling that a weight-streaming kernel of the same footprint can reach."""
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def run(i, sp):
+        _lib.check(_lib.q4k_read_probe(rot[i][0].data_ptr(), nbytes, sink.data_ptr(), sp))
+    return run
 
 
 class Rotor:
@@ -194,6 +205,14 @@ def main():
             _lib.check(_lib.q4k_dequantize_bf16(wd.data_ptr(), od.data_ptr(), n, k, sp))
         kernels.append(("dequant_bf16_4096x4096", run_dq, nbytes, 0, rot))
 
+    # ---- plain streaming read of the same weight footprints (ceiling for the GEMV path)
+    if want("read_probe"):
+        for n, k in ((D_MODEL, D_MODEL), (D_FF, D_MODEL)):
+            nbytes = q4k_bytes(n, k)
+            rot = Rotor(torch, [synth.q4k_weights(n, k, seed=0)], nbytes)
+            kernels.append(("read_probe_%d" % nbytes, read_probe_runner(_lib, rot, nbytes, torch),
+                            nbytes, 0, rot))
+
     if args.copy_probe:
         # one elementwise kernel that reads 256 MiB and writes 256 MiB: the reference
         # dispatch for scaling the FETCH_SIZE / WRITE_SIZE counters
@@ -300,6 +319,8 @@ def main():
             "gemm_m512_mfma_bf16": round(100 * gemm["mfma_frac"], 2) if gemm else None,
         },
         "gemm_m512_tflops": gemm["tflops"] if gemm else None,
+        "read_ceiling_gbs": {name[len("read_probe_"):]: r["gbs"] for name, r in per.items()
+                             if name.startswith("read_probe_")} or None,
         "roofline": None,
         "roofline_gemm": None,
         "cpu_baseline": cpu,
@@ -376,6 +397,8 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "sweep_gemv_14336x4096_batched"
     if "k_dequant_q4k<true>" in name:
         return "dequant_bf16_4096x4096"
+    if "k_read_probe" in name:
+        return "read_probe"
     if "k_zero_f32" in name:
         return "split_k_zero_fill"
     if "copy" in name.lower() or "elementwise" in name:
@@ -404,7 +427,8 @@ def _find(d, suffix):
 def summarize_profile(args):
     """Write a markdown summary of rocprofv3 runs: per-workload kernel durations from the
     kernel trace; with counter runs, HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, KiB,
-    scaled by what the same counters read for the 256 MiB copy probe)."""
+    scaled by what the same counters read for the 256 MiB copy probe), and with a fourth
+    directory the MFMA and VALU utilization of each kernel."""
     import statistics
     dirs = args.summarize_profile
     trace = _read_csv(_find(dirs[0], "kernel_trace.csv"))
@@ -458,6 +482,26 @@ def summarize_profile(args):
         lines += ["", "Calibration: an elementwise kernel that reads and writes 256 MiB (262144 KiB each way) "
                   "read FETCH_SIZE = %s KiB and WRITE_SIZE = %s KiB; scale factors (262144 / reading): %s." % (
                       cal.get("FETCH_SIZE"), cal.get("WRITE_SIZE"), scale)]
+    if len(dirs) >= 4:
+        # Utilization pass: MfmaUtil (% of SIMD cycles with the matrix core busy), VALUBusy (% of
+        # CU cycles issuing VALU) and the bf16 MFMA FLOP count (MOPS x 512).
+        util = {}
+        for r in _read_csv(_find(dirs[3], "counter_collection.csv")):
+            kname = _short_name(r["Kernel_Name"])
+            gx = int(r["Grid_Size"]) if "Grid_Size" in r else 0
+            lds = int(r.get("LDS_Block_Size", 0))
+            util.setdefault((kname, lds, gx), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        lines += ["", "Compute utilization per dispatch from counters, median over dispatches:", "",
+                  "| kernel | LDS B | grid | MfmaUtil % | VALUBusy % | bf16 MFMA FLOP |", "|---|---|---|---|---|---|"]
+        for (kname, lds, gx), cs in sorted(util.items()):
+            if "elementwise" in kname or "copyBuffer" in kname:
+                continue
+            med = {c: statistics.median(v) for c, v in cs.items()}
+            mops = med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+            lines.append("| `%s` | %d | %d | %.1f | %.1f | %s |" % (
+                kname[:60], lds, gx, med.get("MfmaUtil", -1), med.get("VALUBusy", -1),
+                "%.4g" % (mops * 512) if mops else "0"))
     if traffic_bytes:
         lines += ["", "traffic_json: " + json.dumps({"source_hash": kernel_source_hash(),
                                                      "bytes_per_launch": traffic_bytes})]

@@ -35,6 +35,7 @@ SIGNATURES = {
     "q4k_swiglu_mlp": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "q4k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q4k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "q4k_read_probe": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
 }
 
 
@@ -119,3 +120,7 @@ def q4k_dequantize_f32(w, out, n, k, stream) -> int:
 
 def q4k_dequantize_bf16(w, out, n, k, stream) -> int:
     return load().q4k_dequantize_bf16(w, out, n, k, stream)
+
+
+def q4k_read_probe(buf, nbytes, sink, stream) -> int:
+    return load().q4k_read_probe(buf, nbytes, sink, stream)

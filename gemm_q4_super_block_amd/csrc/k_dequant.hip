@@ -1,10 +1,11 @@
-// k_dequant.hip -- diagnostic export of a Q4_K matrix as fp32 or bf16.
+// k_dequant.hip -- diagnostic export of a Q4_K matrix as fp32 or bf16, and a
+// streaming read probe.
 //
-// Runs the same device routines as the GEMV (group_scales, dequant_dword)
-// and the GEMM tile fill (dequant16_bf16), so the bit-exact check of this
-// export ("CPU kernel parity ..." PR page, "Validation": every variant
-// bit-exact against the reference decode) covers what the other kernels
-// compute.
+// The export runs the same device routines as the GEMV (group_scales,
+// dequant_dword) and the GEMM kernels (dequant8_bf16, through
+// dequant16_bf16), so the bit-exact check of this export ("CPU kernel parity
+// ..." PR page, "Validation": every variant bit-exact against the reference
+// decode) covers what the other kernels compute.
 //
 // One thread per 16 quant bytes: (row, block, group g, half hh).  It writes
 // the 16 low-nibble weights 64g+16hh.. and the 16 high-nibble weights
@@ -62,7 +63,39 @@ hipError_t launch(const uint8_t* w, void* out, int64_t n, int64_t k, hipStream_t
   return hipGetLastError();
 }
 
+// A plain streaming read of a buffer with 16-byte loads, four in flight per
+// thread: the read rate a working set of that size allows on this device,
+// measured beside the GEMV kernels on the same cold buffers.  The loaded words
+// feed a value that is stored only on a 2^-32 coincidence, which keeps the
+// loads without writing anything in practice.
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, int64_t n16,
+                                                    uint32_t* __restrict__ sink) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= (a.x + a.y + a.z + a.w) ^ (b.x + b.y + b.z + b.w) ^ (c.x + c.y + c.z + c.w) ^
+           (d.x + d.y + d.z + d.w);
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x + a.y + a.z + a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
+                             hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  const int64_t want = (n16 + 1023) / 1024;  // about four loads per thread
+  const unsigned grid = static_cast<unsigned>(want < 1 ? 1 : (want > 2048 ? 2048 : want));
+  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, stream,
+                     static_cast<const uint4*>(buf), n16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant_f32(const uint8_t* w, float* out, int64_t n, int64_t k,
                               hipStream_t stream) {

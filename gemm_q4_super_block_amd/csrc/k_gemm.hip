@@ -281,21 +281,6 @@ __device__ __forceinline__ void wait_copies_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// 8 weights of one MFMA slice: nibbles (shift 0: low, 4: high) of the 8
-// quant bytes d0, d1, as bf16 of fma(a, q*2^-9, -b).
-__device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t d0, uint32_t d1, int shift, float a,
-                                                  float b) {
-  const uint32_t l0 = (d0 >> shift) & 0x0F0F0F0Fu;
-  const uint32_t l1 = (d1 >> shift) & 0x0F0F0F0Fu;
-  const f2_t p0 = fp8x2_lo(l0), p1 = fp8x2_hi(l0), p2 = fp8x2_lo(l1), p3 = fp8x2_hi(l1);
-  return __builtin_bit_cast(
-      bf16x8_t,
-      make_uint4(pack_bf16x2(__builtin_fmaf(a, p0.x, -b), __builtin_fmaf(a, p0.y, -b)),
-                 pack_bf16x2(__builtin_fmaf(a, p1.x, -b), __builtin_fmaf(a, p1.y, -b)),
-                 pack_bf16x2(__builtin_fmaf(a, p2.x, -b), __builtin_fmaf(a, p2.y, -b)),
-                 pack_bf16x2(__builtin_fmaf(a, p3.x, -b), __builtin_fmaf(a, p3.y, -b))));
-}
-
 struct XFrag {
   bf16x8_t a[2][4];  // [slice u][M block i]
 };

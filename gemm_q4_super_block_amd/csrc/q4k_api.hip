@@ -212,4 +212,18 @@ int q4k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k, void
                   "q4k_dequantize_bf16");
 }
 
+int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(Q4K_ERR_INVALID_ARG, "q4k_read_probe: null pointer");
+  if (bytes < 16 || bytes % 16 != 0)
+    return fail(Q4K_ERR_INVALID_ARG, "q4k_read_probe: bytes=%lld is not a positive multiple of 16",
+                (long long)bytes);
+  if (!aligned16(buf) || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return fail(Q4K_ERR_ALIGN, "q4k_read_probe: buf must be 16-byte and sink 4-byte aligned");
+  if (overlap(sink, 4, buf, static_cast<size_t>(bytes)))
+    return fail(Q4K_ERR_INVALID_ARG, "q4k_read_probe: sink overlaps buf");
+  if (int rc = check_device()) return rc;
+  return launched(q4k::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)),
+                  "q4k_read_probe");
+}
+
 }  // extern "C"

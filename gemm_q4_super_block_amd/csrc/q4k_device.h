@@ -101,22 +101,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Dequantize 16 quant bytes of group g (one 16-byte load) to bf16: lo8[0..7]
-// are the 16 low-nibble weights (sub-block 2g) as 8 packed pairs, hi8[0..7]
-// the 16 high-nibble weights (sub-block 2g+1).  This is the GEMM's LDS fill
-// and the bf16 diagnostic export.
+// 8 weights as bf16: the nibbles at bit `shift` (0: low, 4: high) of the 8
+// quant bytes in d0, d1 (byte order), each fma(a, q*2^-9, -b) rounded to
+// nearest even, packed in pairs (first weight in the low half).  This is the
+// MFMA operand routine of the GEMM kernels.
+__device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t d0, uint32_t d1, int shift, float a,
+                                                  float b) {
+  const uint32_t l0 = (d0 >> shift) & 0x0F0F0F0Fu;
+  const uint32_t l1 = (d1 >> shift) & 0x0F0F0F0Fu;
+  const f2_t p0 = fp8x2_lo(l0), p1 = fp8x2_hi(l0), p2 = fp8x2_lo(l1), p3 = fp8x2_hi(l1);
+  return __builtin_bit_cast(
+      bf16x8_t,
+      make_uint4(pack_bf16x2(__builtin_fmaf(a, p0.x, -b), __builtin_fmaf(a, p0.y, -b)),
+                 pack_bf16x2(__builtin_fmaf(a, p1.x, -b), __builtin_fmaf(a, p1.y, -b)),
+                 pack_bf16x2(__builtin_fmaf(a, p2.x, -b), __builtin_fmaf(a, p2.y, -b)),
+                 pack_bf16x2(__builtin_fmaf(a, p3.x, -b), __builtin_fmaf(a, p3.y, -b))));
+}
+
+// Dequantize 16 quant bytes of group g (one 16-byte load) to bf16 through
+// dequant8_bf16: lo8[0..7] are the 16 low-nibble weights (sub-block 2g) as 8
+// packed pairs, hi8[0..7] the 16 high-nibble weights (sub-block 2g+1).  This
+// is the bf16 diagnostic export and the tile fill of the split-K GEMM.
 __device__ __forceinline__ void dequant16_bf16(uint4 q, const GroupScales& s, uint32_t lo8[8],
                                                uint32_t hi8[8]) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float lo[4], hi[4];
-    dequant_dword(w[i], s, lo, hi);
-    lo8[2 * i + 0] = pack_bf16x2(lo[0], lo[1]);
-    lo8[2 * i + 1] = pack_bf16x2(lo[2], lo[3]);
-    hi8[2 * i + 0] = pack_bf16x2(hi[0], hi[1]);
-    hi8[2 * i + 1] = pack_bf16x2(hi[2], hi[3]);
-  }
+  const uint4 l0 = __builtin_bit_cast(uint4, dequant8_bf16(q.x, q.y, 0, s.a_lo, s.b_lo));
+  const uint4 l1 = __builtin_bit_cast(uint4, dequant8_bf16(q.z, q.w, 0, s.a_lo, s.b_lo));
+  const uint4 h0 = __builtin_bit_cast(uint4, dequant8_bf16(q.x, q.y, 4, s.a_hi, s.b_hi));
+  const uint4 h1 = __builtin_bit_cast(uint4, dequant8_bf16(q.z, q.w, 4, s.a_hi, s.b_hi));
+  lo8[0] = l0.x; lo8[1] = l0.y; lo8[2] = l0.z; lo8[3] = l0.w;
+  lo8[4] = l1.x; lo8[5] = l1.y; lo8[6] = l1.z; lo8[7] = l1.w;
+  hi8[0] = h0.x; hi8[1] = h0.y; hi8[2] = h0.z; hi8[3] = h0.w;
+  hi8[4] = h1.x; hi8[5] = h1.y; hi8[6] = h1.z; hi8[7] = h1.w;
 }
 
 __device__ __forceinline__ uint4 load16(const uint8_t* p) {

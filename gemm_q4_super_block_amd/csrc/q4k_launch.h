@@ -39,4 +39,7 @@ hipError_t launch_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64
 hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);
 
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
+                             hipStream_t stream);
+
 }  // namespace q4k

@@ -101,9 +101,10 @@ int q4k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
  *   x_bf16: bf16 bit patterns [m, k] row-major, 16-byte aligned.
  *   y: fp32 [m, n] row-major, 16-byte aligned.
  *   m >= 1, n >= 1, k >= 256 with k % 256 == 0.
- * Weight tiles are dequantized to bf16 (round to nearest even of the fp32
- * weight) in LDS and contracted on bf16 MFMA with fp32 accumulation; each
- * output lies within 1e-2 * sum_c |W[j,c] X[i,c]| of the exact value.
+ * Weights are dequantized to bf16 (round to nearest even of the fp32 weight)
+ * -- in registers or through LDS, by shape -- and contracted on bf16 MFMA
+ * with fp32 accumulation; each output lies within 1e-2 * sum_c |W[j,c] X[i,c]|
+ * of the exact value.
  * [P1 "SLM-Tiled GEMM and Graph Recording"; P3 tile kernels.] */
 int q4k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m,
              int64_t n, int64_t k, void* stream);
@@ -131,6 +132,14 @@ int q4k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k,
                        void* stream);
 int q4k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
                         void* stream);
+
+/* Measurement aid, not part of the method: streams `bytes` of buf with
+ * 16-byte loads and discards them (sink, 4 bytes of device memory, is
+ * written only on a 2^-32 coincidence of the data).  Timed on the same cold
+ * buffers as a GEMV, it gives the read rate that working-set size allows.
+ *   buf 16-byte aligned, bytes a positive multiple of 16; sink 4-byte aligned.
+ * Errors: Q4K_ERR_INVALID_ARG, Q4K_ERR_ALIGN, Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

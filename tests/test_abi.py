@@ -123,3 +123,13 @@ def test_ops_reject_cpu_tensors():
     w = torch.zeros((4, 144), dtype=torch.uint8)
     with pytest.raises(ValueError):
         q4k.gemv(w, torch.zeros(256))
+
+
+def test_read_probe_rejects_bad_arguments():
+    assert _lib.q4k_read_probe(0, 4096, A, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q4k_read_probe(A, 0, 2 * A, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q4k_read_probe(A, 4100, 2 * A, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q4k_read_probe(A + 4, 4096, 2 * A, None) == _lib.Q4K_ERR_ALIGN
+    assert _lib.q4k_read_probe(A, 4096, 2 * A + 2, None) == _lib.Q4K_ERR_ALIGN
+    assert _lib.q4k_read_probe(A, 4096, A + 64, None) == _lib.Q4K_ERR_INVALID_ARG  # sink in buf
+    assert _lib.q4k_last_error().startswith("q4k_read_probe")

@@ -328,3 +328,18 @@ def test_gemm_m1_equals_bf16_weight_dot(q4k):
     ref = Xf @ Wf.T
     scale = np.abs(Xf) @ np.abs(Wf.T)
     assert np.all(np.abs(Y - ref) <= 1e-5 * scale)
+
+
+# ------------------------------------------------------------------ read probe
+
+@pytest.mark.parametrize("nbytes", [16, 144 * 4096, 9437184 + 48])
+def test_read_probe_runs_and_leaves_sink(q4k, nbytes):
+    """The streaming read probe (a measurement aid) reads the whole buffer and, for data
+    whose folded sum is not its sentinel value, leaves the sink untouched."""
+    from gemm_q4_super_block_amd import _lib
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    assert _lib.q4k_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream) == _lib.Q4K_OK
+    torch.cuda.synchronize()
+    assert sink.cpu().tolist() == [7, 7, 7, 7]
