@@ -285,12 +285,30 @@ struct XFrag {
   bf16x8_t a[2][4];  // [slice u][M block i]
 };
 
-// xcd_map: 1 = all M-tiles of an N-tile on one XCD (tiles_n % 8 == 0).
+// Output tile of workgroup `bid`.  Workgroups are dealt to the eight XCDs in
+// turn (XCD = bid mod 8), each with its own L2.  With xcd_gm = 0 the tiles run
+// M-fastest.  Otherwise the tile grid is cut into gm x (8 / gm) blocks, one per
+// XCD, so that an XCD's workgroups share their X rows and weight columns in its
+// L2 instead of every XCD fetching all of W (needs tiles_m % gm == 0 and
+// tiles_n % (8 / gm) == 0; the host picks gm).
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int xcd_gm,
+                                            int& tm, int& tn) {
+  if (xcd_gm) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int a = tiles_m / xcd_gm;  // M-tiles per XCD block
+    tm = (xcd % xcd_gm) * a + slot % a;
+    tn = (xcd / xcd_gm) * (tiles_n / (8 / xcd_gm)) + slot / a;
+  } else {
+    tm = bid % tiles_m;
+    tn = bid / tiles_m;
+  }
+}
+
 __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __restrict__ w,
                                                              const uint16_t* __restrict__ x,
                                                              float* __restrict__ y, int m, int n,
                                                              int k, int tiles_m, int tiles_n,
-                                                             int xcd_map) {
+                                                             int xcd_gm) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kWLds];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -300,14 +318,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __re
   const int kp = wave >> 1;  // K parity: 0 = low nibbles, 1 = high nibbles
   const int wn = wave & 1;   // N half
   int tm, tn;
-  if (xcd_map) {
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    tm = slot % tiles_m;
-    tn = xcd * (tiles_n / 8) + slot / tiles_m;
-  } else {
-    tm = blockIdx.x % tiles_m;
-    tn = blockIdx.x / tiles_m;
-  }
+  tile_coords(blockIdx.x, tiles_m, tiles_n, xcd_gm, tm, tn);
   const int m0 = tm * kWBM, n0 = tn * kWBN;
   const int nsb = k >> 8;                     // super-blocks along K
   const int nst = k >> 6;                     // 64-wide steps
@@ -589,7 +600,8 @@ template <int TI, int NJ>
 __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* __restrict__ w,
                                                                  const uint16_t* __restrict__ x,
                                                                  float* __restrict__ y, int m,
-                                                                 int n, int k, int tiles_m) {
+                                                                 int n, int k, int tiles_m,
+                                                                 int tiles_n, int xcd_gm) {
   using C = KSlice<TI, NJ>;
   constexpr int kColsPerWave = 32 * NJ;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::Lds];
@@ -602,7 +614,8 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   const int par = kq >> 1;   // nibble parity of this K slice
   const int bh = kq & 1;     // byte half of this K slice
   const int wn = wave >> 2;  // N half
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, xcd_gm, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int nsb = k >> 8, nst = k >> 6;
   const uint32_t row_bytes = static_cast<uint32_t>(nsb) * kBlockBytes;
@@ -817,6 +830,25 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   }
 }
 
+// XCD blocking of a tiles_m x tiles_n grid of bm x bn tiles (see tile_coords):
+// the gm in {1, 2, 4, 8} that divides the grid and minimizes the bytes one
+// XCD's workgroups stream per K element (2 per X row, 9/16 per weight row),
+// or 0 if none divides it.
+int xcd_groups(int tiles_m, int tiles_n, int bm, int bn) {
+  int best = 0;
+  long best_cost = 0;
+  for (int gm = 1; gm <= 8; gm *= 2) {
+    const int gn = 8 / gm;
+    if (tiles_m % gm != 0 || tiles_n % gn != 0) continue;
+    const long cost = 32L * (tiles_m / gm) * bm + 9L * (tiles_n / gn) * bn;
+    if (best == 0 || cost < best_cost) {
+      best = gm;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 // Split K until the grid reaches one workgroup per CU (256 on MI355X).
 int splits_for(int tiles, int steps) {
   int s = 1;
@@ -837,7 +869,7 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
     if (small_n >= kGemmSmallTiles) {
       // One 32 x 64 tile per workgroup, K split inside the workgroup.
       hipLaunchKernelGGL((k_gemm_q4k_kslice<1, 2>), dim3(small_n), dim3(Small::Threads), 0,
-                         stream, w, x, y, mi, ni, ki, 1);
+                         stream, w, x, y, mi, ni, ki, 1, small_n, 0);
       return hipGetLastError();
     }
     // Small batch: one 32-row slice, the four waves split the 128 weight rows.
@@ -846,9 +878,8 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
   const int big_m = (mi + kWBM - 1) / kWBM, big_n = (ni + kWBN - 1) / kWBN;
   if (mi >= 2 * kWBM && big_m * big_n >= kGemmBigTiles) {
     // Enough 128 x 256 tiles to fill most CUs without splitting K.
-    const bool xcd = big_n % 8 == 0;
     hipLaunchKernelGGL(k_gemm_q4k_128x256, dim3(big_m * big_n), dim3(256), 0, stream, w, x, y,
-                       mi, ni, ki, big_m, big_n, xcd ? 1 : 0);
+                       mi, ni, ki, big_m, big_n, xcd_groups(big_m, big_n, kWBM, kWBN));
     return hipGetLastError();
   }
   using Mid = KSlice<2, 2>;
@@ -856,7 +887,8 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
   if (mid_m * mid_n >= kGemmMidTiles) {
     // Enough 64 x 128 tiles to fill most CUs without splitting K.
     hipLaunchKernelGGL((k_gemm_q4k_kslice<2, 2>), dim3(mid_m * mid_n), dim3(Mid::Threads), 0,
-                       stream, w, x, y, mi, ni, ki, mid_m);
+                       stream, w, x, y, mi, ni, ki, mid_m, mid_n,
+                       xcd_groups(mid_m, mid_n, Mid::BM, Mid::BN));
     return hipGetLastError();
   }
   // 128 x 128 tiles, two workgroups per CU.

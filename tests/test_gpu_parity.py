@@ -304,6 +304,18 @@ def test_gemm_mid_tile_kernel_full_output(q4k):
     assert_within(Y, Yr, A, GEMM_TOL, "gemm 200x6144x256")
 
 
+# Every output of the two grids whose tiles are dealt to the XCDs in 2 x 4
+# blocks (M split in two): 6 x 32 tiles of 64 x 128 and 4 x 36 tiles of
+# 128 x 256 (N = 9216 is not a multiple of eight 256-column tiles per XCD).
+@pytest.mark.parametrize("m,n,k", [(384, 4096, 256), (512, 9216, 256)])
+def test_gemm_xcd_blocked_grids_full_output(q4k, m, n, k):
+    w = synth.q4k_weights(n, k, seed=n + 5)
+    xb = synth.normal_bf16((m, k), seed=n + 5)
+    Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
+    Yr, A = oracle.gemm(w, xb, n, k)
+    assert_within(Y, Yr, A, GEMM_TOL, "gemm %dx%dx%d" % (m, n, k))
+
+
 @pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
 def test_gemm_sweep_shape_sampled(q4k, m):
     n, k = 14336, 4096
