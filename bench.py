@@ -205,9 +205,10 @@ def main():
             _lib.check(_lib.q4k_dequantize_bf16(wd.data_ptr(), od.data_ptr(), n, k, sp))
         kernels.append(("dequant_bf16_4096x4096", run_dq, nbytes, 0, rot))
 
-    # ---- plain streaming read of the same weight footprints (ceiling for the GEMV path)
+    # ---- plain streaming read of the weight footprints (ceilings for the GEMV path: the
+    #      decode weight, one 14336 x 4096 matrix, and the gate/up pair)
     if want("read_probe"):
-        for n, k in ((D_MODEL, D_MODEL), (D_FF, D_MODEL)):
+        for n, k in ((D_MODEL, D_MODEL), (D_FF, D_MODEL), (2 * D_FF, D_MODEL)):
             nbytes = q4k_bytes(n, k)
             rot = Rotor(torch, [synth.q4k_weights(n, k, seed=0)], nbytes)
             kernels.append(("read_probe_%d" % nbytes, read_probe_runner(_lib, rot, nbytes, torch),

@@ -65,14 +65,18 @@ struct WRegs {
 };
 
 // MT activation rows per pass, R weight rows per wave (times NW = 2 weight
-// matrices for the gate/up pair), NWV waves per workgroup.
-template <int MT, int R, bool GLU, int NWV>
+// matrices for the gate/up pair), NWV waves per workgroup.  XREG (batch 1,
+// k <= 4096: one K step, so a lane meets the same 64 x values in every row):
+// each lane holds its x slice and the two sub-block sums in registers, read
+// from LDS once while the first weights are in flight.
+template <int MT, int R, bool GLU, int NWV, bool XREG>
 __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict__ w,
                                                        const uint8_t* __restrict__ w2,
                                                        const float* __restrict__ x,
                                                        float* __restrict__ y, int m, int n,
                                                        int k) {
   static_assert(!GLU || MT == 1, "the gate/up pair runs at batch 1");
+  static_assert(!XREG || MT == 1, "x in registers at batch 1 only");
   constexpr int NW = GLU ? 2 : 1;
   constexpr int NT = 64 * NWV;
   extern __shared__ float smem[];
@@ -105,6 +109,8 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
 #pragma unroll
       for (int i = 0; i < MT; ++i) acc[u][r][i] = 0.0f;
 
+  f4_t xr[XREG ? 16 : 1];  // x[64g .. 64g+63] of super-block b (XREG)
+  float xsum[2] = {0.0f, 0.0f};  // its two sub-block sums (XREG)
   for (int c0 = 0; c0 < k; c0 += kXChunk<MT>) {
     const int kc = min(kXChunk<MT>, k - c0);
     const int s_begin = c0 >> 12;
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
       // read at use (their many accumulators leave no registers to spare).
       // A scheduling fence per slice keeps the compiler from hoisting all the
       // reads of a step (and spilling).
-      constexpr bool kAhead = MT == 1;
+      constexpr bool kAhead = MT == 1 && !XREG;
       f4_t xl_n[MT], xh_n[MT];
       if constexpr (kAhead) {
         xl_n[0] = *reinterpret_cast<const f4_t*>(xs + xo);
@@ -162,7 +168,10 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
         f4_t xl[MT], xh[MT];
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          if constexpr (kAhead) {
+          if constexpr (XREG) {
+            xl[i] = xr[c];
+            xh[i] = xr[8 + c];
+          } else if constexpr (kAhead) {
             xl[i] = xl_n[i];
             xh[i] = xh_n[i];
             if (c < 7) {
@@ -209,8 +218,8 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
           const GroupScales sc = group_scales(B.hd[u][r], g);
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
-            const float slo = ssum[i * sst + kb_local * 8 + 2 * g];
-            const float shi = ssum[i * sst + kb_local * 8 + 2 * g + 1];
+            const float slo = XREG ? xsum[0] : ssum[i * sst + kb_local * 8 + 2 * g];
+            const float shi = XREG ? xsum[1] : ssum[i * sst + kb_local * 8 + 2 * g + 1];
             float a = sc.a_lo * pl[u][r][i];
             a = __builtin_fmaf(sc.a_hi, ph[u][r][i], a);
             a = __builtin_fmaf(-sc.b_lo, slo, a);
@@ -287,6 +296,19 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
       store_x16(idx, v);
     }
     __syncthreads();
+    if constexpr (XREG) {
+      // One K step: super-block b of the chunk (lanes past the last block read
+      // block 0 and add nothing).
+      const int kb_local = b < kb_count ? b : 0;
+      const int xo = xs_index(kb_local * kQK + 64 * g);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        xr[c] = *reinterpret_cast<const f4_t*>(xs + xo + 4 * c);
+        xr[8 + c] = *reinterpret_cast<const f4_t*>(xs + xo + 32 + 4 * c);
+      }
+      xsum[0] = ssum[kb_local * 8 + 2 * g];
+      xsum[1] = ssum[kb_local * 8 + 2 * g + 1];
+    }
 
     for (int j = 0; j < jobs; j += 2) {
       if (j + 1 < jobs) issue(j + 1, bufB);
@@ -321,11 +343,11 @@ hipError_t device_facts(int dev, int* cus, int* lds_per_cu) {
   return hipSuccess;
 }
 
-template <int MT, int R, bool GLU, int NWV>
+template <int MT, int R, bool GLU, int NWV, bool XREG = false>
 hipError_t launch(const uint8_t* w, const uint8_t* w2, const float* x, float* y, int m, int n,
                   int k, hipStream_t stream) {
   static std::atomic<int> resident[kMaxDevices];  // workgroups per CU, LDS aside
-  const auto kern = &k_gemv_q4k<MT, R, GLU, NWV>;
+  const auto kern = &k_gemv_q4k<MT, R, GLU, NWV, XREG>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -370,9 +392,13 @@ hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, in
     hipError_t e;
     if (mm == 1) {
       // One row per wave; matrices with few rows per CU take 16 waves per
-      // workgroup (x staged once per 16 waves), taller ones 8.
+      // workgroup (x staged once per 16 waves).  Taller ones take 4 waves and,
+      // within one K step (k <= 4096), keep x in registers across their rows;
+      // past one K step, 8 waves.
       if (n <= kGemvWideRows) {
         e = launch<1, kGemvRowsPerWave, false, 16>(w, w, xs, ys, mm, ni, ki, stream);
+      } else if (k <= 4096) {
+        e = launch<1, kGemvRowsPerWave, false, 4, true>(w, w, xs, ys, mm, ni, ki, stream);
       } else {
         e = launch<1, kGemvRowsPerWave, false, 8>(w, w, xs, ys, mm, ni, ki, stream);
       }

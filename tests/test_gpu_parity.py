@@ -127,8 +127,13 @@ def test_gemv_decode_4096(q4k):
     assert_within(y, yr[0], a[0], GEMV_TOL, "gemv 4096x4096")
 
 
+# Batch 1 runs three launch shapes: up to 8192 rows (16 waves per workgroup),
+# taller matrices with k <= 4096 (x held in registers; 8200 x 768 leaves 13 of
+# the 16 super-block lanes idle, 9001 x 4096 has a ragged last row set) and
+# taller ones past one K step (8193 x 4352).
 @pytest.mark.parametrize("n,k", [(1, 256), (17, 256), (257, 768), (100, 3840), (33, 4352),
-                                 (64, 14336), (1000, 1280)])
+                                 (64, 14336), (1000, 1280), (8200, 768), (9001, 4096),
+                                 (8193, 4352)])
 def test_gemv_ragged_shapes(q4k, n, k):
     w = synth.q4k_weights(n, k, seed=5)
     x = synth.normal_f32(k, seed=5)
