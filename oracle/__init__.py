@@ -58,9 +58,19 @@ def lib():
         L.oracle_swiglu_mlp.argtypes = [_u8p, _u8p, _u8p, _f32p, _i64, _i64,
                                         _f64p, _f64p, _f64p, _f64p, _f64p, _f64p,
                                         _f64p]
+        L.oracle_q5k_quant.restype = ctypes.c_int
+        L.oracle_q5k_quant.argtypes = [_u8p, _u8p, ctypes.c_int]
+        L.oracle_q5k_dequant_block.restype = None
+        L.oracle_q5k_dequant_block.argtypes = [_u8p, _f32p]
+        L.oracle_q5k_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
+        L.oracle_q5k_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
+        L.oracle_q5k_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
+        L.oracle_q5k_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
+                                           _f64p, _f64p]
         for name in ("oracle_dequant_f32", "oracle_dequant_bf16", "oracle_gemv",
                      "oracle_gemv_rows", "oracle_gemm", "oracle_gemm_cols",
-                     "oracle_swiglu_mlp"):
+                     "oracle_swiglu_mlp", "oracle_q5k_dequant_f32", "oracle_q5k_dequant_bf16",
+                     "oracle_q5k_gemv", "oracle_q5k_gemv_rows"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -199,3 +209,63 @@ def swiglu_mlp(w_gate, w_up, w_down, x, d_model: int, d_ff: int):
         _p(r["g"], _f64p), _p(r["ag"], _f64p), _p(r["u"], _f64p), _p(r["au"], _f64p),
         _p(r["h"], _f64p), _p(r["out"], _f64p), _p(r["aout"], _f64p)), "swiglu_mlp")
     return r
+
+
+# ---- Q5_K (q5k_oracle.h) ----------------------------------------------------
+
+Q5K_BLOCK_BYTES = 176
+
+
+def q5k_quant(qh: np.ndarray, qs: np.ndarray, i: int) -> int:
+    qh = _c(qh, np.uint8)
+    qs = _c(qs, np.uint8)
+    assert qh.size == 32 and qs.size == 128
+    return lib().oracle_q5k_quant(_p(qh, _u8p), _p(qs, _u8p), int(i))
+
+
+def q5k_dequant_block(blk: np.ndarray) -> np.ndarray:
+    blk = _c(blk, np.uint8)
+    assert blk.size == Q5K_BLOCK_BYTES
+    w = np.zeros(256, np.float32)
+    lib().oracle_q5k_dequant_block(_p(blk, _u8p), _p(w, _f32p))
+    return w
+
+
+def q5k_dequant_f32(w: np.ndarray, n: int, k: int) -> np.ndarray:
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * Q5K_BLOCK_BYTES
+    out = np.zeros((n, k), np.float32)
+    _check(lib().oracle_q5k_dequant_f32(_p(w, _u8p), n, k, _p(out, _f32p)), "q5k_dequant_f32")
+    return out
+
+
+def q5k_dequant_bf16(w: np.ndarray, n: int, k: int) -> np.ndarray:
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * Q5K_BLOCK_BYTES
+    out = np.zeros((n, k), np.uint16)
+    _check(lib().oracle_q5k_dequant_bf16(_p(w, _u8p), n, k, _p(out, _u16p)), "q5k_dequant_bf16")
+    return out
+
+
+def q5k_gemv(w: np.ndarray, x: np.ndarray, n: int, k: int):
+    """y, a = oracle GEMV on Q5_K weights; x fp32 [m, k] (or [k]); fp64 [m, n]."""
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32).reshape(-1, k)
+    m = x.shape[0]
+    y = np.zeros((m, n), np.float64)
+    a = np.zeros((m, n), np.float64)
+    _check(lib().oracle_q5k_gemv(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(y, _f64p),
+                                 _p(a, _f64p)), "q5k_gemv")
+    return y, a
+
+
+def q5k_gemv_rows(w: np.ndarray, x: np.ndarray, n: int, k: int, rows):
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32).reshape(-1, k)
+    rows = _c(rows, np.int64)
+    m = x.shape[0]
+    y = np.zeros((m, rows.size), np.float64)
+    a = np.zeros((m, rows.size), np.float64)
+    _check(lib().oracle_q5k_gemv_rows(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(rows, _i64p),
+                                      rows.size, _p(y, _f64p), _p(a, _f64p)), "q5k_gemv_rows")
+    return y, a

@@ -12,7 +12,7 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "q4k_oracle.c")
+SRCS = [os.path.join(HERE, "q4k_oracle.c"), os.path.join(HERE, "q5k_oracle.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
@@ -22,7 +22,7 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
 def build(verbose: bool = False) -> str:
     """Compile the oracle unconditionally and return the library path."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", *CFLAGS, *SRCS, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -21,6 +21,9 @@ d and dmin = |N(0,1)| * 0.01, activations N(0,1)):
 * Activations are fp32 N(0,1); bf16 activations are the fp32 draw rounded to
   bf16 (round to nearest even, torch's conversion).
 
+A Q5_K super-block (176 bytes) is drawn the same way: fp16 ``d`` and ``dmin`` at
+bytes 0 and 2, the other 172 bytes uniform.
+
 Random streams come from numpy's PCG64 seeded with ``SeedSequence([seed,
 stream])``, so every tensor of a case has its own independent stream and a
 case is reproducible from ``seed`` alone.
@@ -30,7 +33,8 @@ from __future__ import annotations
 import numpy as np
 
 QK = 256            # weights per super-block
-BLOCK_BYTES = 144   # bytes per super-block
+BLOCK_BYTES = 144   # bytes per Q4_K super-block
+Q5K_BLOCK_BYTES = 176  # bytes per Q5_K super-block (Q4_K plus 32 high-bit bytes)
 
 # stream ids: one per tensor role, so cases never share draws
 W, X, W_GATE, W_UP, W_DOWN = 0, 1, 2, 3, 4
@@ -54,6 +58,24 @@ def q4k_weights(n: int, k: int, seed: int = 0, stream: int = W,
     blocks[:, 2:4] = dmin.view(np.uint8).reshape(nb, 2)
     blocks[:, 4:] = g.integers(0, 256, size=(nb, BLOCK_BYTES - 4), dtype=np.uint8)
     return blocks.reshape(n, (k // QK) * BLOCK_BYTES)
+
+
+def q5k_weights(n: int, k: int, seed: int = 0, stream: int = W,
+                scale: float = 0.01) -> np.ndarray:
+    """Random Q5_K matrix W [n, k] as uint8 [n, (k/256)*176]: fp16 d and dmin as for Q4_K,
+    the other 172 bytes (scales, high bits, nibbles) uniform, so every 5-bit quant is
+    uniform in 0..31 whatever the packing."""
+    if k % QK:
+        raise ValueError("k must be a multiple of 256")
+    nb = n * (k // QK)
+    g = rng(seed, stream)
+    blocks = np.empty((nb, Q5K_BLOCK_BYTES), np.uint8)
+    d = (np.abs(g.standard_normal(nb)) * scale).astype(np.float16)
+    dmin = (np.abs(g.standard_normal(nb)) * scale).astype(np.float16)
+    blocks[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    blocks[:, 2:4] = dmin.view(np.uint8).reshape(nb, 2)
+    blocks[:, 4:] = g.integers(0, 256, size=(nb, Q5K_BLOCK_BYTES - 4), dtype=np.uint8)
+    return blocks.reshape(n, (k // QK) * Q5K_BLOCK_BYTES)
 
 
 def normal_f32(shape, seed: int = 0, stream: int = X) -> np.ndarray:

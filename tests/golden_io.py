@@ -19,8 +19,8 @@ def _expand(tokens):
     return out
 
 
-def hand_blocks(name: str = "hand_blocks.txt"):
-    """Return {block name: (bytes uint8[144], expected fp64[256])}."""
+def hand_blocks(name: str = "hand_blocks.txt", block_bytes: int = 144):
+    """Return {block name: (bytes uint8[block_bytes], expected fp64[256])}."""
     blocks = {}
     cur = None
     with open(os.path.join(GOLDEN, name)) as f:
@@ -34,7 +34,7 @@ def hand_blocks(name: str = "hand_blocks.txt"):
                 blocks[cur] = [None, None]
             elif head == "bytes":
                 b = np.array(_expand(rest), dtype=np.uint8)
-                assert b.size == 144, (cur, b.size)
+                assert b.size == block_bytes, (cur, b.size)
                 blocks[cur][0] = b
             elif head == "expect":
                 kind, *vals = rest

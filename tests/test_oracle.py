@@ -307,3 +307,107 @@ def test_swiglu_mlp_matches_library_composition():
     # the GEMV of W_down against the same h reproduces out (down = GEMV stage)
     yd, _ = oracle.gemv(wd, r["h"].astype(np.float32), dm, dff)
     assert np.allclose(yd[0], out, rtol=1e-5, atol=1e-6 * np.abs(out).max())
+
+
+# ---------------------------------------------------------------- Q5_K oracle
+
+Q5K_HAND = hand_blocks("hand_blocks_q5k.txt", block_bytes=176)
+
+
+@pytest.mark.parametrize("name", sorted(Q5K_HAND))
+def test_q5k_hand_packed_blocks(name):
+    blk, expected = Q5K_HAND[name]
+    got = oracle.q5k_dequant_block(blk).astype(np.float64)
+    assert np.array_equal(got, expected), name
+
+
+def test_q5k_with_clear_high_bits_equals_q4k():
+    # With every fifth bit clear a Q5_K block is the Q4_K block with the same
+    # scales and nibbles: ties the Q5_K decoder to the pinned Q4_K one.
+    w4 = synth.q4k_weights(64, 256, seed=11)
+    for b4 in w4:
+        b5 = np.concatenate([b4[:16], np.zeros(32, np.uint8), b4[16:]])
+        assert np.array_equal(oracle.q5k_dequant_block(b5).view(np.uint32),
+                              oracle.dequant_block(b4).view(np.uint32))
+
+
+def test_q5k_high_bit_map_every_bit():
+    # One high bit at a time (d = 1, dmin = 0, sc = 1, nibbles 0): exactly the
+    # weight 64 (u div 2) + 32 (u mod 2) + l of bit u of qh[l] becomes 16.
+    base = np.zeros(176, np.uint8)
+    base[1] = 0x3C
+    base[4:8] = 1
+    base[12:16] = 1
+    for l in range(32):
+        for u in range(8):
+            blk = base.copy()
+            blk[16 + l] = 1 << u
+            w = oracle.q5k_dequant_block(blk)
+            want = np.zeros(256, np.float32)
+            want[64 * (u // 2) + 32 * (u % 2) + l] = 16.0
+            assert np.array_equal(w, want), (l, u)
+
+
+def test_q5k_quant_roundtrip_every_position_and_value():
+    from q5k_pack import pack_high_bits
+    from q4k_pack import pack_quants
+    for v in range(32):
+        for i in range(256):
+            q = np.zeros(256, np.int64)
+            q[i] = v
+            qh, qs = pack_high_bits(q), pack_quants(q % 16)
+            assert oracle.q5k_quant(qh, qs, i) == v
+            if v:
+                j = (i + 97) % 256
+                assert oracle.q5k_quant(qh, qs, j) == 0
+
+
+def test_q5k_zero_quants_give_minus_dmin_m():
+    from q5k_pack import pack_q5k_block
+    sc = [3, 7, 0, 63, 1, 2, 40, 5]
+    mn = [9, 0, 63, 4, 33, 1, 6, 17]
+    blk = pack_q5k_block(0x3C00, 0x3555, sc, mn, np.zeros(256, np.int64))
+    dmin = float(np.array([0x3555], np.uint16).view(np.float16)[0])
+    want = np.repeat([np.float32(-dmin * m) for m in mn], 32)
+    assert np.array_equal(oracle.q5k_dequant_block(blk), want)
+
+
+def test_q5k_dequant_bf16_is_rne_of_f32():
+    w = synth.q5k_weights(16, 512, seed=4)
+    f = oracle.q5k_dequant_f32(w, 16, 512)
+    b = oracle.q5k_dequant_bf16(w, 16, 512)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b, ref)
+
+
+def test_q5k_gemv_unit_vectors_give_columns():
+    n, k = 24, 512
+    w = synth.q5k_weights(n, k, seed=8)
+    W = oracle.q5k_dequant_f32(w, n, k).astype(np.float64)
+    for c in (0, 1, 31, 32, 63, 64, 255, 256, 300, 511):
+        x = np.zeros(k, np.float32)
+        x[c] = 1.0
+        y, _ = oracle.q5k_gemv(w, x, n, k)
+        assert np.array_equal(y[0], W[:, c])
+
+
+def test_q5k_gemv_matches_library_matmul():
+    n, k, m = 40, 768, 3
+    w = synth.q5k_weights(n, k, seed=12)
+    x = synth.normal_f32((m, k), seed=12)
+    y, a = oracle.q5k_gemv(w, x, n, k)
+    W = oracle.q5k_dequant_f32(w, n, k).astype(np.float64)
+    ref = x.astype(np.float64) @ W.T
+    assert np.all(np.abs(y - ref) <= 1e-12 * a)
+    assert np.allclose(a, np.abs(x.astype(np.float64)) @ np.abs(W.T))
+    rows = np.array([0, 7, 39])
+    yr, ar = oracle.q5k_gemv_rows(w, x, n, k, rows)
+    assert np.array_equal(yr, y[:, rows]) and np.array_equal(ar, a[:, rows])
+
+
+def test_q5k_bad_shapes_rejected():
+    w = synth.q5k_weights(2, 256, seed=0)
+    L = oracle.lib()
+    out = np.zeros(512, np.float32)
+    assert L.oracle_q5k_dequant_f32(oracle._p(w, oracle._u8p), 2, 300,
+                                    oracle._p(out, oracle._f32p)) == -1
