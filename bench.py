@@ -39,6 +39,7 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096
 COLD_BYTES = 576 << 20         # rotating working set per kernel: over twice the 256 MB MALL
 
 D_MODEL, D_FF = 4096, 14336
+Q5K_BLOCK = 176               # bytes per Q5_K super-block
 SWEEP_M = (1, 2, 4, 8, 16, 32)
 
 
@@ -59,7 +60,7 @@ def parse():
                    help="also run one device copy of 256 MiB (counter calibration)")
     p.add_argument("--only", default="",
                    help="comma list of kernels to run "
-                        "(gemv,sweep_gemv,sweep_gemm,mlp,gemm,dequant,read_probe)")
+                        "(gemv,q5k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,dequant,read_probe)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
     p.add_argument("--eager-only", action="store_true",
                    help="time only the eagerly enqueued launches (no HIP graph replay)")
@@ -138,6 +139,19 @@ def main():
             wd, xd, yd = rot[i]
             _lib.check(_lib.q4k_gemv(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), 1, n, k, sp))
         kernels.append(("gemv_4096x4096", run_gemv, nbytes, 2 * n * k, rot))
+
+    # ---- decode GEMV on the Q5_K sibling format, 4096 x 4096
+    if want("q5k_gemv"):
+        n = k = D_MODEL
+        w = synth.q5k_weights(n, k, seed=0)
+        x = synth.normal_f32(k, seed=0)
+        nbytes = n * (k // 256) * Q5K_BLOCK + 4 * k + 4 * n
+        rot = Rotor(torch, [w, x, np.zeros(n, np.float32)], nbytes)
+
+        def run_q5(i, sp, rot=rot, n=n, k=k):
+            wd, xd, yd = rot[i]
+            _lib.check(_lib.q5k_gemv(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), 1, n, k, sp))
+        kernels.append(("q5k_gemv_4096x4096", run_q5, nbytes, 2 * n * k, rot))
 
     # ---- small-batch sweep, W 14336 x 4096
     if want("sweep_gemv") or want("sweep_gemm"):
@@ -334,7 +348,8 @@ def main():
     if head:
         out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": head["hbm_frac"], "traffic": traffic("gemv_4096x4096"),
-                           "kernel": "k_gemv_q4k<1,1,false,16>", "bytes_per_launch": 9469952}
+                           "kernel": "k_gemv_q4k<1, 1, false, 16, false, 4>",
+                           "bytes_per_launch": 9469952}
     if gemm:
         out["roofline_gemm"] = {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": gemm["mfma_frac"],
@@ -375,15 +390,34 @@ def traffic(name):
     return None
 
 
+def _template_args(name, kernel):
+    """Template arguments of `kernel<...>` in a demangled name, as a tuple of strings."""
+    i = name.find(kernel + "<")
+    if i < 0:
+        return None
+    j = name.index(">", i)
+    return tuple(a.strip() for a in name[i + len(kernel) + 1:j].split(","))
+
+
 # Dispatch signatures of the timed kernels -> workload.  Grid sizes (total work-items) and
 # LDS sizes follow from the launch code for these shapes.
 def dispatch_workload(name, threads, lds, hint=""):
-    if "k_gemv_q4k<1, 1, false, 16>" in name:
-        return "swiglu_mlp_down_4096x14336" if hint == "mlp" else "gemv_4096x4096"
-    if "k_gemv_q4k<1, 1, false, 8>" in name:
-        return "sweep_gemv_14336x4096_m1"
-    if "k_gemv_q4k<1, 1, true" in name:
-        return "swiglu_mlp_gateup_14336x4096"
+    gv = _template_args(name, "k_gemv_q4k")
+    if gv:
+        # <MT, R, GLU, NWV, XREG, FMT>
+        mt, glu, nwv, fmt = gv[0], gv[2], gv[3], gv[5] if len(gv) > 5 else "4"
+        if glu == "true":
+            return "swiglu_mlp_gateup_14336x4096"
+        if fmt == "5":
+            return "q5k_gemv_4096x4096" if mt == "1" else "q5k_other"
+        if mt == "1" and nwv == "16":
+            return "swiglu_mlp_down_4096x14336" if hint == "mlp" else "gemv_4096x4096"
+        if mt == "1":
+            return "sweep_gemv_14336x4096_m1"
+        return "sweep_gemv_14336x4096_batched"
+    dq = _template_args(name, "k_dequant_q4k")
+    if dq:
+        return "dequant_bf16_4096x4096" if dq == ("true", "4") else "dequant_other"
     if "k_gemm_q4k_128x256" in name:
         return "gemm_512x14336x4096" if threads == 57344 else "gemm_other"
     if "k_gemm_q4k_kslice<2, 2>" in name:
@@ -394,10 +428,6 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "gemm_other"
     if "k_gemm_q4k<1, 4, 1, 1, 2>" in name:
         return "sweep_gemm_14336x4096"
-    if "k_gemv_q4k<" in name:
-        return "sweep_gemv_14336x4096_batched"
-    if "k_dequant_q4k<true>" in name:
-        return "dequant_bf16_4096x4096"
     if "k_read_probe" in name:
         return "read_probe"
     if "k_zero_f32" in name:
@@ -525,6 +555,11 @@ def spot_check(kernels, args, np, torch):
             w, x, y = (a.cpu().numpy() for a in t)
             rows = np.arange(0, 4096, 37)
             yr, a = oracle.gemv_rows(w, x, 4096, 4096, rows)
+            res[name] = float((np.abs(y[rows] - yr[0]) / (1e-4 * a[0])).max())
+        elif name == "q5k_gemv_4096x4096":
+            w, x, y = (a.cpu().numpy() for a in t)
+            rows = np.arange(0, 4096, 37)
+            yr, a = oracle.q5k_gemv_rows(w, x, 4096, 4096, rows)
             res[name] = float((np.abs(y[rows] - yr[0]) / (1e-4 * a[0])).max())
         elif name.startswith("gemm_512"):
             w, xb, y = (a.cpu().numpy() for a in t)

@@ -21,6 +21,7 @@ Q4K_ERR_LAUNCH = -4
 Q4K_QK = 256
 Q4K_BLOCK_BYTES = 144
 Q4K_GEMV_MAX_M = 32
+Q5K_BLOCK_BYTES = 176
 
 # Every symbol the header declares, with (restype, argtypes).
 _vp = ctypes.c_void_p
@@ -36,6 +37,9 @@ SIGNATURES = {
     "q4k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q4k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q4k_read_probe": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
+    "q5k_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q5k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "q5k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
 }
 
 
@@ -124,3 +128,15 @@ def q4k_dequantize_bf16(w, out, n, k, stream) -> int:
 
 def q4k_read_probe(buf, nbytes, sink, stream) -> int:
     return load().q4k_read_probe(buf, nbytes, sink, stream)
+
+
+def q5k_gemv(w, x, y, m, n, k, stream) -> int:
+    return load().q5k_gemv(w, x, y, m, n, k, stream)
+
+
+def q5k_dequantize_f32(w, out, n, k, stream) -> int:
+    return load().q5k_dequantize_f32(w, out, n, k, stream)
+
+
+def q5k_dequantize_bf16(w, out, n, k, stream) -> int:
+    return load().q5k_dequantize_bf16(w, out, n, k, stream)

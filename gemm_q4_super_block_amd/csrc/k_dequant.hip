@@ -9,7 +9,10 @@
 //
 // One thread per 16 quant bytes: (row, block, group g, half hh).  It writes
 // the 16 low-nibble weights 64g+16hh.. and the 16 high-nibble weights
-// 64g+32+16hh.. of its block.
+// 64g+32+16hh.. of its block.  Q5_K (FMT 5) adds the 16 high-bit bytes
+// qh[16hh ..] that hold those weights' fifth bits and widens the 5-bit bytes
+// exactly (v_cvt_f32_ubyte) with the scale d*sc, so fma(d*sc, q, -dmin*m)
+// is again the exact weight rounded once.
 #include <hip/hip_runtime.h>
 
 #include "q4k_device.h"
@@ -18,7 +21,7 @@
 namespace q4k {
 namespace {
 
-template <bool BF16>
+template <bool BF16, int FMT>
 __global__ __launch_bounds__(256) void k_dequant_q4k(const uint8_t* __restrict__ w,
                                                      void* __restrict__ out, size_t chunks) {
   const size_t t = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -26,13 +29,46 @@ __global__ __launch_bounds__(256) void k_dequant_q4k(const uint8_t* __restrict__
   const int hh = static_cast<int>(t & 1);
   const int g = static_cast<int>((t >> 1) & 3);
   const size_t blk = t >> 3;  // row * (k/256) + block
-  const uint8_t* p = w + blk * kBlockBytes;
+  const uint8_t* p = w + blk * block_bytes<FMT>();
   const uint4 hd = load16(p);
-  const uint4 q = load16(p + 16 + 32 * g + 16 * hh);
+  const uint4 q = load16(p + (FMT == 5 ? kQ5QuantOffset : 16) + 32 * g + 16 * hh);
   const GroupScales s = group_scales(hd, g);
   // Row-major [n, k]: weight (row, 256*block + i) is element blk*256 + i.
   const size_t base = blk * kQK + 64 * g + 16 * hh;
-  if constexpr (BF16) {
+  if constexpr (FMT == 5) {
+    const uint4 qh = load16(p + kQ5HighOffset + 16 * hh);
+    const uint32_t qv[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t hv[4] = {qh.x, qh.y, qh.z, qh.w};
+    // a carries the 2^9 of the fp8 widening; the bytes here are exact integers.
+    const float a_lo = s.a_lo * (1.0f / kNibbleUnscale), a_hi = s.a_hi * (1.0f / kNibbleUnscale);
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = q5_bytes(qv[i], hv[i], 0, 2 * g);
+      hi[i] = q5_bytes(qv[i], hv[i], 4, 2 * g + 1);
+    }
+    if constexpr (BF16) {
+      uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + base);
+      o[0] = dequant8_bf16_q5(lo[0], lo[1], a_lo, s.b_lo);
+      o[1] = dequant8_bf16_q5(lo[2], lo[3], a_lo, s.b_lo);
+      uint4* o2 = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + base + 32);
+      o2[0] = dequant8_bf16_q5(hi[0], hi[1], a_hi, s.b_hi);
+      o2[1] = dequant8_bf16_q5(hi[2], hi[3], a_hi, s.b_hi);
+    } else {
+      float* o = static_cast<float*>(out) + base;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f4_t vl, vh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vl[j] = __builtin_fmaf(a_lo, ubyte_f32(lo[i], j), -s.b_lo);
+          vh[j] = __builtin_fmaf(a_hi, ubyte_f32(hi[i], j), -s.b_hi);
+        }
+        *reinterpret_cast<f4_t*>(o + 4 * i) = vl;
+        *reinterpret_cast<f4_t*>(o + 32 + 4 * i) = vh;
+      }
+    }
+  } else if constexpr (BF16) {
     uint32_t lo8[8], hi8[8];
     dequant16_bf16(q, s, lo8, hi8);
     uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + base);
@@ -54,11 +90,11 @@ __global__ __launch_bounds__(256) void k_dequant_q4k(const uint8_t* __restrict__
   }
 }
 
-template <bool BF16>
+template <bool BF16, int FMT>
 hipError_t launch(const uint8_t* w, void* out, int64_t n, int64_t k, hipStream_t stream) {
   const size_t chunks = static_cast<size_t>(n) * static_cast<size_t>(k / kQK) * 8;
   const size_t grid = (chunks + 255) / 256;
-  hipLaunchKernelGGL((k_dequant_q4k<BF16>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+  hipLaunchKernelGGL((k_dequant_q4k<BF16, FMT>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
                      stream, w, out, chunks);
   return hipGetLastError();
 }
@@ -99,12 +135,22 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
 
 hipError_t launch_dequant_f32(const uint8_t* w, float* out, int64_t n, int64_t k,
                               hipStream_t stream) {
-  return launch<false>(w, out, n, k, stream);
+  return launch<false, 4>(w, out, n, k, stream);
 }
 
 hipError_t launch_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64_t k,
                                hipStream_t stream) {
-  return launch<true>(w, out, n, k, stream);
+  return launch<true, 4>(w, out, n, k, stream);
+}
+
+hipError_t launch_q5k_dequant_f32(const uint8_t* w, float* out, int64_t n, int64_t k,
+                                  hipStream_t stream) {
+  return launch<false, 5>(w, out, n, k, stream);
+}
+
+hipError_t launch_q5k_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64_t k,
+                                   hipStream_t stream) {
+  return launch<true, 5>(w, out, n, k, stream);
 }
 
 }  // namespace q4k

@@ -59,17 +59,21 @@ __host__ __device__ constexpr size_t gemv_lds_bytes(int mt, int kc) {
   return static_cast<size_t>(mt) * (xs_stride(kc) + kc / 32) * sizeof(float);
 }
 
-template <int R, int NW>
+template <int R, int NW, int FMT>
 struct WRegs {
   uint4 hd[NW][R], qa[NW][R], qb[NW][R];
+  uint4 h0[NW][FMT == 5 ? R : 1], h1[NW][FMT == 5 ? R : 1];  // Q5_K high bits
 };
 
 // MT activation rows per pass, R weight rows per wave (times NW = 2 weight
 // matrices for the gate/up pair), NWV waves per workgroup.  XREG (batch 1,
 // k <= 4096: one K step, so a lane meets the same 64 x values in every row):
 // each lane holds its x slice and the two sub-block sums in registers, read
-// from LDS once while the first weights are in flight.
-template <int MT, int R, bool GLU, int NWV, bool XREG>
+// from LDS once while the first weights are in flight.  FMT: 4 (Q4_K) or 5
+// (Q5_K: a lane also loads the block's 32 high-bit bytes and widens its 5-bit
+// quant bytes exactly with v_cvt_f32_ubyte, so its scale is d*sc without the
+// 2^9 of the fp8 path).
+template <int MT, int R, bool GLU, int NWV, bool XREG, int FMT = 4>
 __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict__ w,
                                                        const uint8_t* __restrict__ w2,
                                                        const float* __restrict__ x,
@@ -91,7 +95,9 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
   const int b = lane >> 2;
   const int g = lane & 3;
   const int kb_count = k >> 8;
-  const size_t row_bytes = static_cast<size_t>(kb_count) * kBlockBytes;
+  constexpr int kBB = block_bytes<FMT>();
+  constexpr int kQOff = FMT == 5 ? kQ5QuantOffset : 16;
+  const size_t row_bytes = static_cast<size_t>(kb_count) * kBB;
   const int nsets = (n + R - 1) / R;
   const int gw = blockIdx.x * NWV + wave;
   const int tw = gridDim.x * NWV;
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
     const int jobs = my_sets * ns;
     const bool last_chunk = c0 + kc >= k;
 
-    auto issue = [&](int j, WRegs<R, NW>& B) {
+    auto issue = [&](int j, WRegs<R, NW, FMT>& B) {
       const int si = j / ns;
       const int st = s_begin + (j - si * ns);
       const int row0 = (gw + si * tw) * R;
@@ -128,16 +134,19 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int row = min(row0 + r, n - 1);
-          const uint8_t* p =
-              (u ? w2 : w) + row * row_bytes + static_cast<size_t>(kb) * kBlockBytes;
+          const uint8_t* p = (u ? w2 : w) + row * row_bytes + static_cast<size_t>(kb) * kBB;
           B.hd[u][r] = load16(p);
-          B.qa[u][r] = load16(p + 16 + 32 * g);
-          B.qb[u][r] = load16(p + 32 + 32 * g);
+          B.qa[u][r] = load16(p + kQOff + 32 * g);
+          B.qb[u][r] = load16(p + kQOff + 16 + 32 * g);
+          if constexpr (FMT == 5) {
+            B.h0[u][r] = load16(p + kQ5HighOffset);
+            B.h1[u][r] = load16(p + kQ5HighOffset + 16);
+          }
         }
       }
     };
 
-    auto compute = [&](int j, const WRegs<R, NW>& B) {
+    auto compute = [&](int j, const WRegs<R, NW, FMT>& B) {
       const int si = j / ns;
       const int sl = j - si * ns;
       const int st = s_begin + sl;
@@ -188,10 +197,25 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             const uint32_t v = c < 4 ? word(B.qa[u][r], c) : word(B.qb[u][r], c - 4);
-            const uint32_t lo = v & 0x0F0F0F0Fu;
-            const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
-            const f2_t l01 = fp8x2_lo(lo), l23 = fp8x2_hi(lo);
-            const f2_t h01 = fp8x2_lo(hi), h23 = fp8x2_hi(hi);
+            f2_t l01, l23, h01, h23;
+            if constexpr (FMT == 5) {
+              // High-bit dword c: qh bytes 4c .. 4c+3, the fifth bits of
+              // weights 64g + 4c + i (bit 2g) and 64g + 32 + 4c + i (bit 2g+1).
+              const uint32_t hw = c < 4 ? word(B.h0[u][r], c) : word(B.h1[u][r], c - 4);
+              const uint32_t lo = q5_bytes(v, hw, 0, 2 * g);
+              const uint32_t hi = q5_bytes(v, hw, 4, 2 * g + 1);
+              l01 = f2_t{ubyte_f32(lo, 0), ubyte_f32(lo, 1)};
+              l23 = f2_t{ubyte_f32(lo, 2), ubyte_f32(lo, 3)};
+              h01 = f2_t{ubyte_f32(hi, 0), ubyte_f32(hi, 1)};
+              h23 = f2_t{ubyte_f32(hi, 2), ubyte_f32(hi, 3)};
+            } else {
+              const uint32_t lo = v & 0x0F0F0F0Fu;
+              const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+              l01 = fp8x2_lo(lo);
+              l23 = fp8x2_hi(lo);
+              h01 = fp8x2_lo(hi);
+              h23 = fp8x2_hi(hi);
+            }
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
               float a = pl[u][r][i];
@@ -215,7 +239,11 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
       for (int u = 0; u < NW; ++u) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const GroupScales sc = group_scales(B.hd[u][r], g);
+          GroupScales sc = group_scales(B.hd[u][r], g);
+          if constexpr (FMT == 5) {  // the quants are exact integers, not q * 2^-9
+            sc.a_lo *= 1.0f / kNibbleUnscale;
+            sc.a_hi *= 1.0f / kNibbleUnscale;
+          }
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
             const float slo = XREG ? xsum[0] : ssum[i * sst + kb_local * 8 + 2 * g];
@@ -286,7 +314,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
     const bool first = 16 * t < MT * kc;
     f4_t v0[4];
     if (first) load_x16(16 * t, v0);
-    WRegs<R, NW> bufA, bufB;
+    WRegs<R, NW, FMT> bufA, bufB;
     if (jobs > 0) issue(0, bufA);
     if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
     if (first) store_x16(16 * t, v0);
@@ -343,11 +371,11 @@ hipError_t device_facts(int dev, int* cus, int* lds_per_cu) {
   return hipSuccess;
 }
 
-template <int MT, int R, bool GLU, int NWV, bool XREG = false>
+template <int MT, int R, bool GLU, int NWV, bool XREG = false, int FMT = 4>
 hipError_t launch(const uint8_t* w, const uint8_t* w2, const float* x, float* y, int m, int n,
                   int k, hipStream_t stream) {
   static std::atomic<int> resident[kMaxDevices];  // workgroups per CU, LDS aside
-  const auto kern = &k_gemv_q4k<MT, R, GLU, NWV, XREG>;
+  const auto kern = &k_gemv_q4k<MT, R, GLU, NWV, XREG, FMT>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -379,10 +407,9 @@ hipError_t launch(const uint8_t* w, const uint8_t* w2, const float* x, float* y,
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
-                       int64_t k, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_gemv_fmt(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                           int64_t k, hipStream_t stream) {
   // Batches above 8 rows run as passes of 8 over x and y; W is re-streamed.
   for (int64_t i0 = 0; i0 < m; i0 += 8) {
     const int mm = static_cast<int>(m - i0 < 8 ? m - i0 : 8);
@@ -396,22 +423,34 @@ hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, in
       // within one K step (k <= 4096), keep x in registers across their rows;
       // past one K step, 8 waves.
       if (n <= kGemvWideRows) {
-        e = launch<1, kGemvRowsPerWave, false, 16>(w, w, xs, ys, mm, ni, ki, stream);
+        e = launch<1, kGemvRowsPerWave, false, 16, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
       } else if (k <= 4096) {
-        e = launch<1, kGemvRowsPerWave, false, 4, true>(w, w, xs, ys, mm, ni, ki, stream);
+        e = launch<1, kGemvRowsPerWave, false, 4, true, FMT>(w, w, xs, ys, mm, ni, ki, stream);
       } else {
-        e = launch<1, kGemvRowsPerWave, false, 8>(w, w, xs, ys, mm, ni, ki, stream);
+        e = launch<1, kGemvRowsPerWave, false, 8, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
       }
     } else if (mm == 2) {
-      e = launch<2, 2, false, 4>(w, w, xs, ys, mm, ni, ki, stream);
+      e = launch<2, 2, false, 4, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
     } else if (mm <= 4) {
-      e = launch<4, 2, false, 4>(w, w, xs, ys, mm, ni, ki, stream);
+      e = launch<4, 2, false, 4, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
     } else {
-      e = launch<8, 1, false, 8>(w, w, xs, ys, mm, ni, ki, stream);
+      e = launch<8, 1, false, 8, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
     }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                       int64_t k, hipStream_t stream) {
+  return launch_gemv_fmt<4>(w, x, y, m, n, k, stream);
+}
+
+hipError_t launch_q5k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                           int64_t k, hipStream_t stream) {
+  return launch_gemv_fmt<5>(w, x, y, m, n, k, stream);
 }
 
 hipError_t launch_gateup_swiglu(const uint8_t* w_gate, const uint8_t* w_up, const float* x,

@@ -79,8 +79,8 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool valid_k(int64_t k) { return k >= 256 && k % 256 == 0 && k <= INT32_MAX; }
 
-size_t q4k_bytes(int64_t rows, int64_t k) {
-  return static_cast<size_t>(rows) * static_cast<size_t>(k / 256) * 144u;
+size_t q4k_bytes(int64_t rows, int64_t k, size_t block = 144u) {
+  return static_cast<size_t>(rows) * static_cast<size_t>(k / 256) * block;
 }
 
 int launched(hipError_t e, const char* what) {
@@ -116,25 +116,41 @@ const char* q4k_device_name(void) {
 
 const char* q4k_last_error(void) { return g_last_error.c_str(); }
 
-int q4k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int64_t k,
-             void* stream) {
-  if (!w || !x || !y) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: null pointer");
+// Argument checks shared by the Q4_K and Q5_K GEMVs (block: bytes per
+// super-block of the format).
+static int gemv_checks(const char* what, const void* w, const float* x, const float* y,
+                       int64_t m, int64_t n, int64_t k, size_t block) {
+  if (!w || !x || !y) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
   if (m < 1 || m > Q4K_GEMV_MAX_M)
-    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: m=%lld outside 1..%d", (long long)m,
+    return fail(Q4K_ERR_INVALID_ARG, "%s: m=%lld outside 1..%d", what, (long long)m,
                 Q4K_GEMV_MAX_M);
-  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: n=%lld", (long long)n);
+  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
   if (!valid_k(k))
-    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: k=%lld is not a positive multiple of 256",
+    return fail(Q4K_ERR_INVALID_ARG, "%s: k=%lld is not a positive multiple of 256", what,
                 (long long)k);
   if (!aligned16(w) || !aligned16(x) || !aligned16(y))
-    return fail(Q4K_ERR_ALIGN, "q4k_gemv: w, x and y must be 16-byte aligned");
+    return fail(Q4K_ERR_ALIGN, "%s: w, x and y must be 16-byte aligned", what);
   const size_t ny = static_cast<size_t>(m * n) * 4;
-  if (overlap(y, ny, x, static_cast<size_t>(m * k) * 4) || overlap(y, ny, w, q4k_bytes(n, k)))
-    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemv: y overlaps an input");
-  if (int rc = check_device()) return rc;
+  if (overlap(y, ny, x, static_cast<size_t>(m * k) * 4) ||
+      overlap(y, ny, w, q4k_bytes(n, k, block)))
+    return fail(Q4K_ERR_INVALID_ARG, "%s: y overlaps an input", what);
+  return check_device();
+}
+
+int q4k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (int rc = gemv_checks("q4k_gemv", w, x, y, m, n, k, 144u)) return rc;
   return launched(q4k::launch_gemv(static_cast<const uint8_t*>(w), x, y, m, n, k,
                                    static_cast<hipStream_t>(stream)),
                   "q4k_gemv");
+}
+
+int q5k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (int rc = gemv_checks("q5k_gemv", w, x, y, m, n, k, 176u)) return rc;
+  return launched(q4k::launch_q5k_gemv(static_cast<const uint8_t*>(w), x, y, m, n, k,
+                                       static_cast<hipStream_t>(stream)),
+                  "q5k_gemv");
 }
 
 int q4k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m, int64_t n, int64_t k,
@@ -185,7 +201,7 @@ int q4k_swiglu_mlp(const void* w_gate, const void* w_up, const void* w_down, con
 }
 
 static int dequant_checks(const char* what, const void* w, const void* out, int64_t n,
-                          int64_t k, size_t elem) {
+                          int64_t k, size_t elem, size_t block = 144u) {
   if (!w || !out) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
   if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
   if (!valid_k(k))
@@ -193,7 +209,8 @@ static int dequant_checks(const char* what, const void* w, const void* out, int6
                 (long long)k);
   if (!aligned16(w) || !aligned16(out))
     return fail(Q4K_ERR_ALIGN, "%s: w and out must be 16-byte aligned", what);
-  if (overlap(out, static_cast<size_t>(n) * static_cast<size_t>(k) * elem, w, q4k_bytes(n, k)))
+  if (overlap(out, static_cast<size_t>(n) * static_cast<size_t>(k) * elem, w,
+              q4k_bytes(n, k, block)))
     return fail(Q4K_ERR_INVALID_ARG, "%s: out overlaps w", what);
   return check_device();
 }
@@ -210,6 +227,20 @@ int q4k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k, void
   return launched(q4k::launch_dequant_bf16(static_cast<const uint8_t*>(w), out, n, k,
                                            static_cast<hipStream_t>(stream)),
                   "q4k_dequantize_bf16");
+}
+
+int q5k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k, void* stream) {
+  if (int rc = dequant_checks("q5k_dequantize_f32", w, out, n, k, 4, 176u)) return rc;
+  return launched(q4k::launch_q5k_dequant_f32(static_cast<const uint8_t*>(w), out, n, k,
+                                              static_cast<hipStream_t>(stream)),
+                  "q5k_dequantize_f32");
+}
+
+int q5k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k, void* stream) {
+  if (int rc = dequant_checks("q5k_dequantize_bf16", w, out, n, k, 2, 176u)) return rc;
+  return launched(q4k::launch_q5k_dequant_bf16(static_cast<const uint8_t*>(w), out, n, k,
+                                               static_cast<hipStream_t>(stream)),
+                  "q5k_dequantize_bf16");
 }
 
 int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {

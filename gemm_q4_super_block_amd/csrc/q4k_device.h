@@ -21,7 +21,21 @@
 namespace q4k {
 
 constexpr int kQK = 256;          // weights per super-block
-constexpr int kBlockBytes = 144;  // bytes per super-block
+constexpr int kBlockBytes = 144;  // bytes per Q4_K super-block
+
+// Q5_K (the 5-bit sibling; "CPU kernel parity ..." PR page: k4 and k5 share
+// one fused form; the layout is the GGUF reading, the pages print none):
+//   176 bytes = the Q4_K header (16 bytes), 32 high-bit bytes qh, then the
+//   128 Q4_K nibble bytes.  Weight 64g + r takes bit (2g + [r >= 32]) of
+//   qh[r mod 32] as its fifth bit: q = nibble + 16 * bit.
+constexpr int kQ5BlockBytes = 176;
+constexpr int kQ5HighOffset = 16;   // qh[32]
+constexpr int kQ5QuantOffset = 48;  // qs[128]
+
+template <int FMT>
+constexpr int block_bytes() {
+  return FMT == 5 ? kQ5BlockBytes : kBlockBytes;
+}
 
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
@@ -93,6 +107,19 @@ __device__ __forceinline__ void dequant_dword(uint32_t v, const GroupScales& s, 
   hi[3] = __builtin_fmaf(s.a_hi, h23.y, -s.b_hi);
 }
 
+// Q5_K: the four 5-bit quants of one quant dword's low (shift 0) or high
+// (shift 4) nibbles, as bytes: nibbles plus the fifth bits, bit `hb` of each
+// byte of the matching high-bit dword (hb = 2g for low nibbles, 2g + 1 for
+// high ones).
+__device__ __forceinline__ uint32_t q5_bytes(uint32_t v, uint32_t h, int shift, int hb) {
+  return ((v >> shift) & 0x0F0F0F0Fu) | (((h >> hb) & 0x01010101u) << 4);
+}
+
+// Byte i of v as an exact float (one v_cvt_f32_ubyte<i>).
+__device__ __forceinline__ float ubyte_f32(uint32_t v, int i) {
+  return static_cast<float>((v >> (8 * i)) & 0xFFu);
+}
+
 // Round two fp32 values to bf16 (nearest even, v_cvt_pk_bf16_f32) and pack
 // them: first value in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -132,6 +159,20 @@ __device__ __forceinline__ void dequant16_bf16(uint4 q, const GroupScales& s, ui
   lo8[4] = l1.x; lo8[5] = l1.y; lo8[6] = l1.z; lo8[7] = l1.w;
   hi8[0] = h0.x; hi8[1] = h0.y; hi8[2] = h0.z; hi8[3] = h0.w;
   hi8[4] = h1.x; hi8[5] = h1.y; hi8[6] = h1.z; hi8[7] = h1.w;
+}
+
+// Q5_K: 8 weights as bf16 from the 5-bit quant bytes of two dwords (q5_bytes),
+// each fma(a5, q, -b) with a5 = d*sc (no 2^9: the bytes are widened exactly by
+// v_cvt_f32_ubyte), rounded to nearest even, packed in pairs.
+__device__ __forceinline__ uint4 dequant8_bf16_q5(uint32_t q0, uint32_t q1, float a5, float b) {
+  return make_uint4(pack_bf16x2(__builtin_fmaf(a5, ubyte_f32(q0, 0), -b),
+                                __builtin_fmaf(a5, ubyte_f32(q0, 1), -b)),
+                    pack_bf16x2(__builtin_fmaf(a5, ubyte_f32(q0, 2), -b),
+                                __builtin_fmaf(a5, ubyte_f32(q0, 3), -b)),
+                    pack_bf16x2(__builtin_fmaf(a5, ubyte_f32(q1, 0), -b),
+                                __builtin_fmaf(a5, ubyte_f32(q1, 1), -b)),
+                    pack_bf16x2(__builtin_fmaf(a5, ubyte_f32(q1, 2), -b),
+                                __builtin_fmaf(a5, ubyte_f32(q1, 3), -b)));
 }
 
 __device__ __forceinline__ uint4 load16(const uint8_t* p) {

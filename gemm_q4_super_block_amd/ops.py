@@ -2,27 +2,29 @@
 
 PyTorch provides device memory and the current stream; every computation runs
 in libq4k's HIP kernels.  Weights are ``torch.uint8`` tensors holding raw Q4_K
-super-blocks, shape ``[n, (k // 256) * 144]``.
+super-blocks, shape ``[n, (k // 256) * 144]`` (Q5_K: 176-byte blocks,
+``[n, (k // 256) * 176]``, for the ``q5k_`` functions).
 """
 from __future__ import annotations
 
 import torch
 
 from . import _lib
-from ._lib import Q4K_BLOCK_BYTES, Q4K_QK, check
+from ._lib import Q4K_BLOCK_BYTES, Q4K_QK, Q5K_BLOCK_BYTES, check
 
 
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _q4k_shape(w: torch.Tensor):
+def _q4k_shape(w: torch.Tensor, block: int = Q4K_BLOCK_BYTES):
     if w.dtype != torch.uint8 or w.dim() != 2 or not w.is_cuda or not w.is_contiguous():
-        raise ValueError("Q4_K weights must be a contiguous CUDA uint8 tensor [n, k/256*144]")
+        raise ValueError("weights must be a contiguous CUDA uint8 tensor [n, k/256*%d]" % block)
     n, row_bytes = w.shape
-    if row_bytes % Q4K_BLOCK_BYTES:
-        raise ValueError("row length %d is not a whole number of 144-byte blocks" % row_bytes)
-    return n, (row_bytes // Q4K_BLOCK_BYTES) * Q4K_QK
+    if row_bytes % block:
+        raise ValueError("row length %d is not a whole number of %d-byte blocks"
+                         % (row_bytes, block))
+    return n, (row_bytes // block) * Q4K_QK
 
 
 def _dev_tensor(t: torch.Tensor, dtype, what: str) -> torch.Tensor:
@@ -33,7 +35,16 @@ def _dev_tensor(t: torch.Tensor, dtype, what: str) -> torch.Tensor:
 
 def gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """y = x W^T for fp32 x [k] or [m, k] (m <= 32); returns fp32 [n] or [m, n]."""
-    n, k = _q4k_shape(w)
+    return _gemv(w, x, out, Q4K_BLOCK_BYTES, _lib.q4k_gemv)
+
+
+def q5k_gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemv() for a Q5_K W (uint8 [n, k/256*176])."""
+    return _gemv(w, x, out, Q5K_BLOCK_BYTES, _lib.q5k_gemv)
+
+
+def _gemv(w, x, out, block, fn):
+    n, k = _q4k_shape(w, block)
     _dev_tensor(x, torch.float32, "x")
     squeeze = x.dim() == 1
     x2 = x.view(1, -1) if squeeze else x
@@ -42,7 +53,7 @@ def gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> t
     m = x2.shape[0]
     y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=w.device)
     _dev_tensor(y, torch.float32, "out")
-    check(_lib.q4k_gemv(w.data_ptr(), x2.data_ptr(), y.data_ptr(), m, n, k, _stream(w.device)))
+    check(fn(w.data_ptr(), x2.data_ptr(), y.data_ptr(), m, n, k, _stream(w.device)))
     return y.view(n) if squeeze else y
 
 
@@ -94,4 +105,20 @@ def dequantize_bf16(w: torch.Tensor) -> torch.Tensor:
     n, k = _q4k_shape(w)
     out = torch.empty((n, k), dtype=torch.bfloat16, device=w.device)
     check(_lib.q4k_dequantize_bf16(w.data_ptr(), out.data_ptr(), n, k, _stream(w.device)))
+    return out
+
+
+def q5k_dequantize_f32(w: torch.Tensor) -> torch.Tensor:
+    """Dequantized Q5_K W as fp32 [n, k]."""
+    n, k = _q4k_shape(w, Q5K_BLOCK_BYTES)
+    out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    check(_lib.q5k_dequantize_f32(w.data_ptr(), out.data_ptr(), n, k, _stream(w.device)))
+    return out
+
+
+def q5k_dequantize_bf16(w: torch.Tensor) -> torch.Tensor:
+    """Dequantized Q5_K W as bf16 [n, k] (nearest-even rounding of the fp32 weight)."""
+    n, k = _q4k_shape(w, Q5K_BLOCK_BYTES)
+    out = torch.empty((n, k), dtype=torch.bfloat16, device=w.device)
+    check(_lib.q5k_dequantize_bf16(w.data_ptr(), out.data_ptr(), n, k, _stream(w.device)))
     return out

@@ -65,6 +65,8 @@ extern "C" {
 #define Q4K_QK 256
 #define Q4K_BLOCK_BYTES 144
 #define Q4K_GEMV_MAX_M 32
+/* Bytes per Q5_K super-block (the q5k_ entry points). */
+#define Q5K_BLOCK_BYTES 176
 
 /* Checks that a HIP device is present and is gfx950, for the current device.
  * Idempotent and cheap after the first call per device; the compute entry
@@ -140,6 +142,31 @@ int q4k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
  *   buf 16-byte aligned, bytes a positive multiple of 16; sink 4-byte aligned.
  * Errors: Q4K_ERR_INVALID_ARG, Q4K_ERR_ALIGN, Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
 int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/* ---- Q5_K, the 5-bit sibling ------------------------------------------------
+ * [P3, the kernel work: the 4-bit and 5-bit k-quants "share one fused form".]
+ * The pages print no Q5_K layout either; the library reads the Q4_K
+ * super-block with one high-bit plane added:
+ *   176 bytes encode 256 weights.
+ *     bytes 0..15    d, dmin and s[12] exactly as in Q4_K
+ *     bytes 16..47   qh[32]: bit (2g + [r >= 32]) of qh[r mod 32] is the fifth
+ *                    bit of weight 64g + r
+ *     bytes 48..175  qs[128]: the 4-bit nibbles, Q4_K's map
+ *   q_i = nibble_i + 16 * bit_i (0..31); weight i = d * sc[i/32] * q_i -
+ *   dmin * mn[i/32], rounded once to fp32.
+ * A matrix is laid out as for Q4_K with 176-byte blocks. */
+
+/* Decode GEMV on Q5_K weights: as q4k_gemv (same x, y, m, n, k, tolerance
+ * and errors) with w a Q5_K matrix [n, k], 16-byte aligned. */
+int q5k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
+             int64_t k, void* stream);
+
+/* Diagnostic dequantization of a Q5_K matrix: as q4k_dequantize_f32 / _bf16
+ * (exact weight rounded once to fp32; bf16 = nearest even of that). */
+int q5k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k,
+                       void* stream);
+int q5k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,13 +21,14 @@ HEADER = os.path.join(ROOT, "include", "q4k.h")
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(q4k_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(q[45]k_\w+)\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for name in ("q4k_gemv", "q4k_gemm", "q4k_swiglu_mlp", "q4k_init", "q4k_last_error",
-                 "q4k_dequantize_f32", "q4k_dequantize_bf16", "q4k_device_name", "q4k_version"):
+                 "q4k_dequantize_f32", "q4k_dequantize_bf16", "q4k_device_name", "q4k_version",
+                 "q5k_gemv", "q5k_dequantize_f32", "q5k_dequantize_bf16"):
         assert name in syms
 
 
@@ -42,7 +43,8 @@ def test_library_loads_and_exports_every_declared_symbol():
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("Q4K_OK", "Q4K_ERR_INVALID_ARG", "Q4K_ERR_ALIGN", "Q4K_ERR_DEVICE",
-                 "Q4K_ERR_LAUNCH", "Q4K_QK", "Q4K_BLOCK_BYTES", "Q4K_GEMV_MAX_M"):
+                 "Q4K_ERR_LAUNCH", "Q4K_QK", "Q4K_BLOCK_BYTES", "Q4K_GEMV_MAX_M",
+                 "Q5K_BLOCK_BYTES"):
         mm = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
         assert mm, name
         assert int(mm.group(1)) == getattr(_lib, name), name
@@ -133,3 +135,17 @@ def test_read_probe_rejects_bad_arguments():
     assert _lib.q4k_read_probe(A, 4096, 2 * A + 2, None) == _lib.Q4K_ERR_ALIGN
     assert _lib.q4k_read_probe(A, 4096, A + 64, None) == _lib.Q4K_ERR_INVALID_ARG  # sink in buf
     assert _lib.q4k_last_error().startswith("q4k_read_probe")
+
+
+def test_q5k_rejects_bad_arguments():
+    assert _lib.q5k_gemv(0, A, 2 * A, 1, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q4k_last_error().startswith("q5k_gemv")
+    assert _lib.q5k_gemv(A, 2 * A, 3 * A, 33, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q5k_gemv(A, 2 * A, 3 * A, 1, 16, 300, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q5k_gemv(A + 8, 2 * A, 3 * A, 1, 16, 256, None) == _lib.Q4K_ERR_ALIGN
+    # 16 rows of one 176-byte block span 2816 bytes from A: y may not start inside
+    assert _lib.q5k_gemv(A, 2 * A, A + 2800, 1, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q5k_dequantize_f32(0, A, 4, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q5k_dequantize_bf16(A, 2 * A + 4, 4, 256, None) == _lib.Q4K_ERR_ALIGN
+    assert _lib.q5k_dequantize_f32(A, A + 688, 4, 256, None) == _lib.Q4K_ERR_INVALID_ARG  # out in w
+    assert _lib.q4k_last_error().startswith("q5k_dequantize_f32")

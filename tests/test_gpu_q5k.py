@@ -1,0 +1,123 @@
+"""Parity of the Q5_K entry points (q5k_gemv, q5k_dequantize_*) with the oracle.
+
+Same bars as Q4_K: dequantized weights bit-exact (fp32, and bf16 = nearest
+even of fp32); GEMV within 1e-4 * sum|w x| per output.  Shapes cover each
+batch-1 launch shape (up to 8192 rows; taller with k <= 4096, x in
+registers; taller past one K step), ragged K steps, the batched passes and
+the degenerate fields of the format.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from golden_io import hand_blocks
+from q5k_pack import pack_q5k_block
+
+pytestmark = pytest.mark.gpu
+
+GEMV_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def q4k():
+    if torch.cuda.device_count() == 0:
+        pytest.skip("no GPU")
+    import gemm_q4_super_block_amd as lib
+    lib.load_library()
+    torch.cuda.set_device(0)
+    return lib
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def assert_within(got, ref, scale, tol, what):
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    bad = err > tol * scale
+    assert not bad.any(), "%s: %d outputs outside %g * sum|w x|, worst %g" % (
+        what, bad.sum(), tol, (err / np.maximum(tol * scale, 1e-300)).max())
+
+
+def check_dequant(q4k, w, n, k):
+    got = q4k.q5k_dequantize_f32(dev(w)).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oracle.q5k_dequant_f32(w, n, k).view(np.uint32))
+    got16 = q4k.q5k_dequantize_bf16(dev(w)).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got16, oracle.q5k_dequant_bf16(w, n, k))
+
+
+@pytest.mark.parametrize("n,k,seed", [(256, 1024, 0), (256, 1024, 1), (37, 768, 2),
+                                      (4096, 4096, 0)])
+def test_q5k_dequant_bit_exact(q4k, n, k, seed):
+    check_dequant(q4k, synth.q5k_weights(n, k, seed=seed), n, k)
+
+
+def test_q5k_dequant_hand_blocks(q4k):
+    blocks = hand_blocks("hand_blocks_q5k.txt", block_bytes=176)
+    w = np.stack([b for b, _ in blocks.values()])
+    got = q4k.q5k_dequantize_f32(dev(w)).cpu().numpy()
+    for row, (_, expected) in zip(got, blocks.values()):
+        assert np.array_equal(row.astype(np.float64), expected)
+    check_dequant(q4k, w, w.shape[0], 256)
+
+
+def test_q5k_dequant_degenerate_fields(q4k):
+    rng = np.random.default_rng(5)
+    rows = []
+    for d_bits, dmin_bits in [(0x0001, 0x0000), (0x03FF, 0x0201), (0x7BFF, 0x7BFF),
+                              (0x3C00, 0x0000), (0x0000, 0x3C00)]:
+        for q in (np.zeros(256, np.int64), np.full(256, 31), np.full(256, 16),
+                  rng.integers(0, 32, 256)):
+            sc = rng.integers(0, 64, 8)
+            mn = rng.integers(0, 64, 8)
+            rows.append(pack_q5k_block(d_bits, dmin_bits, sc, mn, q))
+    w = np.stack(rows)
+    check_dequant(q4k, w, w.shape[0], 256)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_q5k_gemv_small(q4k, seed):
+    n, k = 256, 1024
+    w = synth.q5k_weights(n, k, seed=seed)
+    x = synth.normal_f32(k, seed=seed)
+    y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
+    yr, a = oracle.q5k_gemv(w, x, n, k)
+    assert_within(y, yr[0], a[0], GEMV_TOL, "q5k gemv 256x1024 seed %d" % seed)
+
+
+@pytest.mark.parametrize("n,k", [(4096, 4096), (1, 256), (300, 768), (33, 4352), (64, 14336),
+                                 (8200, 768), (9001, 4096), (8193, 4352)])
+def test_q5k_gemv_shapes(q4k, n, k):
+    w = synth.q5k_weights(n, k, seed=n % 97)
+    x = synth.normal_f32(k, seed=n % 97)
+    y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
+    yr, a = oracle.q5k_gemv(w, x, n, k)
+    assert_within(y, yr[0], a[0], GEMV_TOL, "q5k gemv %dx%d" % (n, k))
+
+
+@pytest.mark.parametrize("m", [2, 3, 5, 8, 9, 32])
+def test_q5k_gemv_batched(q4k, m):
+    n, k = 300, 1024
+    w = synth.q5k_weights(n, k, seed=m)
+    x = synth.normal_f32((m, k), seed=m)
+    y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
+    yr, a = oracle.q5k_gemv(w, x, n, k)
+    assert_within(y, yr, a, GEMV_TOL, "q5k gemv m=%d" % m)
+
+
+def test_q5k_gemv_unit_vectors_give_columns(q4k):
+    # y(e_c) is column c of the dequantized W (one non-zero product per row)
+    n, k = 40, 512
+    w = synth.q5k_weights(n, k, seed=3)
+    W = oracle.q5k_dequant_f32(w, n, k)
+    cols = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 300, 511]
+    x = np.zeros((len(cols), k), np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
+    for i, c in enumerate(cols):
+        assert np.array_equal(y[i], W[:, c]), c
