@@ -60,7 +60,7 @@ def parse():
                    help="also run one device copy of 256 MiB (counter calibration)")
     p.add_argument("--only", default="",
                    help="comma list of kernels to run "
-                        "(gemv,q5k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,dequant,read_probe)")
+                        "(gemv,q5k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,q5k_gemm,dequant,read_probe)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
     p.add_argument("--eager-only", action="store_true",
                    help="time only the eagerly enqueued launches (no HIP graph replay)")
@@ -207,6 +207,19 @@ def main():
                 _lib.check(_lib.q4k_gemm(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
             kernels.append(("gemm_512x%dx4096" % n, run, nbytes, 2 * m * n * k, rot))
 
+    # ---- prefill GEMM on Q5_K weights, M = 512, N = K = 4096
+    if want("q5k_gemm"):
+        m, n, k = 512, D_MODEL, D_MODEL
+        xb = synth.normal_bf16((m, k), seed=0)
+        w = synth.q5k_weights(n, k, seed=0)
+        nbytes = n * (k // 256) * Q5K_BLOCK + 2 * m * k + 4 * m * n
+        rot = Rotor(torch, [w, xb.view(np.int16), np.zeros((m, n), np.float32)], nbytes)
+
+        def run_q5g(i, sp, rot=rot, m=m, n=n, k=k):
+            wd, xd, yd = rot[i]
+            _lib.check(_lib.q5k_gemm(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
+        kernels.append(("q5k_gemm_512x4096x4096", run_q5g, nbytes, 2 * m * n * k, rot))
+
     # ---- dequant export (bf16) of the 4096 x 4096 matrix
     if want("dequant"):
         n = k = D_MODEL
@@ -294,7 +307,7 @@ def main():
             r["hbm_frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
         if flop:
             r["tflops"] = round(flop / (us * 1e-6) / 1e12, 2)
-        if name.startswith("gemm_") or name.startswith("sweep_gemm"):
+        if name.startswith("gemm_") or name.startswith("sweep_gemm") or name.startswith("q5k_gemm"):
             r["mfma_frac"] = round(r["tflops"] / BF16_PEAK_TFLOPS, 4)
         per[name] = r
 
@@ -424,6 +437,9 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "gemm_512x4096x4096" if threads == 131072 else "gemm_other"
     if "k_gemm_q4k_kslice<1, 2>" in name:
         return "sweep_gemm_14336x4096"
+    sk = _template_args(name, "k_gemm_q4k")
+    if sk and len(sk) > 5 and sk[5] == "5":
+        return "q5k_gemm_512x4096x4096"
     if "k_gemm_q4k<4, 1, 1, 4, 2>" in name:
         return "gemm_other"
     if "k_gemm_q4k<1, 4, 1, 1, 2>" in name:
@@ -561,6 +577,11 @@ def spot_check(kernels, args, np, torch):
             rows = np.arange(0, 4096, 37)
             yr, a = oracle.q5k_gemv_rows(w, x, 4096, 4096, rows)
             res[name] = float((np.abs(y[rows] - yr[0]) / (1e-4 * a[0])).max())
+        elif name == "q5k_gemm_512x4096x4096":
+            w, xb, y = (a.cpu().numpy() for a in t)
+            cols = np.arange(0, 4096, 256)
+            yr, a = oracle.q5k_gemm_cols(w, xb.view(np.uint16), 4096, 4096, cols)
+            res[name] = float((np.abs(y[:, cols] - yr) / (1e-2 * a)).max())
         elif name.startswith("gemm_512"):
             w, xb, y = (a.cpu().numpy() for a in t)
             n = y.shape[1]

@@ -38,6 +38,7 @@ SIGNATURES = {
     "q4k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q4k_read_probe": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "q5k_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q5k_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q5k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q5k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
 }
@@ -140,3 +141,7 @@ def q5k_dequantize_f32(w, out, n, k, stream) -> int:
 
 def q5k_dequantize_bf16(w, out, n, k, stream) -> int:
     return load().q5k_dequantize_bf16(w, out, n, k, stream)
+
+
+def q5k_gemm(w, x_bf16, y, m, n, k, stream) -> int:
+    return load().q5k_gemm(w, x_bf16, y, m, n, k, stream)

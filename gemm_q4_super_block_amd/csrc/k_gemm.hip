@@ -40,7 +40,7 @@ constexpr int kBN = 128;       // weight rows per tile
 constexpr int kBK = 64;        // weights per K step (one quant group)
 constexpr int kLdsStride = 72; // bf16 per LDS row: 64 + 8 pad (144 B rows)
 
-template <int WAVES_M, int WAVES_N, int TI, int TJ, int MINB>
+template <int WAVES_M, int WAVES_N, int TI, int TJ, int MINB, int FMT = 4>
 __global__ __launch_bounds__(256, MINB) void k_gemm_q4k(const uint8_t* __restrict__ w,
                                                         const uint16_t* __restrict__ x,
                                                         float* __restrict__ y, int m, int n, int k,
@@ -67,8 +67,8 @@ __global__ __launch_bounds__(256, MINB) void k_gemm_q4k(const uint8_t* __restric
   // Tile-fill role: weight row f_row of the tile, 16-byte half f_hh of the group.
   const int f_row = t >> 1;
   const int f_hh = t & 1;
-  const uint8_t* f_base =
-      w + static_cast<size_t>(min(n0 + f_row, n - 1)) * kb_count * kBlockBytes;
+  constexpr int kBB = block_bytes<FMT>();
+  const uint8_t* f_base = w + static_cast<size_t>(min(n0 + f_row, n - 1)) * kb_count * kBB;
 
   // A-operand role: rows of X this lane feeds (clamped; clamped rows are not stored).
   const uint16_t* a_ptr[TI];
@@ -88,11 +88,19 @@ __global__ __launch_bounds__(256, MINB) void k_gemm_q4k(const uint8_t* __restric
 
   // Loads past the last step re-read the last step (results unused) so the
   // pipeline needs no branches.
-  auto load_w = [&](int s, uint4& hd, uint4& q) {
+  // Q5_K also loads the 16 high-bit bytes of this thread's 32 weights (qh is
+  // unused for Q4_K).
+  auto load_w = [&](int s, uint4& hd, uint4& q, uint4& qh) {
     const int sc = min(s, s_end - 1);
-    const uint8_t* p = f_base + static_cast<size_t>(sc >> 2) * kBlockBytes;
+    const uint8_t* p = f_base + static_cast<size_t>(sc >> 2) * kBB;
     hd = load16(p);
-    q = load16(p + 16 + 32 * (sc & 3) + 16 * f_hh);
+    if constexpr (FMT == 5) {
+      q = load16(p + kQ5QuantOffset + 32 * (sc & 3) + 16 * f_hh);
+      qh = load16(p + kQ5HighOffset + 16 * f_hh);
+    } else {
+      q = load16(p + 16 + 32 * (sc & 3) + 16 * f_hh);
+      qh = q;
+    }
   };
   auto load_x = [&](int s, uint4 (&xr)[TI][4]) {
     const int sc = min(s, s_end - 1);
@@ -103,10 +111,16 @@ __global__ __launch_bounds__(256, MINB) void k_gemm_q4k(const uint8_t* __restric
       for (int c = 0; c < 4; ++c) xr[i][c] = *reinterpret_cast<const uint4*>(p + 8 * c);
     }
   };
-  auto store_w = [&](int buf, int s, const uint4& hd, const uint4& q) {
-    const GroupScales sc = group_scales(hd, s & 3);
+  auto store_w = [&](int buf, int s, const uint4& hd, const uint4& q, const uint4& qh) {
+    GroupScales sc = group_scales(hd, s & 3);
     uint32_t lo8[8], hi8[8];
-    dequant16_bf16(q, sc, lo8, hi8);
+    if constexpr (FMT == 5) {
+      sc.a_lo *= 1.0f / kNibbleUnscale;  // exact integers, not q * 2^-9
+      sc.a_hi *= 1.0f / kNibbleUnscale;
+      dequant16_bf16_q5(q, qh, sc, s & 3, lo8, hi8);
+    } else {
+      dequant16_bf16(q, sc, lo8, hi8);
+    }
     uint16_t* dst = &ws[buf][f_row * kLdsStride + 16 * f_hh];
     *reinterpret_cast<uint4*>(dst) = make_uint4(lo8[0], lo8[1], lo8[2], lo8[3]);
     *reinterpret_cast<uint4*>(dst + 8) = make_uint4(lo8[4], lo8[5], lo8[6], lo8[7]);
@@ -138,25 +152,25 @@ __global__ __launch_bounds__(256, MINB) void k_gemm_q4k(const uint8_t* __restric
   // at step s the MFMAs read LDS buffer s%2 and X registers set s%2, while
   // the weights of step s+1 are dequantized into the other LDS buffer and the
   // X fragments of step s+2 and raw weights of step s+2 are fetched.
-  uint4 xA[TI][4], xB[TI][4], hA, qA, hB, qB;
-  load_w(s_begin, hA, qA);
+  uint4 xA[TI][4], xB[TI][4], hA, qA, eA, hB, qB, eB;  // e: Q5_K high bits
+  load_w(s_begin, hA, qA, eA);
   load_x(s_begin, xA);
   load_x(s_begin + 1, xB);
-  store_w(0, s_begin, hA, qA);
-  load_w(s_begin + 1, hB, qB);
-  load_w(s_begin + 2, hA, qA);
+  store_w(0, s_begin, hA, qA, eA);
+  load_w(s_begin + 1, hB, qB, eB);
+  load_w(s_begin + 2, hA, qA, eA);
   __syncthreads();
   for (int s = s_begin; s < s_end; s += 2) {
     mfma_step(0, xA);
     load_x(s + 2, xA);
-    if (s + 1 < s_end) store_w(1, s + 1, hB, qB);
-    load_w(s + 3, hB, qB);
+    if (s + 1 < s_end) store_w(1, s + 1, hB, qB, eB);
+    load_w(s + 3, hB, qB, eB);
     __syncthreads();
     if (s + 1 >= s_end) break;
     mfma_step(1, xB);
     load_x(s + 3, xB);
-    if (s + 2 < s_end) store_w(0, s + 2, hA, qA);
-    load_w(s + 4, hA, qA);
+    if (s + 2 < s_end) store_w(0, s + 2, hA, qA, eA);
+    load_w(s + 4, hA, qA, eA);
     __syncthreads();
   }
 
@@ -193,7 +207,7 @@ __global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ y, size_t 
   }
 }
 
-template <int WAVES_M, int WAVES_N, int TI, int TJ, int MINB>
+template <int WAVES_M, int WAVES_N, int TI, int TJ, int MINB, int FMT = 4>
 hipError_t launch(const uint8_t* w, const uint16_t* x, float* y, int m, int n, int k,
                   int splits_wanted, hipStream_t stream) {
   constexpr int BM = WAVES_M * 32 * TI;
@@ -212,7 +226,7 @@ hipError_t launch(const uint8_t* w, const uint16_t* x, float* y, int m, int n, i
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_gemm_q4k<WAVES_M, WAVES_N, TI, TJ, MINB>), dim3(tiles_n, tiles_m, splits),
+  hipLaunchKernelGGL((k_gemm_q4k<WAVES_M, WAVES_N, TI, TJ, MINB, FMT>), dim3(tiles_n, tiles_m, splits),
                      dim3(256), 0, stream, w, x, y, m, n, k, per, splits > 1 ? 1 : 0);
   return hipGetLastError();
 }
@@ -894,6 +908,19 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
   // 128 x 128 tiles, two workgroups per CU.
   const int tiles = ((mi + 127) / 128) * tiles_n;
   return launch<4, 1, 1, 4, 2>(w, x, y, mi, ni, ki, splits_for(tiles, steps), stream);
+}
+
+// Q5_K: the tile kernel that dequantizes each step's weight tile into LDS (the
+// register-dequant kernels read Q4_K's 144-byte records), split K when the
+// tile grid is small.
+hipError_t launch_q5k_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                           int64_t k, hipStream_t stream) {
+  const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
+  const int steps = ki / kBK;
+  const int tiles_n = (ni + kBN - 1) / kBN;
+  if (mi <= 32) return launch<1, 4, 1, 1, 2, 5>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
+  const int tiles = ((mi + 127) / 128) * tiles_n;
+  return launch<4, 1, 1, 4, 2, 5>(w, x, y, mi, ni, ki, splits_for(tiles, steps), stream);
 }
 
 }  // namespace q4k

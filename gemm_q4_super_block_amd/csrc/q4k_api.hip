@@ -153,24 +153,38 @@ int q5k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int6
                   "q5k_gemv");
 }
 
-int q4k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m, int64_t n, int64_t k,
-             void* stream) {
-  if (!w || !x_bf16 || !y) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: null pointer");
-  if (m < 1 || m > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: m=%lld", (long long)m);
-  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: n=%lld", (long long)n);
+// Argument checks shared by the Q4_K and Q5_K GEMMs.
+static int gemm_checks(const char* what, const void* w, const uint16_t* x_bf16, const float* y,
+                       int64_t m, int64_t n, int64_t k, size_t block) {
+  if (!w || !x_bf16 || !y) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
+  if (m < 1 || m > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: m=%lld", what, (long long)m);
+  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
   if (!valid_k(k))
-    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: k=%lld is not a positive multiple of 256",
+    return fail(Q4K_ERR_INVALID_ARG, "%s: k=%lld is not a positive multiple of 256", what,
                 (long long)k);
   if (!aligned16(w) || !aligned16(x_bf16) || !aligned16(y))
-    return fail(Q4K_ERR_ALIGN, "q4k_gemm: w, x and y must be 16-byte aligned");
+    return fail(Q4K_ERR_ALIGN, "%s: w, x and y must be 16-byte aligned", what);
   const size_t ny = static_cast<size_t>(m) * static_cast<size_t>(n) * 4;
   if (overlap(y, ny, x_bf16, static_cast<size_t>(m) * static_cast<size_t>(k) * 2) ||
-      overlap(y, ny, w, q4k_bytes(n, k)))
-    return fail(Q4K_ERR_INVALID_ARG, "q4k_gemm: y overlaps an input");
-  if (int rc = check_device()) return rc;
+      overlap(y, ny, w, q4k_bytes(n, k, block)))
+    return fail(Q4K_ERR_INVALID_ARG, "%s: y overlaps an input", what);
+  return check_device();
+}
+
+int q4k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (int rc = gemm_checks("q4k_gemm", w, x_bf16, y, m, n, k, 144u)) return rc;
   return launched(q4k::launch_gemm(static_cast<const uint8_t*>(w), x_bf16, y, m, n, k,
                                    static_cast<hipStream_t>(stream)),
                   "q4k_gemm");
+}
+
+int q5k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (int rc = gemm_checks("q5k_gemm", w, x_bf16, y, m, n, k, 176u)) return rc;
+  return launched(q4k::launch_q5k_gemm(static_cast<const uint8_t*>(w), x_bf16, y, m, n, k,
+                                       static_cast<hipStream_t>(stream)),
+                  "q5k_gemm");
 }
 
 int q4k_swiglu_mlp(const void* w_gate, const void* w_up, const void* w_down, const float* x,

@@ -175,6 +175,25 @@ __device__ __forceinline__ uint4 dequant8_bf16_q5(uint32_t q0, uint32_t q1, floa
                                 __builtin_fmaf(a5, ubyte_f32(q1, 3), -b)));
 }
 
+// Q5_K: dequant16_bf16 for 16 quant bytes of group g with the 16 high-bit
+// bytes of the same weights (qh[16hh ..] for quant bytes 32g + 16hh ..); s.a_*
+// must already be d*sc (without the 2^9).
+__device__ __forceinline__ void dequant16_bf16_q5(uint4 q, uint4 qh, const GroupScales& s, int g,
+                                                  uint32_t lo8[8], uint32_t hi8[8]) {
+  const uint4 l0 = dequant8_bf16_q5(q5_bytes(q.x, qh.x, 0, 2 * g), q5_bytes(q.y, qh.y, 0, 2 * g),
+                                    s.a_lo, s.b_lo);
+  const uint4 l1 = dequant8_bf16_q5(q5_bytes(q.z, qh.z, 0, 2 * g), q5_bytes(q.w, qh.w, 0, 2 * g),
+                                    s.a_lo, s.b_lo);
+  const uint4 h0 = dequant8_bf16_q5(q5_bytes(q.x, qh.x, 4, 2 * g + 1),
+                                    q5_bytes(q.y, qh.y, 4, 2 * g + 1), s.a_hi, s.b_hi);
+  const uint4 h1 = dequant8_bf16_q5(q5_bytes(q.z, qh.z, 4, 2 * g + 1),
+                                    q5_bytes(q.w, qh.w, 4, 2 * g + 1), s.a_hi, s.b_hi);
+  lo8[0] = l0.x; lo8[1] = l0.y; lo8[2] = l0.z; lo8[3] = l0.w;
+  lo8[4] = l1.x; lo8[5] = l1.y; lo8[6] = l1.z; lo8[7] = l1.w;
+  hi8[0] = h0.x; hi8[1] = h0.y; hi8[2] = h0.z; hi8[3] = h0.w;
+  hi8[4] = h1.x; hi8[5] = h1.y; hi8[6] = h1.z; hi8[7] = h1.w;
+}
+
 __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

@@ -39,6 +39,8 @@ hipError_t launch_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64
 // Q5_K (176-byte super-blocks): GEMV and the dequant exports.
 hipError_t launch_q5k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                            int64_t k, hipStream_t stream);
+hipError_t launch_q5k_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                           int64_t k, hipStream_t stream);
 hipError_t launch_q5k_dequant_f32(const uint8_t* w, float* out, int64_t n, int64_t k,
                                   hipStream_t stream);
 hipError_t launch_q5k_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64_t k,

@@ -59,14 +59,23 @@ def _gemv(w, x, out, block, fn):
 
 def gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X W^T for bf16 X [m, k]; returns fp32 [m, n]."""
-    n, k = _q4k_shape(w)
+    return _gemm(w, x, out, Q4K_BLOCK_BYTES, _lib.q4k_gemm)
+
+
+def q5k_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm() for a Q5_K W (uint8 [n, k/256*176])."""
+    return _gemm(w, x, out, Q5K_BLOCK_BYTES, _lib.q5k_gemm)
+
+
+def _gemm(w, x, out, block, fn):
+    n, k = _q4k_shape(w, block)
     _dev_tensor(x, torch.bfloat16, "x")
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x has shape %s, expected [m, %d]" % (tuple(x.shape), k))
     m = x.shape[0]
     y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=w.device)
     _dev_tensor(y, torch.float32, "out")
-    check(_lib.q4k_gemm(w.data_ptr(), x.data_ptr(), y.data_ptr(), m, n, k, _stream(w.device)))
+    check(fn(w.data_ptr(), x.data_ptr(), y.data_ptr(), m, n, k, _stream(w.device)))
     return y
 
 

@@ -161,6 +161,13 @@ int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream)
 int q5k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
 
+/* Prefill GEMM on Q5_K weights: as q4k_gemm (same x_bf16, y, m, n, k,
+ * tolerance and errors) with w a Q5_K matrix [n, k].  Each step's weight tile
+ * is dequantized to bf16 in LDS (the same rounding), with split K on small
+ * grids. */
+int q5k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m,
+             int64_t n, int64_t k, void* stream);
+
 /* Diagnostic dequantization of a Q5_K matrix: as q4k_dequantize_f32 / _bf16
  * (exact weight rounded once to fp32; bf16 = nearest even of that). */
 int q5k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k,

@@ -67,10 +67,14 @@ def lib():
         L.oracle_q5k_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
         L.oracle_q5k_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
                                            _f64p, _f64p]
+        L.oracle_q5k_gemm.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _f64p, _f64p]
+        L.oracle_q5k_gemm_cols.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _i64p, _i64,
+                                           _f64p, _f64p]
         for name in ("oracle_dequant_f32", "oracle_dequant_bf16", "oracle_gemv",
                      "oracle_gemv_rows", "oracle_gemm", "oracle_gemm_cols",
                      "oracle_swiglu_mlp", "oracle_q5k_dequant_f32", "oracle_q5k_dequant_bf16",
-                     "oracle_q5k_gemv", "oracle_q5k_gemv_rows"):
+                     "oracle_q5k_gemv", "oracle_q5k_gemv_rows", "oracle_q5k_gemm",
+                     "oracle_q5k_gemm_cols"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -268,4 +272,28 @@ def q5k_gemv_rows(w: np.ndarray, x: np.ndarray, n: int, k: int, rows):
     a = np.zeros((m, rows.size), np.float64)
     _check(lib().oracle_q5k_gemv_rows(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(rows, _i64p),
                                       rows.size, _p(y, _f64p), _p(a, _f64p)), "q5k_gemv_rows")
+    return y, a
+
+
+def q5k_gemm(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int):
+    """Y, A = oracle GEMM on Q5_K weights; x_bf16 uint16 [m, k]; fp64 [m, n]."""
+    w = _c(w, np.uint8)
+    x = _c(x_bf16, np.uint16).reshape(-1, k)
+    m = x.shape[0]
+    y = np.zeros((m, n), np.float64)
+    a = np.zeros((m, n), np.float64)
+    _check(lib().oracle_q5k_gemm(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(y, _f64p),
+                                 _p(a, _f64p)), "q5k_gemm")
+    return y, a
+
+
+def q5k_gemm_cols(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int, cols):
+    w = _c(w, np.uint8)
+    x = _c(x_bf16, np.uint16).reshape(-1, k)
+    cols = _c(cols, np.int64)
+    m = x.shape[0]
+    y = np.zeros((m, cols.size), np.float64)
+    a = np.zeros((m, cols.size), np.float64)
+    _check(lib().oracle_q5k_gemm_cols(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(cols, _i64p),
+                                      cols.size, _p(y, _f64p), _p(a, _f64p)), "q5k_gemm_cols")
     return y, a

@@ -46,6 +46,13 @@ int oracle_q5k_gemv_rows(const uint8_t *w, const float *x, int64_t m, int64_t n,
                          int64_t k, const int64_t *rows, int64_t nrows,
                          double *y, double *a);
 
+/* GEMM as oracle_gemm / oracle_gemm_cols (X bf16 bits [m, k]), on Q5_K weights. */
+int oracle_q5k_gemm(const uint8_t *w, const uint16_t *x, int64_t m, int64_t n,
+                    int64_t k, double *y, double *a);
+int oracle_q5k_gemm_cols(const uint8_t *w, const uint16_t *x, int64_t m, int64_t n,
+                         int64_t k, const int64_t *cols, int64_t ncols, double *y,
+                         double *a);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for name in ("q4k_gemv", "q4k_gemm", "q4k_swiglu_mlp", "q4k_init", "q4k_last_error",
                  "q4k_dequantize_f32", "q4k_dequantize_bf16", "q4k_device_name", "q4k_version",
-                 "q5k_gemv", "q5k_dequantize_f32", "q5k_dequantize_bf16"):
+                 "q5k_gemv", "q5k_gemm", "q5k_dequantize_f32", "q5k_dequantize_bf16"):
         assert name in syms
 
 
@@ -145,6 +145,10 @@ def test_q5k_rejects_bad_arguments():
     assert _lib.q5k_gemv(A + 8, 2 * A, 3 * A, 1, 16, 256, None) == _lib.Q4K_ERR_ALIGN
     # 16 rows of one 176-byte block span 2816 bytes from A: y may not start inside
     assert _lib.q5k_gemv(A, 2 * A, A + 2800, 1, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q5k_gemm(A, 2 * A, 3 * A, 8, 16, 300, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q5k_gemm(A, 2 * A + 2, 3 * A, 8, 16, 256, None) == _lib.Q4K_ERR_ALIGN
+    assert _lib.q5k_gemm(A, 2 * A, A + 2800, 8, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q4k_last_error().startswith("q5k_gemm")
     assert _lib.q5k_dequantize_f32(0, A, 4, 256, None) == _lib.Q4K_ERR_INVALID_ARG
     assert _lib.q5k_dequantize_bf16(A, 2 * A + 4, 4, 256, None) == _lib.Q4K_ERR_ALIGN
     assert _lib.q5k_dequantize_f32(A, A + 688, 4, 256, None) == _lib.Q4K_ERR_INVALID_ARG  # out in w

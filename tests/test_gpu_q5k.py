@@ -121,3 +121,47 @@ def test_q5k_gemv_unit_vectors_give_columns(q4k):
     y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
     for i, c in enumerate(cols):
         assert np.array_equal(y[i], W[:, c]), c
+
+
+GEMM_TOL = 1e-2
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+# Batches of at most 32 rows (one 32-row slice, split K) and larger ones
+# (128 x 128 tiles, split K when the grid is small): ragged M, N and K steps.
+@pytest.mark.parametrize("m,n,k", [(1, 256, 512), (8, 520, 1024), (32, 384, 256),
+                                   (100, 300, 512), (129, 256, 768)])
+def test_q5k_gemm_full_output(q4k, m, n, k):
+    w = synth.q5k_weights(n, k, seed=m + n)
+    xb = synth.normal_bf16((m, k), seed=m + n)
+    Y = q4k.q5k_gemm(dev(w), dev_bf16(xb)).cpu().numpy()
+    Yr, A = oracle.q5k_gemm(w, xb, n, k)
+    assert_within(Y, Yr, A, GEMM_TOL, "q5k gemm %dx%dx%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 4096, 4096), (16, 14336, 4096)])
+def test_q5k_gemm_sampled(q4k, m, n, k):
+    w = synth.q5k_weights(n, k, seed=1)
+    xb = synth.normal_bf16((m, k), seed=1)
+    Y = q4k.q5k_gemm(dev(w), dev_bf16(xb)).cpu().numpy()
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, n - 1],
+                                     np.random.default_rng(n).integers(0, n, 43)]))
+    Yr, A = oracle.q5k_gemm_cols(w, xb, n, k, cols)
+    assert_within(Y[:, cols], Yr, A, GEMM_TOL, "q5k gemm %dx%dx%d" % (m, n, k))
+    assert np.all(np.isfinite(Y))
+
+
+def test_q5k_gemm_m1_equals_bf16_weight_dot(q4k):
+    # With X exactly representable, the GEMM at m=1 is the dot of X with the
+    # bf16 weights the GPU exports (tighter than 1e-2).
+    n, k = 256, 2048
+    w = synth.q5k_weights(n, k, seed=30)
+    xb = synth.normal_bf16((1, k), seed=30)
+    Y = q4k.q5k_gemm(dev(w), dev_bf16(xb)).cpu().numpy().astype(np.float64)
+    Wb = oracle.q5k_dequant_bf16(w, n, k)
+    Wf = (Wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    Xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(Y - Xf @ Wf.T) <= 1e-5 * (np.abs(Xf) @ np.abs(Wf.T)))

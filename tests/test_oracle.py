@@ -411,3 +411,26 @@ def test_q5k_bad_shapes_rejected():
     out = np.zeros(512, np.float32)
     assert L.oracle_q5k_dequant_f32(oracle._p(w, oracle._u8p), 2, 300,
                                     oracle._p(out, oracle._f32p)) == -1
+
+
+def test_q5k_gemm_at_m1_with_bf16_exact_x_equals_gemv():
+    n, k = 20, 512
+    w = synth.q5k_weights(n, k, seed=21)
+    xb = synth.normal_bf16((1, k), seed=21)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    y, a = oracle.q5k_gemm(w, xb, n, k)
+    yv, av = oracle.q5k_gemv(w, xf, n, k)
+    assert np.array_equal(y, yv) and np.array_equal(a, av)
+
+
+def test_q5k_gemm_matches_library_matmul():
+    n, k, m = 24, 512, 5
+    w = synth.q5k_weights(n, k, seed=22)
+    xb = synth.normal_bf16((m, k), seed=22)
+    Xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    W = oracle.q5k_dequant_f32(w, n, k).astype(np.float64)
+    y, a = oracle.q5k_gemm(w, xb, n, k)
+    assert np.all(np.abs(y - Xf @ W.T) <= 1e-12 * a)
+    cols = np.array([3, 0, 23])
+    yc, ac = oracle.q5k_gemm_cols(w, xb, n, k, cols)
+    assert np.array_equal(yc, y[:, cols]) and np.array_equal(ac, a[:, cols])
