@@ -360,3 +360,36 @@ def test_read_probe_runs_and_leaves_sink(q4k, nbytes):
                                torch.cuda.current_stream().cuda_stream) == _lib.Q4K_OK
     torch.cuda.synchronize()
     assert sink.cpu().tolist() == [7, 7, 7, 7]
+
+
+# ------------------------------------------------------------------ K chunks
+
+# x is staged a chunk of K at a time (16384 elements at batch 1, 8192 at
+# batch 2, 4096 for larger batches); past one chunk each chunk's partial dot
+# is added into y.  Batch 1 below and above 8192 rows, batch 2 over two
+# chunks, a batch of 3 over two and a batch of 8 over three.
+@pytest.mark.parametrize("m,n,k", [(1, 300, 20480), (1, 9000, 16640), (2, 257, 9216),
+                                   (3, 130, 4352), (8, 64, 8448)])
+def test_gemv_multi_chunk_k(q4k, m, n, k):
+    w = synth.q4k_weights(n, k, seed=k + m)
+    x = synth.normal_f32((m, k), seed=k + m)
+    y = q4k.gemv(dev(w), dev(x)).cpu().numpy()
+    yr, a = oracle.gemv(w, x, n, k)
+    assert_within(y, yr, a, GEMV_TOL, "gemv m=%d %dx%d" % (m, n, k))
+
+
+def test_swiglu_mlp_d_model_past_one_chunk(q4k):
+    # d_model > 16384: the gate/up pair keeps one row set per wave so its two
+    # dots stay in registers across x chunks until silu.
+    dm, dff = 16640, 512
+    _mlp_check(q4k, dm, dff, 7)
+
+
+def test_gemm_long_k(q4k):
+    m, n, k = 64, 512, 16384
+    w = synth.q4k_weights(n, k, seed=3)
+    xb = synth.normal_bf16((m, k), seed=3)
+    Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
+    cols = np.arange(0, n, 7)
+    Yr, A = oracle.gemm_cols(w, xb, n, k, cols)
+    assert_within(Y[:, cols], Yr, A, GEMM_TOL, "gemm 64x512x16384")

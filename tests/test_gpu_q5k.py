@@ -165,3 +165,12 @@ def test_q5k_gemm_m1_equals_bf16_weight_dot(q4k):
     Wf = (Wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     Xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.all(np.abs(Y - Xf @ Wf.T) <= 1e-5 * (np.abs(Xf) @ np.abs(Wf.T)))
+
+
+def test_q5k_gemv_multi_chunk_k(q4k):
+    n, k = 300, 20480
+    w = synth.q5k_weights(n, k, seed=6)
+    x = synth.normal_f32(k, seed=6)
+    y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
+    yr, a = oracle.q5k_gemv(w, x, n, k)
+    assert_within(y, yr[0], a[0], GEMV_TOL, "q5k gemv 300x20480")
