@@ -1,11 +1,13 @@
 // k_dequant.hip -- diagnostic export of a Q4_K matrix as fp32 or bf16, and a
 // streaming read probe.
 //
-// The export runs the same device routines as the GEMV (group_scales,
-// dequant_dword) and the GEMM kernels (dequant8_bf16, through
-// dequant16_bf16), so the bit-exact check of this export ("CPU kernel parity
-// ..." PR page, "Validation": every variant bit-exact against the reference
-// decode) covers what the other kernels compute.
+// The export shares its device routines with the other kernels: the scale
+// decode (group_scales) and the fp8 nibble widening with the GEMV, and the
+// bf16 operand routine (dequant8_bf16, through dequant16_bf16) with the GEMM
+// kernels, so the bit-exact check of this export ("CPU kernel parity ..." PR
+// page, "Validation": every variant bit-exact against the reference decode)
+// covers the decode they compute.  (The GEMV applies the scales per
+// sub-block to its dot product instead of dequantizing each weight.)
 //
 // One thread per 16 quant bytes: (row, block, group g, half hh).  It writes
 // the 16 low-nibble weights 64g+16hh.. and the 16 high-nibble weights
