@@ -372,15 +372,24 @@ def main():
     print(json.dumps(out))
 
 
-KERNEL_SOURCES = ("k_gemv.hip", "k_gemm.hip", "k_dequant.hip", "q4k_device.h")
+KERNEL_SOURCES = ("k_gemv.hip", "k_gemm.hip", "k_dequant.hip", "q4k_device.h", "q4k_launch.h")
+
+
+def _code_only(text):
+    """C++ source without comments and with whitespace runs collapsed: what the compiler
+    sees, so that a comment edit does not mark the measured kernels as changed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "gemm_q4_super_block_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "gemm_q4_super_block_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
