@@ -1,10 +1,10 @@
-"""ctypes view of the plain C oracle (``q4k_oracle.c``).
+"""ctypes view of the plain C oracle (``q4k_oracle.c``, ``q5k_oracle.c``, ``w8a8_oracle.c``).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product path
 (``gemm_q4_super_block_amd``) never imports it and has no CPU fallback.
 
-All arrays are numpy; results are fp64.  See ``q4k_oracle.h`` for what each
+All arrays are numpy; results are fp64 (bf16 bits and int32 for the INT8 layer).  See the headers for what each
 function computes and which page passage it follows.
 """
 from __future__ import annotations
@@ -70,11 +70,23 @@ def lib():
         L.oracle_q5k_gemm.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _f64p, _f64p]
         L.oracle_q5k_gemm_cols.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _i64p, _i64,
                                            _f64p, _f64p]
+        _i8p = ctypes.POINTER(ctypes.c_int8)
+        _i32p = ctypes.POINTER(ctypes.c_int32)
+        L.oracle_w8a8_acc.argtypes = [_i8p, _i8p, _i64, _i64, _i64, _i32p]
+        L.oracle_w8a8_epilogue.argtypes = [_i32p, _f32p, _f32p, _f32p, _i64, _i64, _u16p,
+                                           _f32p]
+        L.oracle_w8a8_linear.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _i64, _i64, _i64,
+                                         _u16p]
+        L.oracle_w8a8_linear_cols.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _i64, _i64,
+                                              _i64, _i64p, _i64, _u16p]
+        L.oracle_w8a8_quantize_rows.argtypes = [_u16p, _i64, _i64, _i8p, _f32p]
         for name in ("oracle_dequant_f32", "oracle_dequant_bf16", "oracle_gemv",
                      "oracle_gemv_rows", "oracle_gemm", "oracle_gemm_cols",
                      "oracle_swiglu_mlp", "oracle_q5k_dequant_f32", "oracle_q5k_dequant_bf16",
                      "oracle_q5k_gemv", "oracle_q5k_gemv_rows", "oracle_q5k_gemm",
-                     "oracle_q5k_gemm_cols"):
+                     "oracle_q5k_gemm_cols", "oracle_w8a8_acc", "oracle_w8a8_epilogue",
+                     "oracle_w8a8_linear", "oracle_w8a8_linear_cols",
+                     "oracle_w8a8_quantize_rows"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -297,3 +309,80 @@ def q5k_gemm_cols(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int, cols):
     _check(lib().oracle_q5k_gemm_cols(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(cols, _i64p),
                                       cols.size, _p(y, _f64p), _p(a, _f64p)), "q5k_gemm_cols")
     return y, a
+
+
+# ---- INT8 W8A8 linear (w8a8_oracle.h) --------------------------------------
+
+_i8p = ctypes.POINTER(ctypes.c_int8)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def w8a8_acc(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """int32 [m, n] = x int8 [m, k] . w int8 [n, k]^T, exact."""
+    x = _c(x, np.int8)
+    w = _c(w, np.int8)
+    m, k = x.shape
+    n = w.shape[0]
+    acc = np.zeros((m, n), np.int32)
+    _check(lib().oracle_w8a8_acc(_p(x, _i8p), _p(w, _i8p), m, n, k, _p(acc, _i32p)), "w8a8_acc")
+    return acc
+
+
+def w8a8_epilogue(acc, x_scale, w_scale, bias=None):
+    """bf16 bits [m, n] and the fp32 value before rounding, for given accumulators."""
+    acc = _c(acc, np.int32)
+    m, n = acc.shape
+    xs = _c(x_scale, np.float32)
+    ws = _c(w_scale, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.zeros((m, n), np.uint16)
+    f = np.zeros((m, n), np.float32)
+    _check(lib().oracle_w8a8_epilogue(_p(acc, _i32p), _p(xs, _f32p), _p(ws, _f32p),
+                                      None if b is None else _p(b, _f32p), m, n,
+                                      _p(out, _u16p), _p(f, _f32p)), "w8a8_epilogue")
+    return out, f
+
+
+def w8a8_linear(x, x_scale, w, w_scale, bias=None) -> np.ndarray:
+    """bf16 bits [m, n] of the W8A8 linear layer (acc then the epilogue)."""
+    x = _c(x, np.int8)
+    w = _c(w, np.int8)
+    m, k = x.shape
+    n = w.shape[0]
+    xs = _c(x_scale, np.float32)
+    ws = _c(w_scale, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.zeros((m, n), np.uint16)
+    _check(lib().oracle_w8a8_linear(_p(x, _i8p), _p(xs, _f32p), _p(w, _i8p), _p(ws, _f32p),
+                                    None if b is None else _p(b, _f32p), m, n, k,
+                                    _p(out, _u16p)), "w8a8_linear")
+    return out
+
+
+def w8a8_linear_cols(x, x_scale, w, w_scale, bias, cols) -> np.ndarray:
+    """bf16 bits [m, len(cols)]: the W8A8 linear layer at the given output columns."""
+    x = _c(x, np.int8)
+    w = _c(w, np.int8)
+    m, k = x.shape
+    n = w.shape[0]
+    xs = _c(x_scale, np.float32)
+    ws = _c(w_scale, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    cols = _c(cols, np.int64)
+    out = np.zeros((m, len(cols)), np.uint16)
+    _check(lib().oracle_w8a8_linear_cols(_p(x, _i8p), _p(xs, _f32p), _p(w, _i8p),
+                                         _p(ws, _f32p), None if b is None else _p(b, _f32p),
+                                         m, n, k, _p(cols, _i64p), len(cols), _p(out, _u16p)),
+           "w8a8_linear_cols")
+    return out
+
+
+def w8a8_quantize_rows(x_bf16_bits):
+    """Row quantizer: bf16 bits [rows, k] -> (int8 codes [rows, k], fp32 scales [rows])."""
+    x = _c(x_bf16_bits, np.uint16)
+    rows, k = x.shape
+    q = np.zeros((rows, k), np.int8)
+    s = np.zeros(rows, np.float32)
+    _check(lib().oracle_w8a8_quantize_rows(_p(x, _u16p), rows, k, _p(q, _i8p), _p(s, _f32p)),
+           "w8a8_quantize_rows")
+    return q, s

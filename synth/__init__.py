@@ -24,6 +24,14 @@ d and dmin = |N(0,1)| * 0.01, activations N(0,1)):
 A Q5_K super-block (176 bytes) is drawn the same way: fp16 ``d`` and ``dmin`` at
 bytes 0 and 2, the other 172 bytes uniform.
 
+INT8 W8A8 inputs (the INT8 linear layer of the xpu-kernels page): int8 codes
+are a normal draw with standard deviation 32, rounded and clipped to
+[-127, 127] (the spread of per-row absmax codes of Gaussian rows at k in the
+thousands); activation row scales are uniform in [0.01, 0.05], weight row
+scales uniform in [2e-4, 1e-3] (absmax / 127 of N(0,1) activations and of
+N(0, 0.02) weights) and the bias is N(0, 0.1), all fp32.  ``int8_uniform``
+draws codes uniformly from the whole int8 range, -128 included, for extremes.
+
 Random streams come from numpy's PCG64 seeded with ``SeedSequence([seed,
 stream])``, so every tensor of a case has its own independent stream and a
 case is reproducible from ``seed`` alone.
@@ -38,6 +46,7 @@ Q5K_BLOCK_BYTES = 176  # bytes per Q5_K super-block (Q4_K plus 32 high-bit bytes
 
 # stream ids: one per tensor role, so cases never share draws
 W, X, W_GATE, W_UP, W_DOWN = 0, 1, 2, 3, 4
+X_SCALE, W_SCALE, BIAS = 5, 6, 7
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -93,3 +102,29 @@ def bf16_bits(x_f32: np.ndarray) -> np.ndarray:
 def normal_bf16(shape, seed: int = 0, stream: int = X) -> np.ndarray:
     """bf16 bits of fp32 N(0,1) draws."""
     return bf16_bits(normal_f32(shape, seed, stream))
+
+
+def int8_codes(shape, seed: int = 0, stream: int = X, std: float = 32.0) -> np.ndarray:
+    """int8 codes: rint(N(0, std)) clipped to [-127, 127]."""
+    v = np.rint(rng(seed, stream).standard_normal(shape) * std)
+    return np.clip(v, -127, 127).astype(np.int8)
+
+
+def int8_uniform(shape, seed: int = 0, stream: int = X) -> np.ndarray:
+    """int8 codes uniform over -128..127."""
+    return rng(seed, stream).integers(-128, 128, size=shape, dtype=np.int8)
+
+
+def uniform_f32(shape, lo: float, hi: float, seed: int = 0, stream: int = X_SCALE) -> np.ndarray:
+    """fp32 uniform in [lo, hi)."""
+    return rng(seed, stream).uniform(lo, hi, size=shape).astype(np.float32)
+
+
+def w8a8_case(m: int, n: int, k: int, seed: int = 0):
+    """(x int8 [m,k], x_scale [m], w int8 [n,k], w_scale [n], bias [n]) of one seeded case."""
+    x = int8_codes((m, k), seed, X)
+    w = int8_codes((n, k), seed, W)
+    xs = uniform_f32((m,), 0.01, 0.05, seed, X_SCALE)
+    ws = uniform_f32((n,), 2e-4, 1e-3, seed, W_SCALE)
+    bias = (rng(seed, BIAS).standard_normal(n) * 0.1).astype(np.float32)
+    return x, xs, w, ws, bias
