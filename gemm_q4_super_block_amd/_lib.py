@@ -1,4 +1,4 @@
-"""ctypes loader for libq4k.so -- the C ABI declared in include/q4k.h.
+"""ctypes loader for libq4k.so -- the C ABI declared in include/q4k.h and include/w8a8.h.
 
 The library is looked up in ``$LIBQ4K_PATH`` (a file path), then next to this
 file.  If it cannot be loaded, every call raises ``Q4KLibraryError``: there is
@@ -22,6 +22,8 @@ Q4K_QK = 256
 Q4K_BLOCK_BYTES = 144
 Q4K_GEMV_MAX_M = 32
 Q5K_BLOCK_BYTES = 176
+W8A8_K_STEP = 128
+W8A8_MAX_K = 130944
 
 # Every symbol the header declares, with (restype, argtypes).
 _vp = ctypes.c_void_p
@@ -41,6 +43,10 @@ SIGNATURES = {
     "q5k_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q5k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q5k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "w8a8_linear": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "w8a8_linear_acc": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "w8a8_dequant_epilogue": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp]),
+    "w8a8_quantize_rows": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
 }
 
 
@@ -145,3 +151,19 @@ def q5k_dequantize_bf16(w, out, n, k, stream) -> int:
 
 def q5k_gemm(w, x_bf16, y, m, n, k, stream) -> int:
     return load().q5k_gemm(w, x_bf16, y, m, n, k, stream)
+
+
+def w8a8_linear(x, x_scale, w, w_scale, bias, out, m, n, k, stream) -> int:
+    return load().w8a8_linear(x, x_scale, w, w_scale, bias, out, m, n, k, stream)
+
+
+def w8a8_linear_acc(x, w, acc, m, n, k, stream) -> int:
+    return load().w8a8_linear_acc(x, w, acc, m, n, k, stream)
+
+
+def w8a8_dequant_epilogue(acc, out, x_scale, w_scale, bias, m, n, stream) -> int:
+    return load().w8a8_dequant_epilogue(acc, out, x_scale, w_scale, bias, m, n, stream)
+
+
+def w8a8_quantize_rows(x_bf16, q, scale, rows, k, stream) -> int:
+    return load().w8a8_quantize_rows(x_bf16, q, scale, rows, k, stream)

@@ -28,6 +28,7 @@
 //     zeroed Y (used when the output tile count cannot fill 256 CUs).
 #include <hip/hip_runtime.h>
 
+#include "lds_copy.h"
 #include "q4k_device.h"
 #include "q4k_launch.h"
 
@@ -267,56 +268,9 @@ constexpr int kWLds = kWXSlots * kWXSlot + 2 * kWWSlot;  // 155648 bytes
 static_assert(kWLds <= 160 * 1024, "LDS budget of one workgroup");
 static_assert(2 * 2 * 32768 <= kWLds, "the K-half exchange reuses the rings");
 
-__device__ __forceinline__ int swz(int r) { return ((r & 15) >> 1) ^ ((r & 1) << 2); }
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
-}
-
-// One 16-byte-per-lane global -> LDS copy: lane i's 16 bytes go to
-// lds_uniform + 16 i.  M0 is saved and restored around the copy.
-__device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds_uniform) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds_uniform)
-      : "memory");
-}
-
-// Wait until at most N copies of this wave are in flight, then barrier.
-template <int N>
-__device__ __forceinline__ void wait_copies_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
 struct XFrag {
   bf16x8_t a[2][4];  // [slice u][M block i]
 };
-
-// Output tile of workgroup `bid`.  Workgroups are dealt to the eight XCDs in
-// turn (XCD = bid mod 8), each with its own L2.  With xcd_gm = 0 the tiles run
-// M-fastest.  Otherwise the tile grid is cut into gm x (8 / gm) blocks, one per
-// XCD, so that an XCD's workgroups share their X rows and weight columns in its
-// L2 instead of every XCD fetching all of W (needs tiles_m % gm == 0 and
-// tiles_n % (8 / gm) == 0; the host picks gm).
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int xcd_gm,
-                                            int& tm, int& tn) {
-  if (xcd_gm) {
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int a = tiles_m / xcd_gm;  // M-tiles per XCD block
-    tm = (xcd % xcd_gm) * a + slot % a;
-    tn = (xcd / xcd_gm) * (tiles_n / (8 / xcd_gm)) + slot / a;
-  } else {
-    tm = bid % tiles_m;
-    tn = bid / tiles_m;
-  }
-}
 
 __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __restrict__ w,
                                                              const uint16_t* __restrict__ x,
@@ -849,18 +803,7 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
 // XCD's workgroups stream per K element (2 per X row, 9/16 per weight row),
 // or 0 if none divides it.
 int xcd_groups(int tiles_m, int tiles_n, int bm, int bn) {
-  int best = 0;
-  long best_cost = 0;
-  for (int gm = 1; gm <= 8; gm *= 2) {
-    const int gn = 8 / gm;
-    if (tiles_m % gm != 0 || tiles_n % gn != 0) continue;
-    const long cost = 32L * (tiles_m / gm) * bm + 9L * (tiles_n / gn) * bn;
-    if (best == 0 || cost < best_cost) {
-      best = gm;
-      best_cost = cost;
-    }
-  }
-  return best;
+  return xcd_blocking(tiles_m, tiles_n, 32L * bm, 9L * bn);
 }
 
 // Split K until the grid reaches one workgroup per CU (256 on MI355X).

@@ -15,6 +15,7 @@
 #include <string>
 
 #include "../../include/q4k.h"
+#include "../../include/w8a8.h"
 #include "q4k_launch.h"
 
 namespace {
@@ -269,6 +270,105 @@ int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream)
   if (int rc = check_device()) return rc;
   return launched(q4k::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)),
                   "q4k_read_probe");
+}
+
+// ---------------------------------------------------------------- INT8 W8A8
+
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Shared by the two GEMM entry points: sizes, alignment of x and w, and the
+// output range [out, out + out_bytes) against the inputs.
+static int w8a8_gemm_checks(const char* what, const int8_t* x, const int8_t* w, const void* out,
+                            size_t out_elem, int64_t m, int64_t n, int64_t k) {
+  if (!x || !w || !out) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
+  if (m < 1 || m > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: m=%lld", what, (long long)m);
+  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
+  if (k < W8A8_K_STEP || k % W8A8_K_STEP != 0 || k > W8A8_MAX_K)
+    return fail(Q4K_ERR_INVALID_ARG, "%s: k=%lld is not a multiple of %d in %d..%d", what,
+                (long long)k, W8A8_K_STEP, W8A8_K_STEP, W8A8_MAX_K);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out))
+    return fail(Q4K_ERR_ALIGN, "%s: x, w and the output must be 16-byte aligned", what);
+  const size_t no = static_cast<size_t>(m) * static_cast<size_t>(n) * out_elem;
+  if (overlap(out, no, x, static_cast<size_t>(m) * static_cast<size_t>(k)) ||
+      overlap(out, no, w, static_cast<size_t>(n) * static_cast<size_t>(k)))
+    return fail(Q4K_ERR_INVALID_ARG, "%s: the output overlaps x or w", what);
+  return Q4K_OK;
+}
+
+// Scales and bias of an epilogue writing `out` (bf16 [m, n]).
+static int w8a8_vector_checks(const char* what, const float* x_scale, const float* w_scale,
+                              const float* bias, const void* out, int64_t m, int64_t n) {
+  if (!x_scale || !w_scale) return fail(Q4K_ERR_INVALID_ARG, "%s: null scale pointer", what);
+  if (!aligned4(x_scale) || !aligned4(w_scale) || (bias && !aligned4(bias)))
+    return fail(Q4K_ERR_ALIGN, "%s: x_scale, w_scale and bias must be 4-byte aligned", what);
+  const size_t no = static_cast<size_t>(m) * static_cast<size_t>(n) * 2;
+  if (overlap(out, no, x_scale, static_cast<size_t>(m) * 4) ||
+      overlap(out, no, w_scale, static_cast<size_t>(n) * 4) ||
+      (bias && overlap(out, no, bias, static_cast<size_t>(n) * 4)))
+    return fail(Q4K_ERR_INVALID_ARG, "%s: out overlaps a scale or the bias", what);
+  return Q4K_OK;
+}
+
+int w8a8_linear(const int8_t* x, const float* x_scale, const int8_t* w, const float* w_scale,
+                const float* bias, uint16_t* out, int64_t m, int64_t n, int64_t k,
+                void* stream) {
+  const char* what = "w8a8_linear";
+  if (int rc = w8a8_gemm_checks(what, x, w, out, 2, m, n, k)) return rc;
+  if (int rc = w8a8_vector_checks(what, x_scale, w_scale, bias, out, m, n)) return rc;
+  if (int rc = check_device()) return rc;
+  return launched(q4k::launch_w8a8_linear(x, x_scale, w, w_scale, bias, out, m, n, k,
+                                          static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+int w8a8_linear_acc(const int8_t* x, const int8_t* w, int32_t* acc, int64_t m, int64_t n,
+                    int64_t k, void* stream) {
+  const char* what = "w8a8_linear_acc";
+  if (int rc = w8a8_gemm_checks(what, x, w, acc, 4, m, n, k)) return rc;
+  if (int rc = check_device()) return rc;
+  return launched(q4k::launch_w8a8_linear_acc(x, w, acc, m, n, k,
+                                              static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+int w8a8_dequant_epilogue(const int32_t* acc, uint16_t* out, const float* x_scale,
+                          const float* w_scale, const float* bias, int64_t m, int64_t n,
+                          void* stream) {
+  const char* what = "w8a8_dequant_epilogue";
+  if (!acc || !out) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
+  if (m < 1 || m > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: m=%lld", what, (long long)m);
+  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
+  if (!aligned16(acc) || !aligned16(out))
+    return fail(Q4K_ERR_ALIGN, "%s: acc and out must be 16-byte aligned", what);
+  if (overlap(out, static_cast<size_t>(m) * static_cast<size_t>(n) * 2, acc,
+              static_cast<size_t>(m) * static_cast<size_t>(n) * 4))
+    return fail(Q4K_ERR_INVALID_ARG, "%s: out overlaps acc", what);
+  if (int rc = w8a8_vector_checks(what, x_scale, w_scale, bias, out, m, n)) return rc;
+  if (int rc = check_device()) return rc;
+  return launched(q4k::launch_w8a8_epilogue(acc, out, x_scale, w_scale, bias, m, n,
+                                            static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+int w8a8_quantize_rows(const uint16_t* x_bf16, int8_t* q, float* scale, int64_t rows, int64_t k,
+                       void* stream) {
+  const char* what = "w8a8_quantize_rows";
+  if (!x_bf16 || !q || !scale) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
+  if (rows < 1 || rows > INT32_MAX)
+    return fail(Q4K_ERR_INVALID_ARG, "%s: rows=%lld", what, (long long)rows);
+  if (k < 8 || k % 8 != 0 || k > INT32_MAX)
+    return fail(Q4K_ERR_INVALID_ARG, "%s: k=%lld is not a positive multiple of 8", what,
+                (long long)k);
+  if (!aligned16(x_bf16) || !aligned16(q) || !aligned4(scale))
+    return fail(Q4K_ERR_ALIGN, "%s: x and q must be 16-byte and scale 4-byte aligned", what);
+  const size_t nx = static_cast<size_t>(rows) * static_cast<size_t>(k);
+  if (overlap(q, nx, x_bf16, nx * 2) || overlap(scale, static_cast<size_t>(rows) * 4, x_bf16, nx * 2) ||
+      overlap(scale, static_cast<size_t>(rows) * 4, q, nx))
+    return fail(Q4K_ERR_INVALID_ARG, "%s: outputs overlap", what);
+  if (int rc = check_device()) return rc;
+  return launched(q4k::launch_w8a8_quantize_rows(x_bf16, q, scale, rows, k,
+                                                 static_cast<hipStream_t>(stream)),
+                  what);
 }
 
 }  // extern "C"

@@ -49,6 +49,18 @@ hipError_t launch_q5k_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, i
 hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);
 
+// INT8 W8A8 linear layer (k % 128 == 0, pointers 16-byte aligned).
+hipError_t launch_w8a8_linear(const int8_t* x, const float* x_scale, const int8_t* w,
+                              const float* w_scale, const float* bias, uint16_t* out, int64_t m,
+                              int64_t n, int64_t k, hipStream_t stream);
+hipError_t launch_w8a8_linear_acc(const int8_t* x, const int8_t* w, int32_t* acc, int64_t m,
+                                  int64_t n, int64_t k, hipStream_t stream);
+hipError_t launch_w8a8_epilogue(const int32_t* acc, uint16_t* out, const float* x_scale,
+                                const float* w_scale, const float* bias, int64_t m, int64_t n,
+                                hipStream_t stream);
+hipError_t launch_w8a8_quantize_rows(const uint16_t* x, int8_t* q, float* scale, int64_t rows,
+                                     int64_t k, hipStream_t stream);
+
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                              hipStream_t stream);
 

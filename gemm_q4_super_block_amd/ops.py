@@ -3,7 +3,8 @@
 PyTorch provides device memory and the current stream; every computation runs
 in libq4k's HIP kernels.  Weights are ``torch.uint8`` tensors holding raw Q4_K
 super-blocks, shape ``[n, (k // 256) * 144]`` (Q5_K: 176-byte blocks,
-``[n, (k // 256) * 176]``, for the ``q5k_`` functions).
+``[n, (k // 256) * 176]``, for the ``q5k_`` functions).  The INT8 W8A8 layer
+(``w8a8_*``) takes int8 codes with fp32 per-row scales and returns bf16.
 """
 from __future__ import annotations
 
@@ -131,3 +132,81 @@ def q5k_dequantize_bf16(w: torch.Tensor) -> torch.Tensor:
     out = torch.empty((n, k), dtype=torch.bfloat16, device=w.device)
     check(_lib.q5k_dequantize_bf16(w.data_ptr(), out.data_ptr(), n, k, _stream(w.device)))
     return out
+
+
+# ---------------------------------------------------------------- INT8 W8A8
+
+def _vec(t, n, what):
+    _dev_tensor(t, torch.float32, what)
+    if t.dim() != 1 or t.shape[0] != n:
+        raise ValueError("%s has shape %s, expected [%d]" % (what, tuple(t.shape), n))
+    return t.data_ptr()
+
+
+def _w8_operands(x, w):
+    _dev_tensor(x, torch.int8, "x")
+    _dev_tensor(w, torch.int8, "w")
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x [m, k] and w [n, k] expected, got %s and %s"
+                         % (tuple(x.shape), tuple(w.shape)))
+    return x.shape[0], w.shape[0], x.shape[1]
+
+
+def w8a8_linear(x: torch.Tensor, x_scale: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor,
+                bias: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [m, n] = (x w^T) * x_scale[:, None] * w_scale[None, :] + bias, int8 x and w."""
+    m, n, k = _w8_operands(x, w)
+    xs = _vec(x_scale, m, "x_scale")
+    ws = _vec(w_scale, n, "w_scale")
+    b = None if bias is None else _vec(bias, n, "bias")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _dev_tensor(y, torch.bfloat16, "out")
+    check(_lib.w8a8_linear(x.data_ptr(), xs, w.data_ptr(), ws, b, y.data_ptr(), m, n, k,
+                           _stream(x.device)))
+    return y
+
+
+def w8a8_linear_acc(x: torch.Tensor, w: torch.Tensor,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """int32 [m, n] = x w^T, exact, for int8 x [m, k] and w [n, k]."""
+    m, n, k = _w8_operands(x, w)
+    acc = out if out is not None else torch.empty((m, n), dtype=torch.int32, device=x.device)
+    _dev_tensor(acc, torch.int32, "out")
+    check(_lib.w8a8_linear_acc(x.data_ptr(), w.data_ptr(), acc.data_ptr(), m, n, k,
+                               _stream(x.device)))
+    return acc
+
+
+def w8a8_dequant(acc: torch.Tensor, x_scale: torch.Tensor, w_scale: torch.Tensor,
+                 bias: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The dequant epilogue alone: int32 [m, n] -> bf16 [m, n]."""
+    _dev_tensor(acc, torch.int32, "acc")
+    if acc.dim() != 2:
+        raise ValueError("acc must be [m, n]")
+    m, n = acc.shape
+    xs = _vec(x_scale, m, "x_scale")
+    ws = _vec(w_scale, n, "w_scale")
+    b = None if bias is None else _vec(bias, n, "bias")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=acc.device)
+    _dev_tensor(y, torch.bfloat16, "out")
+    check(_lib.w8a8_dequant_epilogue(acc.data_ptr(), y.data_ptr(), xs, ws, b, m, n,
+                                     _stream(acc.device)))
+    return y
+
+
+def w8a8_quantize_rows(x: torch.Tensor):
+    """Per-row int8 quantization of bf16 [rows, k]: (int8 codes [rows, k], fp32 scales [rows])."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, k]")
+    rows, k = x.shape
+    q = torch.empty((rows, k), dtype=torch.int8, device=x.device)
+    s = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    check(_lib.w8a8_quantize_rows(x.data_ptr(), q.data_ptr(), s.data_ptr(), rows, k,
+                                  _stream(x.device)))
+    return q, s
+
+
+def prepare_weight(w: torch.Tensor):
+    """bf16 weight [n, k] -> (int8 [n, k], fp32 per-row scale [n]), once per weight."""
+    return w8a8_quantize_rows(w)

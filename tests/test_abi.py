@@ -17,18 +17,22 @@ from gemm_q4_super_block_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "q4k.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_symbols():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(q[45]k_\w+)\(", text, re.M)))
+    text = "\n".join(open(h).read() for h in HEADERS)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?((?:q[45]k|w8a8)_\w+)\(",
+                                 text, re.M)))
 
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for name in ("q4k_gemv", "q4k_gemm", "q4k_swiglu_mlp", "q4k_init", "q4k_last_error",
                  "q4k_dequantize_f32", "q4k_dequantize_bf16", "q4k_device_name", "q4k_version",
-                 "q5k_gemv", "q5k_gemm", "q5k_dequantize_f32", "q5k_dequantize_bf16"):
+                 "q5k_gemv", "q5k_gemm", "q5k_dequantize_f32", "q5k_dequantize_bf16",
+                 "w8a8_linear", "w8a8_linear_acc", "w8a8_dequant_epilogue", "w8a8_quantize_rows"):
         assert name in syms
 
 
@@ -41,10 +45,10 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_header_constants_match_binding():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     for name in ("Q4K_OK", "Q4K_ERR_INVALID_ARG", "Q4K_ERR_ALIGN", "Q4K_ERR_DEVICE",
                  "Q4K_ERR_LAUNCH", "Q4K_QK", "Q4K_BLOCK_BYTES", "Q4K_GEMV_MAX_M",
-                 "Q5K_BLOCK_BYTES"):
+                 "Q5K_BLOCK_BYTES", "W8A8_K_STEP", "W8A8_MAX_K"):
         mm = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
         assert mm, name
         assert int(mm.group(1)) == getattr(_lib, name), name
@@ -153,3 +157,55 @@ def test_q5k_rejects_bad_arguments():
     assert _lib.q5k_dequantize_bf16(A, 2 * A + 4, 4, 256, None) == _lib.Q4K_ERR_ALIGN
     assert _lib.q5k_dequantize_f32(A, A + 688, 4, 256, None) == _lib.Q4K_ERR_INVALID_ARG  # out in w
     assert _lib.q4k_last_error().startswith("q5k_dequantize_f32")
+
+
+def test_w8a8_max_k_keeps_every_sum_in_int32():
+    assert _lib.W8A8_MAX_K % _lib.W8A8_K_STEP == 0
+    assert 128 * 128 * _lib.W8A8_MAX_K <= 2 ** 31 - 1
+    assert 128 * 128 * (_lib.W8A8_MAX_K + _lib.W8A8_K_STEP) > 2 ** 31 - 1
+
+
+def test_w8a8_rejects_bad_arguments():
+    lin = _lib.w8a8_linear
+    X, XS, W, WS, B, O = A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A
+    E = _lib.Q4K_ERR_INVALID_ARG
+    assert lin(0, XS, W, WS, B, O, 4, 8, 128, None) == E                  # null x
+    assert _lib.q4k_last_error().startswith("w8a8_linear")
+    assert lin(X, 0, W, WS, B, O, 4, 8, 128, None) == E                   # null x_scale
+    assert lin(X, XS, W, WS, B, 0, 4, 8, 128, None) == E                  # null out
+    assert lin(X, XS, W, WS, B, O, 0, 8, 128, None) == E                  # m = 0
+    assert lin(X, XS, W, WS, B, O, 4, 0, 128, None) == E                  # n = 0
+    assert lin(X, XS, W, WS, B, O, 4, 8, 64, None) == E                   # k % 128
+    assert lin(X, XS, W, WS, B, O, 4, 8, 0, None) == E                    # k = 0
+    assert lin(X, XS, W, WS, B, O, 4, 8, _lib.W8A8_MAX_K + 128, None) == E  # sums overflow
+    assert lin(X + 8, XS, W, WS, B, O, 4, 8, 128, None) == _lib.Q4K_ERR_ALIGN
+    assert lin(X, XS, W, WS, B, O + 2, 4, 8, 128, None) == _lib.Q4K_ERR_ALIGN
+    assert lin(X, XS + 2, W, WS, B, O, 4, 8, 128, None) == _lib.Q4K_ERR_ALIGN
+    assert lin(X, XS, W, WS, B, X + 256, 4, 8, 128, None) == E            # out inside x
+    assert lin(X, XS, W, WS, O + 32, O, 4, 8, 128, None) == E             # bias inside out
+    acc = _lib.w8a8_linear_acc
+    assert acc(X, W, 0, 4, 8, 128, None) == E
+    assert acc(X, W, O, 4, 8, 100, None) == E
+    assert acc(X, W + 4, O, 4, 8, 128, None) == _lib.Q4K_ERR_ALIGN
+    assert acc(X, W, W + 16, 4, 8, 128, None) == E                        # acc inside w
+    assert _lib.q4k_last_error().startswith("w8a8_linear_acc")
+    epi = _lib.w8a8_dequant_epilogue
+    assert epi(0, O, XS, WS, B, 4, 8, None) == E
+    assert epi(X, O, 0, WS, B, 4, 8, None) == E
+    assert epi(X, O, XS, WS, B, 0, 8, None) == E
+    assert epi(X + 4, O, XS, WS, B, 4, 8, None) == _lib.Q4K_ERR_ALIGN
+    assert epi(X, X + 64, XS, WS, B, 4, 8, None) == E                     # out inside acc
+    assert _lib.q4k_last_error().startswith("w8a8_dequant_epilogue")
+    qr = _lib.w8a8_quantize_rows
+    assert qr(0, O, XS, 4, 128, None) == E
+    assert qr(X, O, XS, 4, 12, None) == E                                 # k % 8
+    assert qr(X, O, XS, 0, 128, None) == E
+    assert qr(X, O + 8, XS, 4, 128, None) == _lib.Q4K_ERR_ALIGN
+    assert qr(X, X + 512, XS, 4, 128, None) == E                          # q inside x
+    assert _lib.q4k_last_error().startswith("w8a8_quantize_rows")
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
+def test_w8a8_valid_arguments_stop_at_the_device_check():
+    assert _lib.w8a8_linear(A, 2 * A, 3 * A, 4 * A, 0, 6 * A, 4, 8, 128, None) == _lib.Q4K_ERR_DEVICE
+    assert _lib.w8a8_quantize_rows(A, 2 * A, 3 * A, 4, 128, None) == _lib.Q4K_ERR_DEVICE
