@@ -6,7 +6,10 @@ inputs, each kernel on cold weights:
   * small-batch GEMV and GEMM, W 14336 x 4096, M in {1, 2, 4, 8, 16, 32};
   * SwiGLU MLP at one token: gate/up 14336 x 4096, down 4096 x 14336;
   * prefill GEMM, X bf16 [512, 4096], W 4096 x 4096 and 14336 x 4096;
-  * the bf16 dequantization export of the 4096 x 4096 matrix.
+  * the bf16 dequantization export of the 4096 x 4096 matrix;
+  * the INT8 W8A8 linear layer at the xpu-kernels page's shape, K = N = 3072,
+    M = 1024 (its headline row) and 8192: the row quantizer of the bf16
+    activations and the int8 MFMA GEMM with the fused dequant epilogue.
 Every kernel rotates over copies of its working set totalling >= 576 MB (past
 the 256 MB MALL and the 4 MB L2 per XCD), so each launch reads cold HBM.
 
@@ -36,11 +39,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+INT8_PEAK_TOPS = 5033.2        # MI355X dense int8 MFMA (256 CU x 2.4 GHz x 8192 OP/clk)
 COLD_BYTES = 576 << 20         # rotating working set per kernel: over twice the 256 MB MALL
 
 D_MODEL, D_FF = 4096, 14336
 Q5K_BLOCK = 176               # bytes per Q5_K super-block
 SWEEP_M = (1, 2, 4, 8, 16, 32)
+W8A8_N = W8A8_K = 3072
+W8A8_M = (1024, 8192)
 
 
 def q4k_bytes(n, k):
@@ -60,7 +66,7 @@ def parse():
                    help="also run one device copy of 256 MiB (counter calibration)")
     p.add_argument("--only", default="",
                    help="comma list of kernels to run "
-                        "(gemv,q5k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,q5k_gemm,dequant,read_probe)")
+                        "(gemv,q5k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,q5k_gemm,dequant,w8a8,read_probe)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
     p.add_argument("--eager-only", action="store_true",
                    help="time only the eagerly enqueued launches (no HIP graph replay)")
@@ -232,6 +238,30 @@ def main():
             _lib.check(_lib.q4k_dequantize_bf16(wd.data_ptr(), od.data_ptr(), n, k, sp))
         kernels.append(("dequant_bf16_4096x4096", run_dq, nbytes, 0, rot))
 
+    # ---- INT8 W8A8 linear layer, K = N = 3072: activation row quantizer (bf16 -> int8 +
+    #      scales) and the fused GEMM + dequant epilogue (int8 x, w -> bf16 out)
+    if want("w8a8"):
+        n, k = W8A8_N, W8A8_K
+        for m in W8A8_M:
+            x, xs, w, ws, b = synth.w8a8_case(m, n, k, seed=0)
+            nbytes = m * k + n * k + 4 * m + 8 * n + 2 * m * n
+            rot = Rotor(torch, [x, xs, w, ws, b, np.zeros((m, n), np.int16)], nbytes)
+
+            def run_w8(i, sp, rot=rot, m=m, n=n, k=k):
+                xd, xsd, wd, wsd, bd, od = rot[i]
+                _lib.check(_lib.w8a8_linear(xd.data_ptr(), xsd.data_ptr(), wd.data_ptr(), wsd.data_ptr(),
+                                            bd.data_ptr(), od.data_ptr(), m, n, k, sp))
+            kernels.append(("w8a8_linear_%dx%dx%d" % (m, n, k), run_w8, nbytes, 2 * m * n * k, rot))
+        m = W8A8_M[0]
+        xb = synth.normal_bf16((m, k), seed=0)
+        nbytes = 2 * m * k + m * k + 4 * m
+        rot = Rotor(torch, [xb.view(np.int16), np.zeros((m, k), np.int8), np.zeros(m, np.float32)], nbytes)
+
+        def run_wq(i, sp, rot=rot, m=m, k=k):
+            xd, qd, sd = rot[i]
+            _lib.check(_lib.w8a8_quantize_rows(xd.data_ptr(), qd.data_ptr(), sd.data_ptr(), m, k, sp))
+        kernels.append(("w8a8_quantize_%dx%d" % (m, k), run_wq, nbytes, 0, rot))
+
     # ---- plain streaming read of the weight footprints (ceilings for the GEMV path: the
     #      decode weight, one 14336 x 4096 matrix, and the gate/up pair)
     if want("read_probe"):
@@ -309,12 +339,16 @@ def main():
             r["tflops"] = round(flop / (us * 1e-6) / 1e12, 2)
         if name.startswith("gemm_") or name.startswith("sweep_gemm") or name.startswith("q5k_gemm"):
             r["mfma_frac"] = round(r["tflops"] / BF16_PEAK_TFLOPS, 4)
+        if name.startswith("w8a8_linear"):
+            r["tops"] = r.pop("tflops")
+            r["mfma_frac"] = round(r["tops"] / INT8_PEAK_TOPS, 4)
         per[name] = r
 
     check = None if args.no_check else spot_check(kernels, args, np, torch)
 
     head = per.get("gemv_4096x4096")
     gemm = per.get("gemm_512x4096x4096")
+    w8 = per.get("w8a8_linear_%dx%dx%d" % (W8A8_M[0], W8A8_N, W8A8_K))
     value = head["gbs"] if head else None
     cpu = None if args.no_cpu_baseline or not head else cpu_baseline(args, np)
     crossover = None
@@ -341,6 +375,8 @@ def main():
             "prefill_gemm": "Y = X W^T, X bf16 [512, 4096], W 4096 x 4096 Q4_K",
             "mlp": "SwiGLU 4096 -> 14336 -> 4096 at one token",
             "sweep": "W 14336 x 4096, M in %s" % (list(SWEEP_M),),
+            "w8a8": "INT8 W8A8 linear, int8 x [M, 3072] and w [3072, 3072] with fp32 row scales "
+                    "and bias -> bf16, M in %s; bf16 row quantizer at M = %d" % (list(W8A8_M), W8A8_M[0]),
         },
         "percent_of_peak": {
             "gemv_hbm": round(100 * head["hbm_frac"], 2) if head else None,
@@ -351,6 +387,7 @@ def main():
                              if name.startswith("read_probe_")} or None,
         "roofline": None,
         "roofline_gemm": None,
+        "roofline_w8a8": None,
         "cpu_baseline": cpu,
         "kernels": per,
         "sweep_crossover_m": crossover,
@@ -369,10 +406,34 @@ def main():
                                 "traffic": traffic("gemm_512x4096x4096"),
                                 "kernel": "k_gemm_q4k_kslice<2, 2>",
                                 "flop_per_launch": 2 * 512 * 4096 * 4096}
+    if w8:
+        out["roofline_w8a8"] = {"bound": "mfma", "achieved": w8["tops"], "peak": INT8_PEAK_TOPS,
+                                "unit": "TOP/s", "frac": w8["mfma_frac"],
+                                "traffic": traffic("w8a8_linear_%dx%dx%d" % (W8A8_M[0], W8A8_N, W8A8_K)),
+                                "kernel": "k_w8a8_gemm<2, 2, 2, 1>",
+                                "op_per_launch": 2 * W8A8_M[0] * W8A8_N * W8A8_K}
     print(json.dumps(out))
 
 
-KERNEL_SOURCES = ("k_gemv.hip", "k_gemm.hip", "k_dequant.hip", "q4k_device.h", "q4k_launch.h")
+# Sources each workload's kernels are compiled from (a traffic figure is used only while
+# the code of its kernels is unchanged since the counters were taken).
+_COMMON_SOURCES = ("q4k_device.h", "q4k_launch.h")
+KERNEL_SOURCES = {
+    "gemv": ("k_gemv.hip",),
+    "gemm": ("k_gemm.hip", "lds_copy.h"),
+    "dequant": ("k_dequant.hip",),
+    "w8a8": ("k_w8a8.hip", "lds_copy.h"),
+}
+
+
+def _family(workload):
+    if workload.startswith("w8a8"):
+        return "w8a8"
+    if "gemm" in workload:
+        return "gemm"
+    if workload.startswith("dequant") or workload.startswith("read_probe"):
+        return "dequant"
+    return "gemv"
 
 
 def _code_only(text):
@@ -384,10 +445,10 @@ def _code_only(text):
     return " ".join(text.split())
 
 
-def kernel_source_hash():
+def kernel_source_hash(workload):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[_family(workload)] + _COMMON_SOURCES:
         with open(os.path.join(ROOT, "gemm_q4_super_block_amd", "csrc", f)) as fh:
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
@@ -398,14 +459,15 @@ def traffic(name):
     elementwise-kernel calibration) for workload `name`, from the summaries in profiles/,
     or None if none covers it or the kernel sources changed since it was taken."""
     import glob
-    current = kernel_source_hash()
+    current = kernel_source_hash(name)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         try:
             with open(path) as f:
                 for line in f:
                     if line.startswith("traffic_json: "):
                         t = json.loads(line[len("traffic_json: "):])
-                        if t.get("source_hash") == current and name in t.get("bytes_per_launch", {}):
+                        if (t.get("source_hashes", {}).get(name) == current
+                                and name in t.get("bytes_per_launch", {})):
                             return t["bytes_per_launch"][name]
         except (OSError, ValueError):
             continue
@@ -455,6 +517,16 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "sweep_gemm_14336x4096"
     if "k_read_probe" in name:
         return "read_probe"
+    wg = _template_args(name, "k_w8a8_gemm")
+    if wg:
+        # <TI, TJ, S, OUT>: 128 x 128 tiles of the 3072-wide output, 256 threads each
+        if wg[3] == "1" and threads == 24 * (1024 // 128) * 256:
+            return "w8a8_linear_1024x3072x3072"
+        if wg[3] == "1" and threads == 24 * (8192 // 128) * 256:
+            return "w8a8_linear_8192x3072x3072"
+        return "w8a8_other"
+    if "k_w8a8_quantize_rows" in name:
+        return "w8a8_quantize_1024x3072" if threads == 1024 * 64 else "w8a8_other"
     if "k_zero_f32" in name:
         return "split_k_zero_fill"
     if "copy" in name.lower() or "elementwise" in name:
@@ -548,19 +620,23 @@ def summarize_profile(args):
             lds = int(r.get("LDS_Block_Size", 0))
             util.setdefault((kname, lds, gx), {}).setdefault(r["Counter_Name"], []).append(
                 float(r["Counter_Value"]))
-        lines += ["", "Compute utilization per dispatch from counters, median over dispatches:", "",
-                  "| kernel | LDS B | grid | MfmaUtil % | VALUBusy % | bf16 MFMA FLOP |", "|---|---|---|---|---|---|"]
+        lines += ["", "Compute utilization per dispatch from counters, median over dispatches "
+                  "(MFMA ops = SQ_INSTS_VALU_MFMA_MOPS_BF16 or _I8 x 512):", "",
+                  "| kernel | LDS B | grid | MfmaUtil % | VALUBusy % | MFMA ops |", "|---|---|---|---|---|---|"]
         for (kname, lds, gx), cs in sorted(util.items()):
             if "elementwise" in kname or "copyBuffer" in kname:
                 continue
             med = {c: statistics.median(v) for c, v in cs.items()}
-            mops = med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+            mops, kind = med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"), "bf16"
+            if "SQ_INSTS_VALU_MFMA_MOPS_I8" in med:
+                mops, kind = med["SQ_INSTS_VALU_MFMA_MOPS_I8"], "int8"
             lines.append("| `%s` | %d | %d | %.1f | %.1f | %s |" % (
                 kname[:60], lds, gx, med.get("MfmaUtil", -1), med.get("VALUBusy", -1),
-                "%.4g" % (mops * 512) if mops else "0"))
+                "%.4g %s" % (mops * 512, kind) if mops else "0"))
     if traffic_bytes:
-        lines += ["", "traffic_json: " + json.dumps({"source_hash": kernel_source_hash(),
-                                                     "bytes_per_launch": traffic_bytes})]
+        lines += ["", "traffic_json: " + json.dumps(
+            {"source_hashes": {wl: kernel_source_hash(wl) for wl in traffic_bytes},
+             "bytes_per_launch": traffic_bytes})]
     text = "\n".join(lines) + "\n"
     if args.out:
         with open(args.out, "w") as f:
@@ -597,6 +673,17 @@ def spot_check(kernels, args, np, torch):
             cols = np.arange(0, n, n // 16)
             yr, a = oracle.gemm_cols(w, xb.view(np.uint16), n, 4096, cols)
             res[name] = float((np.abs(y[:, cols] - yr) / (1e-2 * a)).max())
+        elif name.startswith("w8a8_linear"):
+            x, xs, w, ws, b, o = (a.cpu().numpy() for a in t)
+            cols = np.arange(0, o.shape[1], 97)
+            ref = oracle.w8a8_linear_cols(x, xs, w, ws, b, cols)
+            res[name + "_bits_differing"] = int((o.view(np.uint16)[:, cols] != ref).sum())
+        elif name.startswith("w8a8_quantize"):
+            xb, q, sc = (a.cpu().numpy() for a in t)
+            rows = np.arange(0, xb.shape[0], 61)
+            rq, rs = oracle.w8a8_quantize_rows(xb.view(np.uint16)[rows])
+            res[name + "_bits_differing"] = int((q[rows] != rq).sum() +
+                                                (sc[rows].view(np.uint32) != rs.view(np.uint32)).sum())
         elif name == "swiglu_mlp_4096_14336":
             g, u, d, x, h, o = (a.cpu().numpy() for a in t)
             yr, a = oracle.gemv(d.reshape(4096, -1), h, 4096, D_FF)
