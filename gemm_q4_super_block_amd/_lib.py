@@ -22,6 +22,7 @@ Q4K_QK = 256
 Q4K_BLOCK_BYTES = 144
 Q4K_GEMV_MAX_M = 32
 Q5K_BLOCK_BYTES = 176
+Q6K_BLOCK_BYTES = 210
 W8A8_K_STEP = 128
 W8A8_MAX_K = 130944
 
@@ -43,6 +44,9 @@ SIGNATURES = {
     "q5k_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q5k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q5k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "q6k_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q6k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "q6k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "w8a8_linear": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "w8a8_linear_acc": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "w8a8_dequant_epilogue": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp]),
@@ -167,3 +171,15 @@ def w8a8_dequant_epilogue(acc, out, x_scale, w_scale, bias, m, n, stream) -> int
 
 def w8a8_quantize_rows(x_bf16, q, scale, rows, k, stream) -> int:
     return load().w8a8_quantize_rows(x_bf16, q, scale, rows, k, stream)
+
+
+def q6k_gemv(w, x, y, m, n, k, stream) -> int:
+    return load().q6k_gemv(w, x, y, m, n, k, stream)
+
+
+def q6k_dequantize_f32(w, out, n, k, stream) -> int:
+    return load().q6k_dequantize_f32(w, out, n, k, stream)
+
+
+def q6k_dequantize_bf16(w, out, n, k, stream) -> int:
+    return load().q6k_dequantize_bf16(w, out, n, k, stream)

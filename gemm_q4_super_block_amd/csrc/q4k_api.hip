@@ -154,6 +154,14 @@ int q5k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int6
                   "q5k_gemv");
 }
 
+int q6k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (int rc = gemv_checks("q6k_gemv", w, x, y, m, n, k, 210u)) return rc;
+  return launched(q4k::launch_q6k_gemv(static_cast<const uint8_t*>(w), x, y, m, n, k,
+                                       static_cast<hipStream_t>(stream)),
+                  "q6k_gemv");
+}
+
 // Argument checks shared by the Q4_K and Q5_K GEMMs.
 static int gemm_checks(const char* what, const void* w, const uint16_t* x_bf16, const float* y,
                        int64_t m, int64_t n, int64_t k, size_t block) {
@@ -256,6 +264,20 @@ int q5k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k, void
   return launched(q4k::launch_q5k_dequant_bf16(static_cast<const uint8_t*>(w), out, n, k,
                                                static_cast<hipStream_t>(stream)),
                   "q5k_dequantize_bf16");
+}
+
+int q6k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k, void* stream) {
+  if (int rc = dequant_checks("q6k_dequantize_f32", w, out, n, k, 4, 210u)) return rc;
+  return launched(q4k::launch_q6k_dequant_f32(static_cast<const uint8_t*>(w), out, n, k,
+                                              static_cast<hipStream_t>(stream)),
+                  "q6k_dequantize_f32");
+}
+
+int q6k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k, void* stream) {
+  if (int rc = dequant_checks("q6k_dequantize_bf16", w, out, n, k, 2, 210u)) return rc;
+  return launched(q4k::launch_q6k_dequant_bf16(static_cast<const uint8_t*>(w), out, n, k,
+                                               static_cast<hipStream_t>(stream)),
+                  "q6k_dequantize_bf16");
 }
 
 int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {

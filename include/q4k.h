@@ -67,6 +67,8 @@ extern "C" {
 #define Q4K_GEMV_MAX_M 32
 /* Bytes per Q5_K super-block (the q5k_ entry points). */
 #define Q5K_BLOCK_BYTES 176
+/* Bytes per Q6_K block (the q6k_ entry points). */
+#define Q6K_BLOCK_BYTES 210
 
 /* Checks that a HIP device is present and is gfx950, for the current device.
  * Idempotent and cheap after the first call per device; the compute entry
@@ -173,6 +175,34 @@ int q5k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m,
 int q5k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k,
                        void* stream);
 int q5k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
+                        void* stream);
+
+/* ---- Q6_K, the 6-bit sibling ------------------------------------------------
+ * [P3, the kernel work: "k6" keeps its two high bits in a plane and flushes
+ * one scale per sub-block into the accumulator.]  The pages print no Q6_K
+ * layout; the library reads the GGUF one:
+ *   210 bytes encode 256 weights = 16 sub-blocks of 16.
+ *     bytes 0..127    ql[128]: weight 128h + 32j + l (h = 0..1, j = 0..3,
+ *                     l = 0..31) has its low 4 bits in the low (j < 2) or
+ *                     high (j >= 2) nibble of ql[64h + 32(j mod 2) + l]
+ *     bytes 128..191  qh[64]: its top 2 bits are bits 2j, 2j+1 of qh[32h + l]
+ *     bytes 192..207  sc[16]: signed 8-bit sub-block scales
+ *     bytes 208..209  d, fp16, little-endian
+ *   weight i = d * sc[i/16] * (q_i - 32), q_i = 0..63, rounded once to fp32.
+ * A matrix is laid out as for Q4_K with 210-byte blocks (a block may start 2
+ * bytes past a 4-byte boundary; the matrix itself must be 16-byte aligned). */
+
+/* Decode GEMV on Q6_K weights: as q4k_gemv (same x, y, m, n, k, tolerance
+ * and errors) with w a Q6_K matrix [n, k], 16-byte aligned.  A batch (m > 1)
+ * streams W once per x row. */
+int q6k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
+             int64_t k, void* stream);
+
+/* Diagnostic dequantization of a Q6_K matrix: as q4k_dequantize_f32 / _bf16
+ * (exact weight rounded once to fp32; bf16 = nearest even of that). */
+int q6k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k,
+                       void* stream);
+int q6k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
                         void* stream);
 
 #ifdef __cplusplus
