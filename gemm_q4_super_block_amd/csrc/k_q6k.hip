@@ -42,15 +42,32 @@ constexpr int kQ6Bytes = 210;
 constexpr int kQ6Chunk = 4096;   // x elements staged per pass (16 KiB)
 constexpr int kQ6RowsPerWave = 4;
 
-// 8 bytes at address p, with s = p mod 4 in {0, 2}: aligned dword loads from
-// p - s (a third one only when s = 2), shifted into place.
-__device__ __forceinline__ uint2 load8_q6(const uint8_t* p, uint32_t s) {
+// A unit's raw bytes as loaded: four 8-byte fields, each as the aligned dwords
+// that hold it (a third dword only when the block starts 2 bytes past a dword
+// boundary, s = 2), and d.
+struct Q6Raw {
+  uint32_t f[4][3];  // ql low half, ql high half, qh, scales of the half
+  uint32_t d;
+  uint32_t s;
+};
+
+__device__ __forceinline__ void load_field(const uint8_t* p, uint32_t s, uint32_t (&f)[3]) {
   const uint32_t* a = reinterpret_cast<const uint32_t*>(p - s);
-  const uint32_t a0 = a[0], a1 = a[1];
-  uint32_t a2 = 0u;
-  if (s) a2 = a[2];
-  // v_alignbyte_b32(hi, lo, n) = the 64-bit {hi, lo} shifted right by n bytes (n = 0..3)
-  return uint2{__builtin_amdgcn_alignbyte(a1, a0, s), __builtin_amdgcn_alignbyte(a2, a1, s)};
+  f[0] = a[0];
+  f[1] = a[1];
+  f[2] = 0u;
+  if (s) f[2] = a[2];
+}
+
+__device__ __forceinline__ Q6Raw load_raw(const uint8_t* blk, int h, int c) {
+  Q6Raw r;
+  r.s = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(blk) & 3u);
+  load_field(blk + 64 * h + 8 * c, r.s, r.f[0]);
+  load_field(blk + 64 * h + 32 + 8 * c, r.s, r.f[1]);
+  load_field(blk + 128 + 32 * h + 8 * c, r.s, r.f[2]);
+  load_field(blk + 192 + 8 * h, r.s, r.f[3]);
+  r.d = *reinterpret_cast<const uint16_t*>(blk + 208);
+  return r;
 }
 
 // The fields of one unit: quants q[j][e / 4] (four 6-bit values per dword,
@@ -60,39 +77,44 @@ struct Q6Unit {
   float dsc[4];
 };
 
-__device__ __forceinline__ Q6Unit load_unit(const uint8_t* blk, int h, int c) {
-  const uint32_t s = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(blk) & 3u);
-  const uint2 lo = load8_q6(blk + 64 * h + 8 * c, s);
-  const uint2 hi = load8_q6(blk + 64 * h + 32 + 8 * c, s);
-  const uint2 qh = load8_q6(blk + 128 + 32 * h + 8 * c, s);
-  const uint2 sc = load8_q6(blk + 192 + 8 * h, s);
-  const uint32_t dbits = *reinterpret_cast<const uint16_t*>(blk + 208);
+__device__ __forceinline__ Q6Unit decode_unit(const Q6Raw& r, int c) {
+  // v_alignbyte_b32(hi, lo, n) = the 64-bit {hi, lo} shifted right by n bytes (n = 0..3)
+  uint32_t v[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i][0] = __builtin_amdgcn_alignbyte(r.f[i][1], r.f[i][0], r.s);
+    v[i][1] = __builtin_amdgcn_alignbyte(r.f[i][2], r.f[i][1], r.s);
+  }
   Q6Unit u;
-  const uint32_t L[2] = {lo.x, lo.y}, H[2] = {hi.x, hi.y}, Q[2] = {qh.x, qh.y};
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    u.q[0][e] = (L[e] & 0x0F0F0F0Fu) | ((Q[e] << 4) & 0x30303030u);
-    u.q[1][e] = (H[e] & 0x0F0F0F0Fu) | ((Q[e] << 2) & 0x30303030u);
-    u.q[2][e] = ((L[e] >> 4) & 0x0F0F0F0Fu) | (Q[e] & 0x30303030u);
-    u.q[3][e] = ((H[e] >> 4) & 0x0F0F0F0Fu) | ((Q[e] >> 2) & 0x30303030u);
+    const uint32_t L = v[0][e], H = v[1][e], Q = v[2][e];
+    u.q[0][e] = (L & 0x0F0F0F0Fu) | ((Q << 4) & 0x30303030u);
+    u.q[1][e] = (H & 0x0F0F0F0Fu) | ((Q << 2) & 0x30303030u);
+    u.q[2][e] = ((L >> 4) & 0x0F0F0F0Fu) | (Q & 0x30303030u);
+    u.q[3][e] = ((H >> 4) & 0x0F0F0F0Fu) | ((Q >> 2) & 0x30303030u);
   }
-  const float d = half_bits_to_float(dbits);
+  const float d = half_bits_to_float(r.d);
   const int cb = c >> 1;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int b = 2 * j + cb;  // scale byte within the half: sub-block 8h + 2j + c/2
-    const uint32_t word = b < 4 ? sc.x : sc.y;
-    const int v = static_cast<int>(static_cast<int8_t>((word >> (8 * (b & 3))) & 0xFFu));
-    u.dsc[j] = d * static_cast<float>(v);
+    const uint32_t word = b < 4 ? v[3][0] : v[3][1];
+    const int sv = static_cast<int>(static_cast<int8_t>((word >> (8 * (b & 3))) & 0xFFu));
+    u.dsc[j] = d * static_cast<float>(sv);
   }
   return u;
 }
 
-// The 32 x values of a unit (x[j][e]) and their 8-sums.
-struct Q6X {
-  float x[4][8];
-  float s8[4];
-};
+__device__ __forceinline__ Q6Unit load_unit(const uint8_t* blk, int h, int c) {
+  return decode_unit(load_raw(blk, h, c), c);
+}
+
+// GEMV: a workgroup of 4 waves, 4 rows per wave; per 4096-wide chunk of x a
+// lane owns units lane and lane + 64 (8 units per block).  The weight loads of
+// the chunk are issued first, then x is staged, so the staging round trip
+// overlaps the weight stream.
+constexpr int kQ6UnitsPerLane = kQ6Chunk / 32 / 64;
 
 __global__ __launch_bounds__(256) void k_gemv_q6k(const uint8_t* __restrict__ w,
                                                   const float* __restrict__ x,
@@ -113,36 +135,45 @@ __global__ __launch_bounds__(256) void k_gemv_q6k(const uint8_t* __restrict__ w,
 
   for (int c0 = 0; c0 < k; c0 += kQ6Chunk) {
     const int kc = min(kQ6Chunk, k - c0);  // a multiple of 256
-    __syncthreads();                       // the previous chunk's reads are done
+    const int units = kc >> 5;             // 8 per block
+    // Units past a short chunk's end re-read its last unit (not accumulated).
+    Q6Raw raw[kQ6UnitsPerLane][kQ6RowsPerWave];
+#pragma unroll
+    for (int t = 0; t < kQ6UnitsPerLane; ++t) {
+      const int u = min(lane + 64 * t, units - 1);
+      const int bg = (c0 >> 8) + (u >> 3);
+#pragma unroll
+      for (int r = 0; r < kQ6RowsPerWave; ++r)
+        raw[t][r] = load_raw(rows[r] + static_cast<size_t>(bg) * kQ6Bytes, (u >> 2) & 1, u & 3);
+    }
+    __syncthreads();  // the previous chunk's reads of xs are done
     for (int i = 4 * static_cast<int>(threadIdx.x); i < kc; i += 4 * 256)
       *reinterpret_cast<float4*>(xs + i) = *reinterpret_cast<const float4*>(x + c0 + i);
     __syncthreads();
-    const int units = kc >> 5;  // 8 per block
-    for (int u = lane; u < units; u += 64) {
+#pragma unroll
+    for (int t = 0; t < kQ6UnitsPerLane; ++t) {
+      const int u = lane + 64 * t;
+      if (u >= units) continue;
       const int bl = u >> 3, h = (u >> 2) & 1, c = u & 3;
-      Q6X xv;
+      float xv[4][8], s8[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float* p = xs + 256 * bl + 128 * h + 32 * j + 8 * c;
         const float4 a = *reinterpret_cast<const float4*>(p);
         const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        xv.x[j][0] = a.x; xv.x[j][1] = a.y; xv.x[j][2] = a.z; xv.x[j][3] = a.w;
-        xv.x[j][4] = b.x; xv.x[j][5] = b.y; xv.x[j][6] = b.z; xv.x[j][7] = b.w;
-        xv.s8[j] = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+        xv[j][0] = a.x; xv[j][1] = a.y; xv[j][2] = a.z; xv[j][3] = a.w;
+        xv[j][4] = b.x; xv[j][5] = b.y; xv[j][6] = b.z; xv[j][7] = b.w;
+        s8[j] = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
       }
-      const int bg = (c0 >> 8) + bl;  // block index within the row
-      Q6Unit wu[kQ6RowsPerWave];
-#pragma unroll
-      for (int r = 0; r < kQ6RowsPerWave; ++r)
-        wu[r] = load_unit(rows[r] + static_cast<size_t>(bg) * kQ6Bytes, h, c);
 #pragma unroll
       for (int r = 0; r < kQ6RowsPerWave; ++r) {
+        const Q6Unit wu = decode_unit(raw[t][r], c);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float dot = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) dot = fmaf(ubyte_f32(wu[r].q[j][e >> 2], e & 3), xv.x[j][e], dot);
-          acc[r] = fmaf(wu[r].dsc[j], fmaf(-32.0f, xv.s8[j], dot), acc[r]);
+          for (int e = 0; e < 8; ++e) dot = fmaf(ubyte_f32(wu.q[j][e >> 2], e & 3), xv[j][e], dot);
+          acc[r] = fmaf(wu.dsc[j], fmaf(-32.0f, s8[j], dot), acc[r]);
         }
       }
     }
