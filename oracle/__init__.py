@@ -1,5 +1,5 @@
 """ctypes view of the plain C oracle (``q4k_oracle.c``, ``q5k_oracle.c``, ``q6k_oracle.c``,
-``w8a8_oracle.c``).
+``q3k_oracle.c``, ``w8a8_oracle.c``).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product path
@@ -71,6 +71,17 @@ def lib():
         L.oracle_q5k_gemm.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _f64p, _f64p]
         L.oracle_q5k_gemm_cols.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _i64p, _i64,
                                            _f64p, _f64p]
+        L.oracle_q3k_quant.restype = ctypes.c_int
+        L.oracle_q3k_quant.argtypes = [_u8p, ctypes.c_int]
+        L.oracle_q3k_scale.restype = ctypes.c_int
+        L.oracle_q3k_scale.argtypes = [_u8p, ctypes.c_int]
+        L.oracle_q3k_dequant_block.restype = None
+        L.oracle_q3k_dequant_block.argtypes = [_u8p, _f32p]
+        L.oracle_q3k_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
+        L.oracle_q3k_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
+        L.oracle_q3k_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
+        L.oracle_q3k_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
+                                           _f64p, _f64p]
         L.oracle_q6k_quant.restype = ctypes.c_int
         L.oracle_q6k_quant.argtypes = [_u8p, ctypes.c_int]
         L.oracle_q6k_dequant_block.restype = None
@@ -97,7 +108,9 @@ def lib():
                      "oracle_q5k_gemm_cols", "oracle_w8a8_acc", "oracle_w8a8_epilogue",
                      "oracle_w8a8_linear", "oracle_w8a8_linear_cols",
                      "oracle_w8a8_quantize_rows", "oracle_q6k_dequant_f32",
-                     "oracle_q6k_dequant_bf16", "oracle_q6k_gemv", "oracle_q6k_gemv_rows"):
+                     "oracle_q6k_dequant_bf16", "oracle_q6k_gemv", "oracle_q6k_gemv_rows",
+                     "oracle_q3k_dequant_f32", "oracle_q3k_dequant_bf16", "oracle_q3k_gemv",
+                     "oracle_q3k_gemv_rows"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -455,4 +468,69 @@ def q6k_gemv_rows(w: np.ndarray, x: np.ndarray, n: int, k: int, rows):
     a = np.zeros((m, rows.size), np.float64)
     _check(lib().oracle_q6k_gemv_rows(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(rows, _i64p),
                                       rows.size, _p(y, _f64p), _p(a, _f64p)), "q6k_gemv_rows")
+    return y, a
+
+
+# ---- Q3_K (q3k_oracle.h) ----------------------------------------------------
+
+Q3K_BLOCK_BYTES = 110
+
+
+def q3k_quant(blk: np.ndarray, i: int) -> int:
+    blk = _c(blk, np.uint8)
+    assert blk.size == Q3K_BLOCK_BYTES
+    return lib().oracle_q3k_quant(_p(blk, _u8p), int(i))
+
+
+def q3k_scale(blk: np.ndarray, t: int) -> int:
+    blk = _c(blk, np.uint8)
+    assert blk.size == Q3K_BLOCK_BYTES
+    return lib().oracle_q3k_scale(_p(blk, _u8p), int(t))
+
+
+def q3k_dequant_block(blk: np.ndarray) -> np.ndarray:
+    blk = _c(blk, np.uint8)
+    assert blk.size == Q3K_BLOCK_BYTES
+    w = np.zeros(256, np.float32)
+    lib().oracle_q3k_dequant_block(_p(blk, _u8p), _p(w, _f32p))
+    return w
+
+
+def q3k_dequant_f32(w: np.ndarray, n: int, k: int) -> np.ndarray:
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * Q3K_BLOCK_BYTES
+    out = np.zeros((n, k), np.float32)
+    _check(lib().oracle_q3k_dequant_f32(_p(w, _u8p), n, k, _p(out, _f32p)), "q3k_dequant_f32")
+    return out
+
+
+def q3k_dequant_bf16(w: np.ndarray, n: int, k: int) -> np.ndarray:
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * Q3K_BLOCK_BYTES
+    out = np.zeros((n, k), np.uint16)
+    _check(lib().oracle_q3k_dequant_bf16(_p(w, _u8p), n, k, _p(out, _u16p)), "q3k_dequant_bf16")
+    return out
+
+
+def q3k_gemv(w: np.ndarray, x: np.ndarray, n: int, k: int):
+    """y, a = oracle GEMV on Q3_K weights; x fp32 [m, k] (or [k]); fp64 [m, n]."""
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32).reshape(-1, k)
+    m = x.shape[0]
+    y = np.zeros((m, n), np.float64)
+    a = np.zeros((m, n), np.float64)
+    _check(lib().oracle_q3k_gemv(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(y, _f64p),
+                                 _p(a, _f64p)), "q3k_gemv")
+    return y, a
+
+
+def q3k_gemv_rows(w: np.ndarray, x: np.ndarray, n: int, k: int, rows):
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32).reshape(-1, k)
+    rows = _c(rows, np.int64)
+    m = x.shape[0]
+    y = np.zeros((m, rows.size), np.float64)
+    a = np.zeros((m, rows.size), np.float64)
+    _check(lib().oracle_q3k_gemv_rows(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(rows, _i64p),
+                                      rows.size, _p(y, _f64p), _p(a, _f64p)), "q3k_gemv_rows")
     return y, a

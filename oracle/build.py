@@ -12,7 +12,7 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRCS = [os.path.join(HERE, f) for f in ("q4k_oracle.c", "q5k_oracle.c", "q6k_oracle.c", "w8a8_oracle.c")]
+SRCS = [os.path.join(HERE, f) for f in ("q4k_oracle.c", "q5k_oracle.c", "q6k_oracle.c", "q3k_oracle.c", "w8a8_oracle.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",

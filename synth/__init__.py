@@ -25,7 +25,9 @@ A Q5_K super-block (176 bytes) is drawn the same way: fp16 ``d`` and ``dmin`` at
 bytes 0 and 2, the other 172 bytes uniform.  A Q6_K block (210 bytes) has its
 208 quant and scale bytes uniform (6-bit quants uniform in 0..63, signed 8-bit
 sub-block scales uniform in -128..127) and fp16 ``d`` = |N(0,1)| * 1e-4 at byte
-208, so weights have a spread like the Q4_K draws.
+208, so weights have a spread like the Q4_K draws.  A Q3_K block (110 bytes) has
+its 108 quant and scale bytes uniform and fp16 ``d`` = |N(0,1)| * 1e-3 at byte
+108.
 
 INT8 W8A8 inputs (the INT8 linear layer of the xpu-kernels page): int8 codes
 are a normal draw with standard deviation 32, rounded and clipped to
@@ -47,6 +49,7 @@ QK = 256            # weights per super-block
 BLOCK_BYTES = 144   # bytes per Q4_K super-block
 Q5K_BLOCK_BYTES = 176  # bytes per Q5_K super-block (Q4_K plus 32 high-bit bytes)
 Q6K_BLOCK_BYTES = 210  # bytes per Q6_K block
+Q3K_BLOCK_BYTES = 110  # bytes per Q3_K block
 
 # stream ids: one per tensor role, so cases never share draws
 W, X, W_GATE, W_UP, W_DOWN = 0, 1, 2, 3, 4
@@ -104,6 +107,21 @@ def q6k_weights(n: int, k: int, seed: int = 0, stream: int = W,
     d = (np.abs(g.standard_normal(nb)) * scale).astype(np.float16)
     blocks[:, 208:210] = d.view(np.uint8).reshape(nb, 2)
     return blocks.reshape(n, (k // QK) * Q6K_BLOCK_BYTES)
+
+
+def q3k_weights(n: int, k: int, seed: int = 0, stream: int = W,
+                scale: float = 1e-3) -> np.ndarray:
+    """Random Q3_K matrix W [n, k] as uint8 [n, (k/256)*110]: 108 uniform bytes and an fp16
+    d per block."""
+    if k % QK:
+        raise ValueError("k must be a multiple of 256")
+    nb = n * (k // QK)
+    g = rng(seed, stream)
+    blocks = np.empty((nb, Q3K_BLOCK_BYTES), np.uint8)
+    blocks[:, :108] = g.integers(0, 256, size=(nb, 108), dtype=np.uint8)
+    d = (np.abs(g.standard_normal(nb)) * scale).astype(np.float16)
+    blocks[:, 108:110] = d.view(np.uint8).reshape(nb, 2)
+    return blocks.reshape(n, (k // QK) * Q3K_BLOCK_BYTES)
 
 
 def normal_f32(shape, seed: int = 0, stream: int = X) -> np.ndarray:

@@ -1,0 +1,98 @@
+"""Pins of the Q3_K oracle to facts fixed outside it.
+
+The oracle (``oracle/q3k_oracle.c``) follows the Q3_K reading documented in
+its header (the daScript PR page names the 3-bit k-quant, its high-bit plane
+and per-sub-block scales, and prints no layout).  Pins: hand-packed blocks with
+hand-computed weights, round trips through an independently written test
+encoder for every position, value and scale, closed forms, and the GEMV
+against unit vectors and numpy.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from golden_io import hand_blocks
+from q3k_pack import pack_q3k_block
+
+Q3K_HAND = hand_blocks("hand_blocks_q3k.txt", block_bytes=110)
+
+
+@pytest.mark.parametrize("name", sorted(Q3K_HAND))
+def test_q3k_hand_packed_blocks(name):
+    blk, expected = Q3K_HAND[name]
+    got = oracle.q3k_dequant_block(blk).astype(np.float64)
+    np.testing.assert_array_equal(got, expected)
+
+
+def test_q3k_quant_every_position_and_value():
+    rng = np.random.default_rng(3)
+    for i in range(256):
+        for v in (-4, -3, -1, 0, 1, 3):
+            q = np.full(256, -4, np.int64)
+            q[i] = v
+            blk = pack_q3k_block(0x3C00, np.ones(16), q)
+            assert oracle.q3k_quant(blk, i) == v
+            for j in rng.choice(256, 8, replace=False):
+                if j != i:
+                    assert oracle.q3k_quant(blk, j) == -4
+
+
+def test_q3k_scale_every_sub_block_and_value():
+    for t in range(16):
+        for v in (-32, -17, -1, 0, 1, 15, 16, 31):
+            sc = np.full(16, -32, np.int64)
+            sc[t] = v
+            blk = pack_q3k_block(0x3C00, sc, np.zeros(256, np.int64))
+            assert [oracle.q3k_scale(blk, u) for u in range(16)] == sc.tolist()
+
+
+def test_q3k_random_round_trip():
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        q = rng.integers(-4, 4, 256)
+        sc = rng.integers(-32, 32, 16)
+        blk = pack_q3k_block(0x3C00, sc, q)  # d = 1
+        w = oracle.q3k_dequant_block(blk).astype(np.float64)
+        np.testing.assert_array_equal(w, np.repeat(sc, 16) * q)
+
+
+def test_q3k_closed_forms():
+    sc = np.arange(-16, 16, 2)
+    # q = 0 everywhere: zero; q = -4 everywhere: -4 d sc with d = 0x3555 = 0.333251953125
+    assert not oracle.q3k_dequant_block(pack_q3k_block(0x3555, sc, np.zeros(256, np.int64))).any()
+    w = oracle.q3k_dequant_block(pack_q3k_block(0x3555, sc, np.full(256, -4)))
+    np.testing.assert_array_equal(w, (np.repeat(sc, 16) * -4 * 0.333251953125).astype(np.float32))
+
+
+def test_q3k_dequant_bf16_is_rne_of_f32():
+    w = synth.q3k_weights(16, 512, seed=4)
+    f = oracle.q3k_dequant_f32(w, 16, 512)
+    b = oracle.q3k_dequant_bf16(w, 16, 512)
+    np.testing.assert_array_equal(b, synth.bf16_bits(f))
+
+
+def test_q3k_gemv_unit_vectors_give_columns():
+    n, k = 8, 512
+    w = synth.q3k_weights(n, k, seed=8)
+    W = oracle.q3k_dequant_f32(w, n, k).astype(np.float64)
+    for c in (0, 1, 255, 256, 511):
+        x = np.zeros(k, np.float32)
+        x[c] = 1.0
+        y, _ = oracle.q3k_gemv(w, x, n, k)
+        np.testing.assert_array_equal(y[0], W[:, c])
+
+
+def test_q3k_gemv_matches_library_matmul():
+    n, k, m = 24, 1024, 3
+    w = synth.q3k_weights(n, k, seed=9)
+    x = synth.normal_f32((m, k), seed=9)
+    y, a = oracle.q3k_gemv(w, x, n, k)
+    W = oracle.q3k_dequant_f32(w, n, k).astype(np.float64)
+    ref = x.astype(np.float64) @ W.T
+    assert np.all(np.abs(y - ref) <= 1e-12 * a)
+    rows = np.array([23, 0, 7])
+    yr, _ = oracle.q3k_gemv_rows(w, x, n, k, rows)
+    np.testing.assert_array_equal(yr, y[:, rows])
