@@ -3,7 +3,7 @@
 One *step* is one pass of the whole hot path over the workload's synthetic
 inputs, each kernel on cold weights:
   * decode GEMV, W 4096 x 4096 Q4_K, fp32 x (the headline configuration), and
-    the same shape on the Q5_K and Q6_K sibling formats;
+    the same shape on the Q5_K, Q6_K and Q3_K sibling formats;
   * small-batch GEMV and GEMM, W 14336 x 4096, M in {1, 2, 4, 8, 16, 32};
   * SwiGLU MLP at one token: gate/up 14336 x 4096, down 4096 x 14336;
   * prefill GEMM, X bf16 [512, 4096], W 4096 x 4096 and 14336 x 4096;
@@ -46,6 +46,7 @@ COLD_BYTES = 576 << 20         # rotating working set per kernel: over twice the
 D_MODEL, D_FF = 4096, 14336
 Q5K_BLOCK = 176               # bytes per Q5_K super-block
 Q6K_BLOCK = 210               # bytes per Q6_K block
+Q3K_BLOCK = 110               # bytes per Q3_K block
 SWEEP_M = (1, 2, 4, 8, 16, 32)
 W8A8_N = W8A8_K = 3072
 W8A8_M = (1024, 8192)
@@ -68,7 +69,7 @@ def parse():
                    help="also run one device copy of 256 MiB (counter calibration)")
     p.add_argument("--only", default="",
                    help="comma list of kernels to run "
-                        "(gemv,q5k_gemv,q6k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,q5k_gemm,dequant,w8a8,"
+                        "(gemv,q5k_gemv,q6k_gemv,q3k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,q5k_gemm,dequant,w8a8,"
                         "read_probe)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
     p.add_argument("--eager-only", action="store_true",
@@ -174,6 +175,19 @@ def main():
             wd, xd, yd = rot[i]
             _lib.check(_lib.q6k_gemv(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), 1, n, k, sp))
         kernels.append(("q6k_gemv_4096x4096", run_q6, nbytes, 2 * n * k, rot))
+
+    # ---- decode GEMV on the Q3_K sibling format, 4096 x 4096
+    if want("q3k_gemv"):
+        n = k = D_MODEL
+        w = synth.q3k_weights(n, k, seed=0)
+        x = synth.normal_f32(k, seed=0)
+        nbytes = n * (k // 256) * Q3K_BLOCK + 4 * k + 4 * n
+        rot = Rotor(torch, [w, x, np.zeros(n, np.float32)], nbytes)
+
+        def run_q3(i, sp, rot=rot, n=n, k=k):
+            wd, xd, yd = rot[i]
+            _lib.check(_lib.q3k_gemv(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), 1, n, k, sp))
+        kernels.append(("q3k_gemv_4096x4096", run_q3, nbytes, 2 * n * k, rot))
 
     # ---- small-batch sweep, W 14336 x 4096
     if want("sweep_gemv") or want("sweep_gemm"):
@@ -439,15 +453,15 @@ KERNEL_SOURCES = {
     "gemm": ("k_gemm.hip", "lds_copy.h"),
     "dequant": ("k_dequant.hip",),
     "w8a8": ("k_w8a8.hip", "lds_copy.h"),
-    "q6k": ("k_q6k.hip",),
+    "planes": ("k_planes.hip",),
 }
 
 
 def _family(workload):
     if workload.startswith("w8a8"):
         return "w8a8"
-    if workload.startswith("q6k"):
-        return "q6k"
+    if workload.startswith("q6k") or workload.startswith("q3k"):
+        return "planes"
     if "gemm" in workload:
         return "gemm"
     if workload.startswith("dequant") or workload.startswith("read_probe"):
@@ -536,10 +550,11 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "sweep_gemm_14336x4096"
     if "k_read_probe" in name:
         return "read_probe"
-    if "k_gemv_q6k" in name:
-        return "q6k_gemv_4096x4096" if threads == 4096 // 16 * 256 else "q6k_other"
-    if "k_dequant_q6k" in name:
-        return "q6k_dequant"
+    gp = _template_args(name, "k_gemv_planes")
+    if gp:
+        return ("q%sk_gemv_4096x4096" % gp[0]) if threads == 4096 // 16 * 256 else "planes_other"
+    if "k_dequant_planes" in name:
+        return "planes_dequant"
     wg = _template_args(name, "k_w8a8_gemm")
     if wg:
         # <TI, TJ, S, OUT>: 128 x 128 tiles of the 3072-wide output, 256 threads each
@@ -689,6 +704,11 @@ def spot_check(kernels, args, np, torch):
             w, x, y = (a.cpu().numpy() for a in t)
             rows = np.arange(0, 4096, 37)
             yr, a = oracle.q6k_gemv_rows(w, x, 4096, 4096, rows)
+            res[name] = float((np.abs(y[rows] - yr[0]) / (1e-4 * a[0])).max())
+        elif name == "q3k_gemv_4096x4096":
+            w, x, y = (a.cpu().numpy() for a in t)
+            rows = np.arange(0, 4096, 37)
+            yr, a = oracle.q3k_gemv_rows(w, x, 4096, 4096, rows)
             res[name] = float((np.abs(y[rows] - yr[0]) / (1e-4 * a[0])).max())
         elif name == "q5k_gemm_512x4096x4096":
             w, xb, y = (a.cpu().numpy() for a in t)

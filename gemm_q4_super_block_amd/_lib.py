@@ -23,6 +23,7 @@ Q4K_BLOCK_BYTES = 144
 Q4K_GEMV_MAX_M = 32
 Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
+Q3K_BLOCK_BYTES = 110
 W8A8_K_STEP = 128
 W8A8_MAX_K = 130944
 
@@ -47,6 +48,9 @@ SIGNATURES = {
     "q6k_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q6k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q6k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "q3k_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q3k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "q3k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "w8a8_linear": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "w8a8_linear_acc": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "w8a8_dequant_epilogue": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp]),
@@ -183,3 +187,15 @@ def q6k_dequantize_f32(w, out, n, k, stream) -> int:
 
 def q6k_dequantize_bf16(w, out, n, k, stream) -> int:
     return load().q6k_dequantize_bf16(w, out, n, k, stream)
+
+
+def q3k_gemv(w, x, y, m, n, k, stream) -> int:
+    return load().q3k_gemv(w, x, y, m, n, k, stream)
+
+
+def q3k_dequantize_f32(w, out, n, k, stream) -> int:
+    return load().q3k_dequantize_f32(w, out, n, k, stream)
+
+
+def q3k_dequantize_bf16(w, out, n, k, stream) -> int:
+    return load().q3k_dequantize_bf16(w, out, n, k, stream)

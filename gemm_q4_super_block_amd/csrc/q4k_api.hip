@@ -162,6 +162,14 @@ int q6k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int6
                   "q6k_gemv");
 }
 
+int q3k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (int rc = gemv_checks("q3k_gemv", w, x, y, m, n, k, 110u)) return rc;
+  return launched(q4k::launch_q3k_gemv(static_cast<const uint8_t*>(w), x, y, m, n, k,
+                                       static_cast<hipStream_t>(stream)),
+                  "q3k_gemv");
+}
+
 // Argument checks shared by the Q4_K and Q5_K GEMMs.
 static int gemm_checks(const char* what, const void* w, const uint16_t* x_bf16, const float* y,
                        int64_t m, int64_t n, int64_t k, size_t block) {
@@ -278,6 +286,20 @@ int q6k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k, void
   return launched(q4k::launch_q6k_dequant_bf16(static_cast<const uint8_t*>(w), out, n, k,
                                                static_cast<hipStream_t>(stream)),
                   "q6k_dequantize_bf16");
+}
+
+int q3k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k, void* stream) {
+  if (int rc = dequant_checks("q3k_dequantize_f32", w, out, n, k, 4, 110u)) return rc;
+  return launched(q4k::launch_q3k_dequant_f32(static_cast<const uint8_t*>(w), out, n, k,
+                                              static_cast<hipStream_t>(stream)),
+                  "q3k_dequantize_f32");
+}
+
+int q3k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k, void* stream) {
+  if (int rc = dequant_checks("q3k_dequantize_bf16", w, out, n, k, 2, 110u)) return rc;
+  return launched(q4k::launch_q3k_dequant_bf16(static_cast<const uint8_t*>(w), out, n, k,
+                                               static_cast<hipStream_t>(stream)),
+                  "q3k_dequantize_bf16");
 }
 
 int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {

@@ -57,6 +57,14 @@ hipError_t launch_q6k_dequant_f32(const uint8_t* w, float* out, int64_t n, int64
 hipError_t launch_q6k_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64_t k,
                                    hipStream_t stream);
 
+// Q3_K (110-byte blocks): GEMV (one launch per x row) and the dequant exports.
+hipError_t launch_q3k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                           int64_t k, hipStream_t stream);
+hipError_t launch_q3k_dequant_f32(const uint8_t* w, float* out, int64_t n, int64_t k,
+                                  hipStream_t stream);
+hipError_t launch_q3k_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64_t k,
+                                   hipStream_t stream);
+
 // INT8 W8A8 linear layer (k % 128 == 0, pointers 16-byte aligned).
 hipError_t launch_w8a8_linear(const int8_t* x, const float* x_scale, const int8_t* w,
                               const float* w_scale, const float* bias, uint16_t* out, int64_t m,

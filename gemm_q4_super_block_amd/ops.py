@@ -4,7 +4,7 @@ PyTorch provides device memory and the current stream; every computation runs
 in libq4k's HIP kernels.  Weights are ``torch.uint8`` tensors holding raw Q4_K
 super-blocks, shape ``[n, (k // 256) * 144]`` (Q5_K: 176-byte blocks,
 ``[n, (k // 256) * 176]``, for the ``q5k_`` functions; Q6_K: 210-byte blocks for the
-``q6k_`` functions).  The INT8 W8A8 layer
+``q6k_`` functions; Q3_K: 110-byte blocks for the ``q3k_`` functions).  The INT8 W8A8 layer
 (``w8a8_*``) takes int8 codes with fp32 per-row scales and returns bf16.
 """
 from __future__ import annotations
@@ -12,7 +12,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import Q4K_BLOCK_BYTES, Q4K_QK, Q5K_BLOCK_BYTES, Q6K_BLOCK_BYTES, check
+from ._lib import Q3K_BLOCK_BYTES, Q4K_BLOCK_BYTES, Q4K_QK, Q5K_BLOCK_BYTES, Q6K_BLOCK_BYTES, check
 
 
 def _stream(device: torch.device) -> int:
@@ -48,6 +48,11 @@ def q5k_gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) 
 def q6k_gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """gemv() for a Q6_K W (uint8 [n, k/256*210])."""
     return _gemv(w, x, out, Q6K_BLOCK_BYTES, _lib.q6k_gemv)
+
+
+def q3k_gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemv() for a Q3_K W (uint8 [n, k/256*110])."""
+    return _gemv(w, x, out, Q3K_BLOCK_BYTES, _lib.q3k_gemv)
 
 
 def _gemv(w, x, out, block, fn):
@@ -153,6 +158,22 @@ def q6k_dequantize_bf16(w: torch.Tensor) -> torch.Tensor:
     n, k = _q4k_shape(w, Q6K_BLOCK_BYTES)
     out = torch.empty((n, k), dtype=torch.bfloat16, device=w.device)
     check(_lib.q6k_dequantize_bf16(w.data_ptr(), out.data_ptr(), n, k, _stream(w.device)))
+    return out
+
+
+def q3k_dequantize_f32(w: torch.Tensor) -> torch.Tensor:
+    """Dequantized Q3_K W as fp32 [n, k]."""
+    n, k = _q4k_shape(w, Q3K_BLOCK_BYTES)
+    out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    check(_lib.q3k_dequantize_f32(w.data_ptr(), out.data_ptr(), n, k, _stream(w.device)))
+    return out
+
+
+def q3k_dequantize_bf16(w: torch.Tensor) -> torch.Tensor:
+    """Dequantized Q3_K W as bf16 [n, k] (nearest-even rounding of the fp32 weight)."""
+    n, k = _q4k_shape(w, Q3K_BLOCK_BYTES)
+    out = torch.empty((n, k), dtype=torch.bfloat16, device=w.device)
+    check(_lib.q3k_dequantize_bf16(w.data_ptr(), out.data_ptr(), n, k, _stream(w.device)))
     return out
 
 

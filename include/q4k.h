@@ -69,6 +69,8 @@ extern "C" {
 #define Q5K_BLOCK_BYTES 176
 /* Bytes per Q6_K block (the q6k_ entry points). */
 #define Q6K_BLOCK_BYTES 210
+/* Bytes per Q3_K block (the q3k_ entry points). */
+#define Q3K_BLOCK_BYTES 110
 
 /* Checks that a HIP device is present and is gfx950, for the current device.
  * Idempotent and cheap after the first call per device; the compute entry
@@ -203,6 +205,34 @@ int q6k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
 int q6k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k,
                        void* stream);
 int q6k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
+                        void* stream);
+
+/* ---- Q3_K, the 3-bit sibling ------------------------------------------------
+ * [P3, the kernel work: "k3", like k6, keeps its high bits in a plane and
+ * flushes one scale per sub-block into the accumulator.]  The pages print no
+ * Q3_K layout; the library reads the GGUF one:
+ *   110 bytes encode 256 weights = 16 sub-blocks of 16.
+ *     bytes 0..31     hmask[32]: the third bit of weight 128h + 32j + l is bit
+ *                     4h + j of hmask[l]
+ *     bytes 32..95    qs[64]: its low two bits are bits 2j, 2j+1 of qs[32h + l]
+ *     bytes 96..107   s[12]: sub-block t's 6-bit scale u_t has the low nibble
+ *                     of s[t] (t < 8) or the high nibble of s[t - 8], and bits
+ *                     2(t/4), 2(t/4)+1 of s[8 + t mod 4] on top
+ *     bytes 108..109  d, fp16, little-endian
+ *   weight i = d * (u_{i/16} - 32) * (q_i - 4), q_i = 0..7 (exact in fp32).
+ * A matrix is laid out as for Q4_K with 110-byte blocks (16-byte aligned). */
+
+/* Decode GEMV on Q3_K weights: as q4k_gemv (same x, y, m, n, k, tolerance
+ * and errors) with w a Q3_K matrix [n, k], 16-byte aligned.  A batch (m > 1)
+ * streams W once per x row. */
+int q3k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
+             int64_t k, void* stream);
+
+/* Diagnostic dequantization of a Q3_K matrix (the exact weight in fp32; bf16 =
+ * nearest even of that). */
+int q3k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k,
+                       void* stream);
+int q3k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
                         void* stream);
 
 #ifdef __cplusplus

@@ -23,7 +23,7 @@ HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.jo
 
 def declared_symbols():
     text = "\n".join(open(h).read() for h in HEADERS)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?((?:q[456]k|w8a8)_\w+)\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?((?:q[3456]k|w8a8)_\w+)\(",
                                  text, re.M)))
 
 
@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     for name in ("q4k_gemv", "q4k_gemm", "q4k_swiglu_mlp", "q4k_init", "q4k_last_error",
                  "q4k_dequantize_f32", "q4k_dequantize_bf16", "q4k_device_name", "q4k_version",
                  "q5k_gemv", "q5k_gemm", "q5k_dequantize_f32", "q5k_dequantize_bf16",
-                 "q6k_gemv", "q6k_dequantize_f32", "q6k_dequantize_bf16", "w8a8_linear", "w8a8_linear_acc", "w8a8_dequant_epilogue", "w8a8_quantize_rows"):
+                 "q6k_gemv", "q6k_dequantize_f32", "q6k_dequantize_bf16", "q3k_gemv",
+                 "q3k_dequantize_f32", "q3k_dequantize_bf16", "w8a8_linear", "w8a8_linear_acc", "w8a8_dequant_epilogue", "w8a8_quantize_rows"):
         assert name in syms
 
 
@@ -48,7 +49,8 @@ def test_header_constants_match_binding():
     text = "\n".join(open(h).read() for h in HEADERS)
     for name in ("Q4K_OK", "Q4K_ERR_INVALID_ARG", "Q4K_ERR_ALIGN", "Q4K_ERR_DEVICE",
                  "Q4K_ERR_LAUNCH", "Q4K_QK", "Q4K_BLOCK_BYTES", "Q4K_GEMV_MAX_M",
-                 "Q5K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "W8A8_K_STEP", "W8A8_MAX_K"):
+                 "Q5K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "Q3K_BLOCK_BYTES", "W8A8_K_STEP",
+                 "W8A8_MAX_K"):
         mm = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
         assert mm, name
         assert int(mm.group(1)) == getattr(_lib, name), name
@@ -223,3 +225,16 @@ def test_q6k_rejects_bad_arguments():
     assert _lib.q6k_dequantize_bf16(A, 2 * A + 4, 4, 256, None) == _lib.Q4K_ERR_ALIGN
     assert _lib.q6k_dequantize_f32(A, A + 832, 4, 256, None) == _lib.Q4K_ERR_INVALID_ARG  # out in w
     assert _lib.q4k_last_error().startswith("q6k_dequantize_f32")
+
+
+def test_q3k_rejects_bad_arguments():
+    assert _lib.q3k_gemv(0, A, 2 * A, 1, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q4k_last_error().startswith("q3k_gemv")
+    assert _lib.q3k_gemv(A, 2 * A, 3 * A, 33, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q3k_gemv(A, 2 * A, 3 * A, 1, 16, 384, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q3k_gemv(A + 4, 2 * A, 3 * A, 1, 16, 256, None) == _lib.Q4K_ERR_ALIGN
+    # 16 rows of one 110-byte block span 1760 bytes from A: y may not start inside
+    assert _lib.q3k_gemv(A, 2 * A, A + 1744, 1, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q3k_dequantize_bf16(A, 2 * A + 2, 4, 256, None) == _lib.Q4K_ERR_ALIGN
+    assert _lib.q3k_dequantize_f32(A, A + 432, 4, 256, None) == _lib.Q4K_ERR_INVALID_ARG  # out in w
+    assert _lib.q4k_last_error().startswith("q3k_dequantize_f32")
