@@ -552,7 +552,7 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "read_probe"
     gp = _template_args(name, "k_gemv_planes")
     if gp:
-        return ("q%sk_gemv_4096x4096" % gp[0]) if threads == 4096 // 16 * 256 else "planes_other"
+        return ("q%sk_gemv_4096x4096" % gp[0]) if threads == 4096 // 16 * 512 else "planes_other"
     if "k_dequant_planes" in name:
         return "planes_dequant"
     wg = _template_args(name, "k_w8a8_gemm")
