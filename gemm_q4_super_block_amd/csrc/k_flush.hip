@@ -1,0 +1,232 @@
+// k_flush.hip -- Q4_K GEMV for batches of 6 to 32 rows on bf16 MFMA, with the
+// sub-block scales flushed into the fp32 accumulator.
+//
+// What it computes is q4k_gemv's y = x W^T (fp32 x, fp32 y, the same
+// tolerance).  The method is the daScript PR page's scale flush ("CPU kernel
+// parity ...", the kernel work: the k-quants "flush their scales fused into
+// the accumulator"): within a 32-weight sub-block every weight is
+// d sc q - dmin m with one (d sc, dmin m) pair, so
+//   sum_i w_i x_i = (d sc) sum_i q_i x_i - (dmin m) sum_i x_i,
+// and the two sums can come from a matrix core working on the raw quants.
+//
+// Design for gfx950:
+//   * v_mfma_f32_16x16x32_bf16: one MFMA is exactly one sub-block (K = 32)
+//     for 16 batch rows (M) and 16 weight rows (N).  The quants q = 0..15 are
+//     exact in bf16.  fp32 x is split into x_hi = bf16(x) and x_lo = bf16(x -
+//     x_hi): every product q x_hi, q x_lo is exact in the fp32 accumulator and
+//     x_hi + x_lo is within 2^-17 |x| of x, so the result has fp32-GEMV
+//     accuracy, not bf16 accuracy.
+//   * per sub-block and 16x16 tile: P = sum q x (two MFMAs, hi and lo) and
+//     S = sum x (two MFMAs against a B of ones, shared by every weight tile);
+//     then acc += (d sc) P - (dmin m) S per output, eight VALU FMAs per lane.
+//     The weights are never dequantized: per weight the VALU cost is one
+//     nibble-to-bf16 conversion, shared by all batch rows.
+//   * operand layout (both operands alike, so any internal k order gives the
+//     same contraction): lane l supplies row l % 16 (a batch row of x, or a
+//     weight row) and the 8 consecutive k of its k-group l / 16.  For quant
+//     group g a lane's 8 quant bytes (32g + 8 (l/16) ..) hold the low nibbles
+//     of sub-block 2g and the high nibbles of sub-block 2g + 1.  The result
+//     tile holds batch row 4 (l/16) + r, weight row l % 16 in register r.
+//   * a workgroup of 4 waves owns 16 NT weight rows (NT = 2 from 8192 rows);
+//     wave w takes super-blocks w, w + 4, ... of the rows (prefetching the
+//     next one's header and quants), and the four partial tiles are summed
+//     through LDS at the end.
+//   * measured against the fp32 FMA passes on 4096 and 14336 rows, it is
+//     faster from 6 batch rows on (14336 x 4096, m = 32: 43 us against 127);
+//     below that the passes stay.
+#include <hip/hip_runtime.h>
+
+#include "q4k_device.h"
+#include "q4k_launch.h"
+
+namespace q4k {
+namespace {
+
+typedef float f4v_t __attribute__((ext_vector_type(4)));
+
+// bf16x8 of 8 bytes' low (HIGH = false) or high nibbles, in byte order.
+template <bool HIGH>
+__device__ __forceinline__ bf16x8_t nibbles_bf16(uint2 q) {
+  const uint32_t a = HIGH ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
+  const uint32_t b = HIGH ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
+  const uint4 v{pack_bf16x2(ubyte_f32(a, 0), ubyte_f32(a, 1)), pack_bf16x2(ubyte_f32(a, 2), ubyte_f32(a, 3)),
+                pack_bf16x2(ubyte_f32(b, 0), ubyte_f32(b, 1)), pack_bf16x2(ubyte_f32(b, 2), ubyte_f32(b, 3))};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// 8 fp32 values -> (hi, lo) bf16x8 with hi = bf16(v), lo = bf16(v - hi).
+__device__ __forceinline__ void split_bf16(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    const float r0 = v[2 * i] - __builtin_bit_cast(float, h[i] << 16);
+    const float r1 = v[2 * i + 1] - __builtin_bit_cast(float, h[i] & 0xFFFF0000u);
+    l[i] = pack_bf16x2(r0, r1);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, uint4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8_t, uint4{l[0], l[1], l[2], l[3]});
+}
+
+template <int MT, int NT>
+__global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ w,
+                                                    const float* __restrict__ x,
+                                                    float* __restrict__ y, int m, int n, int k) {
+  __shared__ __attribute__((aligned(16))) float red[4][MT][NT][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nl = lane & 15, kg = lane >> 4;
+  const int nb = k >> 8;
+  const int n0 = blockIdx.x * 16 * NT;
+
+  // Weight rows of this lane (clamped; rows past n are computed, not stored).
+  const uint8_t* wrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    wrow[t] = w + static_cast<size_t>(min(n0 + 16 * t + nl, n - 1)) * nb * kBlockBytes;
+  // Batch rows this lane feeds as the A operand; rows past m read row m - 1 and
+  // are zeroed.
+  const float* xrow[MT];
+  bool xvalid[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    xrow[t] = x + static_cast<size_t>(min(16 * t + nl, m - 1)) * k;
+    xvalid[t] = 16 * t + nl < m;
+  }
+
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  f4v_t acc[MT][NT];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = f4v_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  struct WBlock {
+    uint4 hd[NT];
+    uint2 q[NT][4];
+  };
+  auto load_w = [&](int b, WBlock& wb) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint8_t* p = wrow[t] + static_cast<size_t>(b) * kBlockBytes;
+      wb.hd[t] = *reinterpret_cast<const uint4*>(p);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) wb.q[t][g] = *reinterpret_cast<const uint2*>(p + 16 + 32 * g + 8 * kg);
+    }
+  };
+
+  WBlock cur, nxt;
+  int b = wave;
+  if (b < nb) load_w(b, cur);
+  for (; b < nb; b += 4) {
+    if (b + 4 < nb) load_w(b + 4, nxt);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // x of sub-blocks 2g (s = 0) and 2g + 1 (s = 1), this lane's 8 k of each
+      bf16x8_t ahi[MT][2], alo[MT][2];
+      f4v_t sx[MT][2];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const float* p = xrow[t] + 256 * b + 64 * g + 32 * s + 8 * kg;
+          const float4 u = *reinterpret_cast<const float4*>(p);
+          const float4 v = *reinterpret_cast<const float4*>(p + 4);
+          float xv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+          if (!xvalid[t]) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[e] = 0.0f;
+          }
+          split_bf16(xv, ahi[t][s], alo[t][s]);
+          f4v_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][s], ones, z, 0, 0, 0);
+          sx[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t][s], ones, z, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const GroupScales sc = group_scales(cur.hd[nt], g);
+        // d sc without the fp8 widening factor (exact: a power of two)
+        const float dlo = sc.a_lo * (1.0f / kNibbleUnscale), dhi = sc.a_hi * (1.0f / kNibbleUnscale);
+        const bf16x8_t blo = nibbles_bf16<false>(cur.q[nt][g]);
+        const bf16x8_t bhi = nibbles_bf16<true>(cur.q[nt][g]);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          f4v_t plo = {0.0f, 0.0f, 0.0f, 0.0f}, phi = {0.0f, 0.0f, 0.0f, 0.0f};
+          plo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][0], blo, plo, 0, 0, 0);
+          plo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t][0], blo, plo, 0, 0, 0);
+          phi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][1], bhi, phi, 0, 0, 0);
+          phi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t][1], bhi, phi, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float a = acc[t][nt][r];
+            a = fmaf(dlo, plo[r], a);
+            a = fmaf(-sc.b_lo, sx[t][0][r], a);
+            a = fmaf(dhi, phi[r], a);
+            a = fmaf(-sc.b_hi, sx[t][1][r], a);
+            acc[t][nt][r] = a;
+          }
+        }
+      }
+    }
+    cur = nxt;
+  }
+
+  // Sum the four waves' partial tiles; wave 0 stores.  Tile register r holds
+  // batch row 4 kg + r, weight row nl.
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][t][nt][r][lane] = acc[t][nt][r];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = ((red[0][t][nt][r][lane] + red[1][t][nt][r][lane]) + red[2][t][nt][r][lane]) +
+                        red[3][t][nt][r][lane];
+        const int row = 16 * t + 4 * kg + r, col = n0 + 16 * nt + nl;
+        if (row < m && col < n) y[static_cast<size_t>(row) * n + col] = v;
+      }
+}
+
+}  // namespace
+
+bool gemv_flush_supported(int64_t m) { return m >= kGemvFlushMinM && m <= 32; }
+
+// One 16-row batch tile for m <= 16, two above.  Matrices of at least
+// kFlushWideRows rows give each workgroup two 16-row weight tiles (x's split
+// and its sums shared by both; measured 1.4-1.6x faster at 14336 rows, slower
+// at 4096, where the grid would drop to 128 workgroups).
+constexpr int kFlushWideRows = 8192;
+
+template <int MT, int NT>
+void launch_flush_tiles(const uint8_t* w, const float* x, float* y, int m, int n, int k,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemv_flush<MT, NT>), dim3((n + 16 * NT - 1) / (16 * NT)), dim3(256), 0,
+                     stream, w, x, y, m, n, k);
+}
+
+hipError_t launch_gemv_flush(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                             int64_t k, hipStream_t stream) {
+  const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
+  if (ni >= kFlushWideRows) {
+    if (mi <= 16)
+      launch_flush_tiles<1, 2>(w, x, y, mi, ni, ki, stream);
+    else
+      launch_flush_tiles<2, 2>(w, x, y, mi, ni, ki, stream);
+  } else {
+    if (mi <= 16)
+      launch_flush_tiles<1, 1>(w, x, y, mi, ni, ki, stream);
+    else
+      launch_flush_tiles<2, 1>(w, x, y, mi, ni, ki, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace q4k

@@ -408,8 +408,8 @@ hipError_t launch(const uint8_t* w, const uint8_t* w2, const float* x, float* y,
 }
 
 template <int FMT>
-hipError_t launch_gemv_fmt(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
-                           int64_t k, hipStream_t stream) {
+hipError_t launch_gemv_passes(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                              int64_t k, hipStream_t stream) {
   // Batches above 8 rows run as passes of 8 over x and y; W is re-streamed.
   for (int64_t i0 = 0; i0 < m; i0 += 8) {
     const int mm = static_cast<int>(m - i0 < 8 ? m - i0 : 8);
@@ -443,14 +443,17 @@ hipError_t launch_gemv_fmt(const uint8_t* w, const float* x, float* y, int64_t m
 
 }  // namespace
 
+// Q4_K batches from kGemvFlushMinM rows take the scale-flush MFMA kernel
+// (k_flush.hip); smaller ones, and Q5_K, the fp32 FMA passes.
 hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream) {
-  return launch_gemv_fmt<4>(w, x, y, m, n, k, stream);
+  if (gemv_flush_supported(m)) return launch_gemv_flush(w, x, y, m, n, k, stream);
+  return launch_gemv_passes<4>(w, x, y, m, n, k, stream);
 }
 
 hipError_t launch_q5k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                            int64_t k, hipStream_t stream) {
-  return launch_gemv_fmt<5>(w, x, y, m, n, k, stream);
+  return launch_gemv_passes<5>(w, x, y, m, n, k, stream);
 }
 
 hipError_t launch_gateup_swiglu(const uint8_t* w_gate, const uint8_t* w_up, const float* x,

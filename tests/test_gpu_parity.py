@@ -393,3 +393,32 @@ def test_gemm_long_k(q4k):
     cols = np.arange(0, n, 7)
     Yr, A = oracle.gemm_cols(w, xb, n, k, cols)
     assert_within(Y[:, cols], Yr, A, GEMM_TOL, "gemm 64x512x16384")
+
+
+# ------------------------------------------------------------------ scale flush
+
+# Q4_K batches of 4..32 rows run on bf16 MFMA with x split into bf16 hi + lo
+# and the sub-block scales flushed into the fp32 accumulator.  Edges: one
+# super-block (only the first of the four K-split waves has work), a block
+# count not divisible by four, single and ragged 16-row weight tiles, batch
+# sizes around the 16-row MFMA tile, matrices past 8192 rows (two weight
+# tiles per workgroup, ragged), and x spanning six decades.
+@pytest.mark.parametrize("m,n,k", [(6, 1, 256), (15, 17, 256), (16, 33, 1280), (17, 16, 4352),
+                                   (32, 15, 768), (7, 4096, 4096), (24, 500, 2048),
+                                   (6, 8200, 512), (20, 8192, 256)])
+def test_gemv_flush_edges(q4k, m, n, k):
+    w = synth.q4k_weights(n, k, seed=m + n)
+    x = synth.normal_f32((m, k), seed=m + n)
+    y = q4k.gemv(dev(w), dev(x)).cpu().numpy()
+    yr, a = oracle.gemv(w, x, n, k)
+    assert_within(y, yr, a, GEMV_TOL, "flush gemv m=%d %dx%d" % (m, n, k))
+
+
+def test_gemv_flush_wide_dynamic_range(q4k):
+    m, n, k = 8, 64, 1024
+    w = synth.q4k_weights(n, k, seed=77)
+    g = synth.rng(77, synth.X)
+    x = (synth.normal_f32((m, k), seed=77) * 10.0 ** g.uniform(-3, 3, (m, k))).astype(np.float32)
+    y = q4k.gemv(dev(w), dev(x)).cpu().numpy()
+    yr, a = oracle.gemv(w, x, n, k)
+    assert_within(y, yr, a, GEMV_TOL, "flush gemv, x over six decades")
