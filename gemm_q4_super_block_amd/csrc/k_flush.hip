@@ -1,5 +1,5 @@
-// k_flush.hip -- Q4_K GEMV for batches of 6 to 32 rows on bf16 MFMA, with the
-// sub-block scales flushed into the fp32 accumulator.
+// k_flush.hip -- Q4_K and Q5_K GEMV for batches of 6 to 32 rows on bf16 MFMA,
+// with the sub-block scales flushed into the fp32 accumulator.
 //
 // What it computes is q4k_gemv's y = x W^T (fp32 x, fp32 y, the same
 // tolerance).  The method is the daScript PR page's scale flush ("CPU kernel
@@ -11,8 +11,9 @@
 //
 // Design for gfx950:
 //   * v_mfma_f32_16x16x32_bf16: one MFMA is exactly one sub-block (K = 32)
-//     for 16 batch rows (M) and 16 weight rows (N).  The quants q = 0..15 are
-//     exact in bf16.  fp32 x is split into x_hi = bf16(x) and x_lo = bf16(x -
+//     for 16 batch rows (M) and 16 weight rows (N).  The quants (0..15, or
+//     0..31 for Q5_K with the fifth bit from the high-bit plane) are exact in
+//     bf16.  fp32 x is split into x_hi = bf16(x) and x_lo = bf16(x -
 //     x_hi): every product q x_hi, q x_lo is exact in the fp32 accumulator and
 //     x_hi + x_lo is within 2^-17 |x| of x, so the result has fp32-GEMV
 //     accuracy, not bf16 accuracy.
@@ -68,7 +69,20 @@ __device__ __forceinline__ void split_bf16(const float (&v)[8], bf16x8_t& hi, bf
   lo = __builtin_bit_cast(bf16x8_t, uint4{l[0], l[1], l[2], l[3]});
 }
 
-template <int MT, int NT>
+// bf16x8 of 8 five-bit quants: the nibbles of q (low or high half) with the
+// fifth bits taken from bit `bit` of the 8 high-bit bytes h.
+template <bool HIGH>
+__device__ __forceinline__ bf16x8_t quants5_bf16(uint2 q, uint2 h, int bit) {
+  const uint32_t a = (HIGH ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu) |
+                     (((h.x >> bit) & 0x01010101u) << 4);
+  const uint32_t b = (HIGH ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu) |
+                     (((h.y >> bit) & 0x01010101u) << 4);
+  const uint4 v{pack_bf16x2(ubyte_f32(a, 0), ubyte_f32(a, 1)), pack_bf16x2(ubyte_f32(a, 2), ubyte_f32(a, 3)),
+                pack_bf16x2(ubyte_f32(b, 0), ubyte_f32(b, 1)), pack_bf16x2(ubyte_f32(b, 2), ubyte_f32(b, 3))};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int MT, int NT, int FMT>
 __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ w,
                                                     const float* __restrict__ x,
                                                     float* __restrict__ y, int m, int n, int k) {
@@ -83,7 +97,7 @@ __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ 
   const uint8_t* wrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    wrow[t] = w + static_cast<size_t>(min(n0 + 16 * t + nl, n - 1)) * nb * kBlockBytes;
+    wrow[t] = w + static_cast<size_t>(min(n0 + 16 * t + nl, n - 1)) * nb * block_bytes<FMT>();
   // Batch rows this lane feeds as the A operand; rows past m read row m - 1 and
   // are zeroed.
   const float* xrow[MT];
@@ -101,17 +115,23 @@ __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ 
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = f4v_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // Q5_K: the 8 high-bit bytes qh[8 kg ..] of the lane's k serve all four
+  // groups (bit 2g for the low nibbles, 2g + 1 for the high ones).
+  constexpr int kQOff = FMT == 5 ? kQ5QuantOffset : 16;
   struct WBlock {
     uint4 hd[NT];
     uint2 q[NT][4];
+    uint2 qh[NT];
   };
   auto load_w = [&](int b, WBlock& wb) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const uint8_t* p = wrow[t] + static_cast<size_t>(b) * kBlockBytes;
+      const uint8_t* p = wrow[t] + static_cast<size_t>(b) * block_bytes<FMT>();
       wb.hd[t] = *reinterpret_cast<const uint4*>(p);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) wb.q[t][g] = *reinterpret_cast<const uint2*>(p + 16 + 32 * g + 8 * kg);
+      for (int g = 0; g < 4; ++g)
+        wb.q[t][g] = *reinterpret_cast<const uint2*>(p + kQOff + 32 * g + 8 * kg);
+      if constexpr (FMT == 5) wb.qh[t] = *reinterpret_cast<const uint2*>(p + kQ5HighOffset + 8 * kg);
     }
   };
 
@@ -148,8 +168,14 @@ __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ 
         const GroupScales sc = group_scales(cur.hd[nt], g);
         // d sc without the fp8 widening factor (exact: a power of two)
         const float dlo = sc.a_lo * (1.0f / kNibbleUnscale), dhi = sc.a_hi * (1.0f / kNibbleUnscale);
-        const bf16x8_t blo = nibbles_bf16<false>(cur.q[nt][g]);
-        const bf16x8_t bhi = nibbles_bf16<true>(cur.q[nt][g]);
+        bf16x8_t blo, bhi;
+        if constexpr (FMT == 5) {
+          blo = quants5_bf16<false>(cur.q[nt][g], cur.qh[nt], 2 * g);
+          bhi = quants5_bf16<true>(cur.q[nt][g], cur.qh[nt], 2 * g + 1);
+        } else {
+          blo = nibbles_bf16<false>(cur.q[nt][g]);
+          bhi = nibbles_bf16<true>(cur.q[nt][g]);
+        }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           f4v_t plo = {0.0f, 0.0f, 0.0f, 0.0f}, phi = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -199,34 +225,49 @@ __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ 
 
 bool gemv_flush_supported(int64_t m) { return m >= kGemvFlushMinM && m <= 32; }
 
+namespace {
+
 // One 16-row batch tile for m <= 16, two above.  Matrices of at least
 // kFlushWideRows rows give each workgroup two 16-row weight tiles (x's split
 // and its sums shared by both; measured 1.4-1.6x faster at 14336 rows, slower
 // at 4096, where the grid would drop to 128 workgroups).
 constexpr int kFlushWideRows = 8192;
 
-template <int MT, int NT>
+template <int MT, int NT, int FMT>
 void launch_flush_tiles(const uint8_t* w, const float* x, float* y, int m, int n, int k,
                         hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemv_flush<MT, NT>), dim3((n + 16 * NT - 1) / (16 * NT)), dim3(256), 0,
-                     stream, w, x, y, m, n, k);
+  hipLaunchKernelGGL((k_gemv_flush<MT, NT, FMT>), dim3((n + 16 * NT - 1) / (16 * NT)), dim3(256),
+                     0, stream, w, x, y, m, n, k);
 }
 
-hipError_t launch_gemv_flush(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
-                             int64_t k, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_flush_fmt(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                            int64_t k, hipStream_t stream) {
   const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
   if (ni >= kFlushWideRows) {
     if (mi <= 16)
-      launch_flush_tiles<1, 2>(w, x, y, mi, ni, ki, stream);
+      launch_flush_tiles<1, 2, FMT>(w, x, y, mi, ni, ki, stream);
     else
-      launch_flush_tiles<2, 2>(w, x, y, mi, ni, ki, stream);
+      launch_flush_tiles<2, 2, FMT>(w, x, y, mi, ni, ki, stream);
   } else {
     if (mi <= 16)
-      launch_flush_tiles<1, 1>(w, x, y, mi, ni, ki, stream);
+      launch_flush_tiles<1, 1, FMT>(w, x, y, mi, ni, ki, stream);
     else
-      launch_flush_tiles<2, 1>(w, x, y, mi, ni, ki, stream);
+      launch_flush_tiles<2, 1, FMT>(w, x, y, mi, ni, ki, stream);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_flush(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                             int64_t k, hipStream_t stream) {
+  return launch_flush_fmt<4>(w, x, y, m, n, k, stream);
+}
+
+hipError_t launch_q5k_gemv_flush(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+                                 int64_t k, hipStream_t stream) {
+  return launch_flush_fmt<5>(w, x, y, m, n, k, stream);
 }
 
 }  // namespace q4k

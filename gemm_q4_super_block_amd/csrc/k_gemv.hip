@@ -443,8 +443,8 @@ hipError_t launch_gemv_passes(const uint8_t* w, const float* x, float* y, int64_
 
 }  // namespace
 
-// Q4_K batches from kGemvFlushMinM rows take the scale-flush MFMA kernel
-// (k_flush.hip); smaller ones, and Q5_K, the fp32 FMA passes.
+// Batches from kGemvFlushMinM rows take the scale-flush MFMA kernel
+// (k_flush.hip); smaller ones the fp32 FMA passes.
 hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream) {
   if (gemv_flush_supported(m)) return launch_gemv_flush(w, x, y, m, n, k, stream);
@@ -453,6 +453,7 @@ hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, in
 
 hipError_t launch_q5k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                            int64_t k, hipStream_t stream) {
+  if (gemv_flush_supported(m)) return launch_q5k_gemv_flush(w, x, y, m, n, k, stream);
   return launch_gemv_passes<5>(w, x, y, m, n, k, stream);
 }
 

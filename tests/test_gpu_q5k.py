@@ -174,3 +174,13 @@ def test_q5k_gemv_multi_chunk_k(q4k):
     y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
     yr, a = oracle.q5k_gemv(w, x, n, k)
     assert_within(y, yr[0], a[0], GEMV_TOL, "q5k gemv 300x20480")
+
+
+@pytest.mark.parametrize("m,n,k", [(6, 8200, 512), (17, 40, 1280), (32, 4096, 1024)])
+def test_q5k_gemv_flush_batches(q4k, m, n, k):
+    # batches of 6..32 rows take the scale-flush MFMA kernel (5-bit quants in bf16)
+    w = synth.q5k_weights(n, k, seed=m + 3)
+    x = synth.normal_f32((m, k), seed=m + 3)
+    y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
+    yr, a = oracle.q5k_gemv(w, x, n, k)
+    assert_within(y, yr, a, GEMV_TOL, "q5k flush gemv m=%d %dx%d" % (m, n, k))
