@@ -140,18 +140,28 @@ __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ 
   if (b < nb) load_w(b, cur);
   for (; b < nb; b += 4) {
     if (b + 4 < nb) load_w(b + 4, nxt);
+    // x of the whole super-block, this lane's 8 k of each of its 8 sub-blocks:
+    // issued together so that one L2 round trip serves the four quant groups.
+    float4 xr[MT][8][2];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int sb = 0; sb < 8; ++sb) {
+        const float* p = xrow[t] + 256 * b + 32 * sb + 8 * kg;
+        xr[t][sb][0] = *reinterpret_cast<const float4*>(p);
+        xr[t][sb][1] = *reinterpret_cast<const float4*>(p + 4);
+      }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // x of sub-blocks 2g (s = 0) and 2g + 1 (s = 1), this lane's 8 k of each
+      // x of sub-blocks 2g (s = 0) and 2g + 1 (s = 1)
       bf16x8_t ahi[MT][2], alo[MT][2];
       f4v_t sx[MT][2];
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const float* p = xrow[t] + 256 * b + 64 * g + 32 * s + 8 * kg;
-          const float4 u = *reinterpret_cast<const float4*>(p);
-          const float4 v = *reinterpret_cast<const float4*>(p + 4);
+          const float4 u = xr[t][2 * g + s][0];
+          const float4 v = xr[t][2 * g + s][1];
           float xv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
           if (!xvalid[t]) {
 #pragma unroll
