@@ -37,7 +37,8 @@
 //     owns units lane and lane + 64; it issues the chunk's weight loads first,
 //     then x is staged once per workgroup in LDS and each lane copies its
 //     units' x values and 8-sums into registers, reused for both rows.
-//     Batches run one x row per launch.
+//     Batches run in passes of up to 4 x rows: each unit's quants are widened
+//     once per pass and serve every x row.
 //   * Dequant export: one thread per unit, fp32 = (d sc) * (q - OFF) (the
 //     exact weight rounded once) or its bf16 (nearest even).
 #include <hip/hip_runtime.h>
@@ -167,76 +168,93 @@ struct Planes<3> {
   }
 };
 
-// WAVES waves per workgroup, RPW rows per wave.
-template <int FMT, int WAVES, int RPW>
+// WAVES waves per workgroup, RPW rows per wave, up to MT rows of x per pass
+// (mrows of them used): each unit's quants are decoded and widened once and
+// serve every x row.
+template <int FMT, int WAVES, int RPW, int MT>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_planes(const uint8_t* __restrict__ w,
                                                             const float* __restrict__ x,
-                                                            float* __restrict__ y, int n, int k) {
+                                                            float* __restrict__ y, int n, int k,
+                                                            int mrows) {
   using P = Planes<FMT>;
-  constexpr int kPlaneRowsPerWave = RPW;
-  __shared__ __attribute__((aligned(16))) float xs[kPlaneChunk];
+  __shared__ __attribute__((aligned(16))) float xs[MT][kPlaneChunk];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * WAVES + wave) * kPlaneRowsPerWave;
+  const int row0 = (blockIdx.x * WAVES + wave) * RPW;
   const size_t row_bytes = static_cast<size_t>(k >> 8) * P::Bytes;
-  const uint8_t* rows[kPlaneRowsPerWave];
+  const uint8_t* rows[RPW];
 #pragma unroll
-  for (int r = 0; r < kPlaneRowsPerWave; ++r)
+  for (int r = 0; r < RPW; ++r)
     rows[r] = w + static_cast<size_t>(min(row0 + r, n - 1)) * row_bytes;
-  float acc[kPlaneRowsPerWave];
+  float acc[MT][RPW];
 #pragma unroll
-  for (int r = 0; r < kPlaneRowsPerWave; ++r) acc[r] = 0.0f;
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[i][r] = 0.0f;
 
   for (int c0 = 0; c0 < k; c0 += kPlaneChunk) {
     const int kc = min(kPlaneChunk, k - c0);  // a multiple of 256
     const int units = kc >> 5;                // 8 per block
     // Units past a short chunk's end re-read its last unit (not accumulated).
-    typename P::Raw raw[kPlaneUnitsPerLane][kPlaneRowsPerWave];
+    typename P::Raw raw[kPlaneUnitsPerLane][RPW];
 #pragma unroll
     for (int t = 0; t < kPlaneUnitsPerLane; ++t) {
       const int u = min(lane + 64 * t, units - 1);
       const int bg = (c0 >> 8) + (u >> 3);
 #pragma unroll
-      for (int r = 0; r < kPlaneRowsPerWave; ++r)
+      for (int r = 0; r < RPW; ++r)
         raw[t][r] = P::load(rows[r] + static_cast<size_t>(bg) * P::Bytes, (u >> 2) & 1, u & 3);
     }
     __syncthreads();  // the previous chunk's reads of xs are done
-    for (int i = 4 * static_cast<int>(threadIdx.x); i < kc; i += 4 * 64 * WAVES)
-      *reinterpret_cast<float4*>(xs + i) = *reinterpret_cast<const float4*>(x + c0 + i);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i >= mrows) break;
+      for (int e = 4 * static_cast<int>(threadIdx.x); e < kc; e += 4 * 64 * WAVES)
+        *reinterpret_cast<float4*>(&xs[i][e]) =
+            *reinterpret_cast<const float4*>(x + static_cast<size_t>(i) * k + c0 + e);
+    }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < kPlaneUnitsPerLane; ++t) {
       const int u = lane + 64 * t;
       if (u >= units) continue;
       const int bl = u >> 3, h = (u >> 2) & 1, c = u & 3;
-      float xv[4][8], s8[4];
+      PlaneUnit wu[RPW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) wu[r] = P::decode(raw[t][r], h, c);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float* p = xs + 256 * bl + 128 * h + 32 * j + 8 * c;
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        xv[j][0] = a.x; xv[j][1] = a.y; xv[j][2] = a.z; xv[j][3] = a.w;
-        xv[j][4] = b.x; xv[j][5] = b.y; xv[j][6] = b.z; xv[j][7] = b.w;
-        s8[j] = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
-      }
+        float qf[RPW][8];
 #pragma unroll
-      for (int r = 0; r < kPlaneRowsPerWave; ++r) {
-        const PlaneUnit wu = P::decode(raw[t][r], h, c);
+        for (int r = 0; r < RPW; ++r)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float dot = 0.0f;
+          for (int e = 0; e < 8; ++e) qf[r][e] = ubyte_f32(wu[r].q[j][e >> 2], e & 3);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) dot = fmaf(ubyte_f32(wu.q[j][e >> 2], e & 3), xv[j][e], dot);
-          acc[r] = fmaf(wu.dsc[j], fmaf(-P::Off, s8[j], dot), acc[r]);
+        for (int i = 0; i < MT; ++i) {
+          if (i >= mrows) break;
+          const float* p = &xs[i][256 * bl + 128 * h + 32 * j + 8 * c];
+          const float4 a = *reinterpret_cast<const float4*>(p);
+          const float4 b = *reinterpret_cast<const float4*>(p + 4);
+          const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          const float s8 = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf(qf[r][e], xv[e], dot);
+            acc[i][r] = fmaf(wu[r].dsc[j], fmaf(-P::Off, s8, dot), acc[i][r]);
+          }
         }
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < kPlaneRowsPerWave; ++r) {
-    const float v = wave_sum(acc[r]);
-    if (lane == 0 && row0 + r < n) y[row0 + r] = v;
-  }
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float v = wave_sum(acc[i][r]);
+      if (lane == 0 && i < mrows && row0 + r < n) y[static_cast<size_t>(i) * n + row0 + r] = v;
+    }
 }
 
 // One thread per unit of the matrix (8 per block, blocks in row-major order).
@@ -268,15 +286,26 @@ __global__ __launch_bounds__(256) void k_dequant_planes(const uint8_t* __restric
   }
 }
 
+// Batches run in passes of up to 4 x rows (W is streamed once per pass).
 template <int FMT, int WAVES = 8, int RPW = 2>
 hipError_t launch_gemv_planes(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                               int64_t k, hipStream_t stream) {
   const int ni = static_cast<int>(n), ki = static_cast<int>(k);
   const int rows_per_wg = WAVES * RPW;
   const dim3 grid(static_cast<unsigned>((ni + rows_per_wg - 1) / rows_per_wg));
-  for (int64_t i = 0; i < m; ++i) {
-    hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW>), grid, dim3(64 * WAVES), 0, stream, w,
-                       x + i * k, y + i * n, ni, ki);
+  for (int64_t i0 = 0; i0 < m; i0 += 4) {
+    const int mm = static_cast<int>(m - i0 < 4 ? m - i0 : 4);
+    const float* xs = x + i0 * k;
+    float* ys = y + i0 * n;
+    if (mm == 1)
+      hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, 1>), grid, dim3(64 * WAVES), 0, stream,
+                         w, xs, ys, ni, ki, mm);
+    else if (mm == 2)
+      hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, 2>), grid, dim3(64 * WAVES), 0, stream,
+                         w, xs, ys, ni, ki, mm);
+    else
+      hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, 4>), grid, dim3(64 * WAVES), 0, stream,
+                         w, xs, ys, ni, ki, mm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

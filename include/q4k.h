@@ -196,7 +196,7 @@ int q5k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
 
 /* Decode GEMV on Q6_K weights: as q4k_gemv (same x, y, m, n, k, tolerance
  * and errors) with w a Q6_K matrix [n, k], 16-byte aligned.  A batch (m > 1)
- * streams W once per x row. */
+ * streams W once per 4 x rows. */
 int q6k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
 
@@ -224,7 +224,7 @@ int q6k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
 
 /* Decode GEMV on Q3_K weights: as q4k_gemv (same x, y, m, n, k, tolerance
  * and errors) with w a Q3_K matrix [n, k], 16-byte aligned.  A batch (m > 1)
- * streams W once per x row. */
+ * streams W once per 4 x rows. */
 int q3k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
 

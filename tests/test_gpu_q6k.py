@@ -74,7 +74,10 @@ def assert_within(got, ref, scale, what):
     (37, 768, 1, 2),        # odd blocks per row, ragged row tile
     (100, 8448, 1, 3),      # three x chunks, the last one block wide
     (14336, 4096, 1, 4),    # tall
-    (300, 1280, 3, 5),      # a batch
+    (300, 1280, 3, 5),      # a batch (one pass of up to 4 x rows)
+    (64, 512, 5, 7),        # two passes: 4 + 1
+    (50, 4352, 8, 8),       # two full passes, x past one chunk
+    (17, 256, 2, 9),        # a pass of 2
 ])
 def test_q6k_gemv(q4k, n, k, m, seed):
     w = synth.q6k_weights(n, k, seed=seed)
