@@ -49,6 +49,8 @@ SIGNATURES = {
     "q6k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q6k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q3k_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q6k_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q3k_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q3k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q3k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "w8a8_linear": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -199,3 +201,11 @@ def q3k_dequantize_f32(w, out, n, k, stream) -> int:
 
 def q3k_dequantize_bf16(w, out, n, k, stream) -> int:
     return load().q3k_dequantize_bf16(w, out, n, k, stream)
+
+
+def q6k_gemm(w, x_bf16, y, m, n, k, stream) -> int:
+    return load().q6k_gemm(w, x_bf16, y, m, n, k, stream)
+
+
+def q3k_gemm(w, x_bf16, y, m, n, k, stream) -> int:
+    return load().q3k_gemm(w, x_bf16, y, m, n, k, stream)

@@ -1,5 +1,5 @@
 // k_planes.hip -- the k-quants that keep their high bits in a separate plane,
-// Q6_K and Q3_K: decode GEMV and the dequant export.
+// Q6_K and Q3_K: decode GEMV, prefill GEMM and the dequant export.
 //
 // Formats (the daScript PR page "CPU kernel parity: decode and tile kernels
 // at llama.cpp speed ..." names "k6" and "k3": their high bits live in planes
@@ -26,8 +26,10 @@
 //     dword boundary (the matrix itself is 16-byte aligned).  Every field read
 //     sits at a multiple of 4 inside the block: it is read as the aligned
 //     dwords below it (one more when the block is 2 bytes off) and
-//     v_alignbyte shifts the bytes into place.  No read leaves the block; d
-//     is one 16-bit load.
+//     v_alignbyte shifts the bytes into place.  A read starts at most 2 bytes
+//     before its field (the previous block's tail: a block 2 bytes off is
+//     never the matrix's first) and ends at most 2 bytes past it, inside the
+//     block; d is one 16-bit load.
 //   * The scale multiplies sums of 8 weights: per unit and j the GEMV forms
 //     dot = sum q x and s8 = sum x in fp32 and adds (d sc) (dot - OFF s8)
 //     (OFF = 32 or 4), so the quant offset costs one FMA per 8 weights.
@@ -287,6 +289,259 @@ __global__ __launch_bounds__(256) void k_dequant_planes(const uint8_t* __restric
 }
 
 // Batches run in passes of up to 4 x rows (W is streamed once per pass).
+// ------------------------------------------------------------ prefill GEMM
+// Y = X W^T with X bf16 [m, k], fp32 Y, on v_mfma_f32_32x32x16_bf16: the
+// tile kernel of the Q4_K path (128 weight rows per tile, K steps of 64
+// weights, the step's weight tile dequantized to bf16 in a double-buffered LDS
+// tile, X fragments straight from global memory, split K with fp32 atomics
+// when the tile grid is small), with a plane-format tile fill.  Fill thread
+// (row t / 2, half f = t % 2) of step s (part s' = s % 4 of super-block s / 4)
+// decodes the 32 weights 64 s' + 32 f + l (l = 0..31) of its row, i.e. h = s'/2,
+// j = 2 (s' % 2) + f: one 32-byte low-bit field and one 32-byte high-bit field
+// (aligned dwords plus a byte shift, as in the GEMV), two sub-block scales
+// and d; each weight (d sc) (q - OFF) rounded once to fp32, then to bf16.
+constexpr int kPBN = 128;      // weight rows per tile
+constexpr int kPBK = 64;       // weights per K step
+constexpr int kPLds = 72;      // bf16 per LDS row: 64 + 8 pad
+
+template <int FMT>
+struct PlaneFill {
+  uint32_t lo[9], hi[9];  // low-bit field (ql / qs), high-bit field (qh / hmask)
+  uint32_t sc[4];         // the scale bytes of the half (Q6_K: 8) or all 12 (Q3_K)
+  uint32_t d, s;
+};
+
+template <int FMT>
+__device__ __forceinline__ void plane_fill_load(const uint8_t* blk, int sp, int f,
+                                                PlaneFill<FMT>& r) {
+  const int h = sp >> 1, j = 2 * (sp & 1) + f;
+  r.s = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(blk) & 3u);
+  if constexpr (FMT == 6) {
+    load_field<8>(blk + 64 * h + 32 * (j & 1), r.s, r.lo);
+    load_field<8>(blk + 128 + 32 * h, r.s, r.hi);
+    uint32_t t[3];
+    load_field<2>(blk + 192 + 8 * h, r.s, t);
+    r.sc[0] = t[0]; r.sc[1] = t[1]; r.sc[2] = t[2]; r.sc[3] = 0u;
+    r.d = *reinterpret_cast<const uint16_t*>(blk + 208);
+  } else {
+    load_field<8>(blk + 32 + 32 * h, r.s, r.lo);
+    load_field<8>(blk, r.s, r.hi);
+    load_field<3>(blk + 96, r.s, r.sc);
+    r.d = *reinterpret_cast<const uint16_t*>(blk + 108);
+  }
+}
+
+// 32 bf16 weights (l = 0..31 of group j of half h) into out[16] (pairs).
+template <int FMT>
+__device__ __forceinline__ void plane_fill_decode(const PlaneFill<FMT>& r, int sp, int f,
+                                                  uint32_t (&out)[16]) {
+  const int h = sp >> 1, j = 2 * (sp & 1) + f;
+  uint32_t L[8], H[8];
+  align_field<8>(r.lo, r.s, L);
+  align_field<8>(r.hi, r.s, H);
+  const float d = half_bits_to_float(r.d);
+  float dsc[2];
+  if constexpr (FMT == 6) {
+    uint32_t S[2];
+    align_field<2>(*reinterpret_cast<const uint32_t(*)[3]>(r.sc), r.s, S);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int b = 2 * j + cb;  // sub-block 8h + 2j + cb
+      dsc[cb] = d * static_cast<float>(static_cast<int8_t>(((b < 4 ? S[0] : S[1]) >> (8 * (b & 3))) & 0xFFu));
+    }
+  } else {
+    uint32_t S[3];
+    align_field<3>(r.sc, r.s, S);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int b = 2 * j + cb;
+      const uint32_t low4 = ((b < 4 ? S[0] : S[1]) >> (8 * (b & 3) + 4 * h)) & 15u;
+      const uint32_t top2 = (S[2] >> (8 * (b & 3) + 2 * (2 * h + (j >> 1)))) & 3u;
+      dsc[cb] = d * static_cast<float>(static_cast<int>(low4 | (top2 << 4)) - 32);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {  // dword e: weights l = 4e .. 4e + 3
+    uint32_t q;
+    if constexpr (FMT == 6)
+      q = (((j < 2) ? L[e] : (L[e] >> 4)) & 0x0F0F0F0Fu) | (((H[e] >> (2 * j)) & 0x03030303u) << 4);
+    else
+      q = ((L[e] >> (2 * j)) & 0x03030303u) | (((H[e] >> (4 * h + j)) & 0x01010101u) << 2);
+    const float sv = dsc[e >> 2];
+    const float off = Planes<FMT>::Off;
+    out[2 * e] = pack_bf16x2(sv * (ubyte_f32(q, 0) - off), sv * (ubyte_f32(q, 1) - off));
+    out[2 * e + 1] = pack_bf16x2(sv * (ubyte_f32(q, 2) - off), sv * (ubyte_f32(q, 3) - off));
+  }
+}
+
+template <int FMT, int WAVES_M, int WAVES_N, int TI, int TJ>
+__global__ __launch_bounds__(256, 2) void k_gemm_planes(const uint8_t* __restrict__ w,
+                                                        const uint16_t* __restrict__ x,
+                                                        float* __restrict__ y, int m, int n, int k,
+                                                        int steps_per_split, int atomic_out) {
+  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  static_assert(WAVES_N * 32 * TJ == kPBN, "the tile fill covers 128 weight rows");
+  constexpr int BM = WAVES_M * 32 * TI;
+  constexpr int BB = Planes<FMT>::Bytes;
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][kPBN * kPLds];
+  typedef float f16v_t __attribute__((ext_vector_type(16)));
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int half = lane >> 5;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kPBN;
+  const int nb = k >> 8;
+  const int steps = k / kPBK;
+  const int s_begin = blockIdx.z * steps_per_split;
+  const int s_end = min(steps, s_begin + steps_per_split);
+  if (s_begin >= s_end) return;  // uniform over the workgroup, before any barrier
+
+  const int f_row = t >> 1, f_hh = t & 1;
+  const uint8_t* f_base = w + static_cast<size_t>(min(n0 + f_row, n - 1)) * nb * BB;
+  const uint16_t* a_ptr[TI];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int row = min(m0 + wm * 32 * TI + 32 * i + (lane & 31), m - 1);
+    a_ptr[i] = x + static_cast<size_t>(row) * k + 32 * half;
+  }
+  f16v_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Loads past the last step re-read the last step (results unused).
+  auto load_w = [&](int s, PlaneFill<FMT>& r) {
+    const int sc = min(s, s_end - 1);
+    plane_fill_load<FMT>(f_base + static_cast<size_t>(sc >> 2) * BB, sc & 3, f_hh, r);
+  };
+  auto load_x = [&](int s, uint4 (&xr)[TI][4]) {
+    const int sc = min(s, s_end - 1);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const uint16_t* p = a_ptr[i] + static_cast<size_t>(sc) * kPBK;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xr[i][c] = *reinterpret_cast<const uint4*>(p + 8 * c);
+    }
+  };
+  auto store_w = [&](int buf, int s, const PlaneFill<FMT>& r) {
+    uint32_t v[16];
+    plane_fill_decode<FMT>(r, s & 3, f_hh, v);
+    uint16_t* dst = &ws[buf][f_row * kPLds + 32 * f_hh];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(dst + 8 * q) = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  };
+  auto mfma_step = [&](int buf, const uint4 (&xr)[TI][4]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8_t bfr[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int nrow = wn * 32 * TJ + 32 * j + (lane & 31);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&ws[buf][nrow * kPLds + 32 * half + 8 * kk]);
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, xr[i][kk]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // The Q4_K tile kernel's pipeline: at step s the MFMAs read LDS buffer s % 2
+  // and X registers set s % 2 while the weights of step s + 1 are decoded into
+  // the other buffer and step s + 2's X fragments and raw weights are fetched.
+  uint4 xA[TI][4], xB[TI][4];
+  PlaneFill<FMT> wA, wB;
+  load_w(s_begin, wA);
+  load_x(s_begin, xA);
+  load_x(s_begin + 1, xB);
+  store_w(0, s_begin, wA);
+  load_w(s_begin + 1, wB);
+  load_w(s_begin + 2, wA);
+  __syncthreads();
+  for (int s = s_begin; s < s_end; s += 2) {
+    mfma_step(0, xA);
+    load_x(s + 2, xA);
+    if (s + 1 < s_end) store_w(1, s + 1, wB);
+    load_w(s + 3, wB);
+    __syncthreads();
+    if (s + 1 >= s_end) break;
+    mfma_step(1, xB);
+    load_x(s + 3, xB);
+    if (s + 2 < s_end) store_w(0, s + 2, wA);
+    load_w(s + 4, wA);
+    __syncthreads();
+  }
+
+  // Accumulator r of a 32x32 tile holds row 8*(r/4) + 4*half + r%4, column lane%32.
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int col = n0 + wn * 32 * TJ + 32 * j + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 32 * TI + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (row < m && col < n) {
+          float* dst = y + static_cast<size_t>(row) * n + col;
+          if (atomic_out)
+            unsafeAtomicAdd(dst, acc[i][j][r]);
+          else
+            *dst = acc[i][j][r];
+        }
+      }
+    }
+}
+
+// Zero fill for split-K outputs (a kernel, not a memset node, so that a
+// captured graph replays it faithfully).
+__global__ __launch_bounds__(256) void k_zero_planes(float* __restrict__ y, size_t count) {
+  const size_t i = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i + 4 <= count) {
+    *reinterpret_cast<f4_t*>(y + i) = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  } else {
+    for (size_t e = i; e < count; ++e) y[e] = 0.0f;
+  }
+}
+
+template <int FMT, int WAVES_M, int WAVES_N, int TI, int TJ>
+hipError_t launch_gemm_planes_tiles(const uint8_t* w, const uint16_t* x, float* y, int m, int n,
+                                    int k, hipStream_t stream) {
+  constexpr int BM = WAVES_M * 32 * TI;
+  const int tiles_m = (m + BM - 1) / BM, tiles_n = (n + kPBN - 1) / kPBN;
+  const int steps = k / kPBK;
+  // Split K until the grid reaches one workgroup per CU (256 on MI355X).
+  int splits = 1;
+  while (tiles_m * tiles_n * splits * 2 <= 256 && splits * 2 <= steps / 8) splits *= 2;
+  const int per = (steps + splits - 1) / splits;
+  splits = (steps + per - 1) / per;
+  if (splits > 1) {
+    const size_t count = static_cast<size_t>(m) * n;
+    hipLaunchKernelGGL(k_zero_planes, dim3(static_cast<unsigned>((count / 4 + 256) / 256)), dim3(256),
+                       0, stream, y, count);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_gemm_planes<FMT, WAVES_M, WAVES_N, TI, TJ>), dim3(tiles_n, tiles_m, splits),
+                     dim3(256), 0, stream, w, x, y, m, n, k, per, splits > 1 ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_gemm_planes(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                              int64_t k, hipStream_t stream) {
+  const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
+  if (mi <= 32) return launch_gemm_planes_tiles<FMT, 1, 4, 1, 1>(w, x, y, mi, ni, ki, stream);
+  return launch_gemm_planes_tiles<FMT, 4, 1, 1, 4>(w, x, y, mi, ni, ki, stream);
+}
+
 template <int FMT, int WAVES = 8, int RPW = 2>
 hipError_t launch_gemv_planes(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                               int64_t k, hipStream_t stream) {
@@ -335,6 +590,15 @@ hipError_t launch_q6k_dequant_f32(const uint8_t* w, float* out, int64_t n, int64
 hipError_t launch_q6k_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64_t k,
                                    hipStream_t stream) {
   return launch_dequant_planes<6, true>(w, out, n, k, stream);
+}
+
+hipError_t launch_q6k_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                           int64_t k, hipStream_t stream) {
+  return launch_gemm_planes<6>(w, x, y, m, n, k, stream);
+}
+hipError_t launch_q3k_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                           int64_t k, hipStream_t stream) {
+  return launch_gemm_planes<3>(w, x, y, m, n, k, stream);
 }
 
 hipError_t launch_q3k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,

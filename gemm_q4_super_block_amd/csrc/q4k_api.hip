@@ -204,6 +204,22 @@ int q5k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m, int64_t
                   "q5k_gemm");
 }
 
+int q6k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (int rc = gemm_checks("q6k_gemm", w, x_bf16, y, m, n, k, 210u)) return rc;
+  return launched(q4k::launch_q6k_gemm(static_cast<const uint8_t*>(w), x_bf16, y, m, n, k,
+                                       static_cast<hipStream_t>(stream)),
+                  "q6k_gemm");
+}
+
+int q3k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m, int64_t n, int64_t k,
+             void* stream) {
+  if (int rc = gemm_checks("q3k_gemm", w, x_bf16, y, m, n, k, 110u)) return rc;
+  return launched(q4k::launch_q3k_gemm(static_cast<const uint8_t*>(w), x_bf16, y, m, n, k,
+                                       static_cast<hipStream_t>(stream)),
+                  "q3k_gemm");
+}
+
 int q4k_swiglu_mlp(const void* w_gate, const void* w_up, const void* w_down, const float* x,
                    float* h, float* out, int64_t d_model, int64_t d_ff, void* stream) {
   if (!w_gate || !w_up || !w_down || !x || !h || !out)

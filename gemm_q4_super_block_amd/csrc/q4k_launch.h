@@ -59,7 +59,7 @@ hipError_t launch_q5k_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, i
 hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);
 
-// Q6_K (210-byte blocks): GEMV (one launch per x row) and the dequant exports.
+// Q6_K (210-byte blocks): GEMV (passes of up to 4 x rows) and the dequant exports.
 hipError_t launch_q6k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                            int64_t k, hipStream_t stream);
 hipError_t launch_q6k_dequant_f32(const uint8_t* w, float* out, int64_t n, int64_t k,
@@ -67,7 +67,13 @@ hipError_t launch_q6k_dequant_f32(const uint8_t* w, float* out, int64_t n, int64
 hipError_t launch_q6k_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, int64_t k,
                                    hipStream_t stream);
 
-// Q3_K (110-byte blocks): GEMV (one launch per x row) and the dequant exports.
+// Prefill GEMMs on the plane formats (X bf16 [m, k], fp32 Y).
+hipError_t launch_q6k_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                           int64_t k, hipStream_t stream);
+hipError_t launch_q3k_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                           int64_t k, hipStream_t stream);
+
+// Q3_K (110-byte blocks): GEMV (passes of up to 4 x rows) and the dequant exports.
 hipError_t launch_q3k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                            int64_t k, hipStream_t stream);
 hipError_t launch_q3k_dequant_f32(const uint8_t* w, float* out, int64_t n, int64_t k,

@@ -79,6 +79,16 @@ def q5k_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) 
     return _gemm(w, x, out, Q5K_BLOCK_BYTES, _lib.q5k_gemm)
 
 
+def q6k_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm() for a Q6_K W (uint8 [n, k/256*210])."""
+    return _gemm(w, x, out, Q6K_BLOCK_BYTES, _lib.q6k_gemm)
+
+
+def q3k_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm() for a Q3_K W (uint8 [n, k/256*110])."""
+    return _gemm(w, x, out, Q3K_BLOCK_BYTES, _lib.q3k_gemm)
+
+
 def _gemm(w, x, out, block, fn):
     n, k = _q4k_shape(w, block)
     _dev_tensor(x, torch.bfloat16, "x")

@@ -200,6 +200,13 @@ int q5k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
 int q6k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
 
+/* Prefill GEMM on Q6_K weights: as q4k_gemm (same x_bf16, y, m, n, k,
+ * tolerance and errors) with w a Q6_K matrix [n, k], 16-byte aligned.  Each
+ * step's weight tile is dequantized to bf16 in LDS (the exact weight rounded
+ * to fp32, then to bf16), with split K on small grids. */
+int q6k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m,
+             int64_t n, int64_t k, void* stream);
+
 /* Diagnostic dequantization of a Q6_K matrix: as q4k_dequantize_f32 / _bf16
  * (exact weight rounded once to fp32; bf16 = nearest even of that). */
 int q6k_dequantize_f32(const void* w, float* out, int64_t n, int64_t k,
@@ -227,6 +234,10 @@ int q6k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
  * streams W once per 4 x rows. */
 int q3k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
+
+/* Prefill GEMM on Q3_K weights: as q6k_gemm with w a Q3_K matrix [n, k]. */
+int q3k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m,
+             int64_t n, int64_t k, void* stream);
 
 /* Diagnostic dequantization of a Q3_K matrix (the exact weight in fp32; bf16 =
  * nearest even of that). */

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
                  "q4k_dequantize_f32", "q4k_dequantize_bf16", "q4k_device_name", "q4k_version",
                  "q5k_gemv", "q5k_gemm", "q5k_dequantize_f32", "q5k_dequantize_bf16",
                  "q6k_gemv", "q6k_dequantize_f32", "q6k_dequantize_bf16", "q3k_gemv",
-                 "q3k_dequantize_f32", "q3k_dequantize_bf16", "w8a8_linear", "w8a8_linear_acc", "w8a8_dequant_epilogue", "w8a8_quantize_rows"):
+                 "q3k_dequantize_f32", "q3k_dequantize_bf16", "q6k_gemm", "q3k_gemm",
+                 "w8a8_linear", "w8a8_linear_acc", "w8a8_dequant_epilogue", "w8a8_quantize_rows"):
         assert name in syms
 
 
@@ -238,3 +239,13 @@ def test_q3k_rejects_bad_arguments():
     assert _lib.q3k_dequantize_bf16(A, 2 * A + 2, 4, 256, None) == _lib.Q4K_ERR_ALIGN
     assert _lib.q3k_dequantize_f32(A, A + 432, 4, 256, None) == _lib.Q4K_ERR_INVALID_ARG  # out in w
     assert _lib.q4k_last_error().startswith("q3k_dequantize_f32")
+
+
+def test_plane_gemms_reject_bad_arguments():
+    for name, blk in (("q6k_gemm", 210), ("q3k_gemm", 110)):
+        fn = getattr(_lib, name)
+        assert fn(0, A, 2 * A, 8, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+        assert _lib.q4k_last_error().startswith(name)
+        assert fn(A, 2 * A, 3 * A, 8, 16, 300, None) == _lib.Q4K_ERR_INVALID_ARG
+        assert fn(A + 2, 2 * A, 3 * A, 8, 16, 256, None) == _lib.Q4K_ERR_ALIGN
+        assert fn(A, 2 * A, A + 16 * blk - 16, 8, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG  # y in w

@@ -101,3 +101,36 @@ def test_q3k_gemv_unit_vectors(q4k):
         x[c] = 1.0
         y = q4k.q3k_gemv(dev(w), dev(x)).cpu().numpy()
         np.testing.assert_allclose(y, W[:, c], rtol=0, atol=1e-6 * np.abs(W[:, c]).max())
+
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 128, 256), (8, 520, 1024), (32, 384, 768), (64, 200, 512),
+                                   (130, 257, 1280)])
+def test_q3k_gemm_full_output(q4k, m, n, k):
+    # split-K grids (small tiles) and full ones, ragged tiles, odd block counts per row
+    w = synth.q3k_weights(n, k, seed=m + n)
+    xb = synth.normal_bf16((m, k), seed=m + n)
+    y = q4k.q3k_gemm(dev(w), _dev_bf16(xb)).cpu().numpy()
+    x64 = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    W = oracle.q3k_dequant_f32(w, n, k).astype(np.float64)
+    ref = x64 @ W.T
+    a = np.abs(x64) @ np.abs(W).T
+    err = np.abs(y - ref)
+    assert (err <= 1e-2 * a).all(), "q3k_gemm %dx%dx%d: worst %g" % (m, n, k, (err / (1e-2 * a)).max())
+
+
+def test_q3k_gemm_prefill_shape_sampled(q4k):
+    m, n, k = 512, 4096, 4096
+    w = synth.q3k_weights(n, k, seed=3)
+    xb = synth.normal_bf16((m, k), seed=3)
+    y = q4k.q3k_gemm(dev(w), _dev_bf16(xb)).cpu().numpy()
+    cols = np.arange(0, n, 97)
+    x64 = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    W = oracle.q3k_dequant_f32(w[cols], len(cols), k).astype(np.float64)
+    ref = x64 @ W.T
+    a = np.abs(x64) @ np.abs(W).T
+    assert (np.abs(y[:, cols] - ref) <= 1e-2 * a).all()
