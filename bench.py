@@ -69,7 +69,8 @@ def parse():
                    help="also run one device copy of 256 MiB (counter calibration)")
     p.add_argument("--only", default="",
                    help="comma list of kernels to run "
-                        "(gemv,q5k_gemv,q6k_gemv,q3k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,q5k_gemm,dequant,w8a8,"
+                        "(gemv,q5k_gemv,q6k_gemv,q3k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,q5k_gemm,q6k_gemm,q3k_gemm,"
+                        "dequant,w8a8,"
                         "read_probe)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
     p.add_argument("--eager-only", action="store_true",
@@ -256,6 +257,22 @@ def main():
             _lib.check(_lib.q5k_gemm(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
         kernels.append(("q5k_gemm_512x4096x4096", run_q5g, nbytes, 2 * m * n * k, rot))
 
+    # ---- prefill GEMM on the Q6_K and Q3_K sibling formats, M = 512, N = K = 4096
+    for fmt, gen, blk, fn in (("q6k", synth.q6k_weights, Q6K_BLOCK, _lib.q6k_gemm),
+                              ("q3k", synth.q3k_weights, Q3K_BLOCK, _lib.q3k_gemm)):
+        if not want(fmt + "_gemm"):
+            continue
+        m, n, k = 512, D_MODEL, D_MODEL
+        xb = synth.normal_bf16((m, k), seed=0)
+        w = gen(n, k, seed=0)
+        nbytes = n * (k // 256) * blk + 2 * m * k + 4 * m * n
+        rot = Rotor(torch, [w, xb.view(np.int16), np.zeros((m, n), np.float32)], nbytes)
+
+        def run_pg(i, sp, rot=rot, m=m, n=n, k=k, fn=fn):
+            wd, xd, yd = rot[i]
+            _lib.check(fn(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), m, n, k, sp))
+        kernels.append(("%s_gemm_512x4096x4096" % fmt, run_pg, nbytes, 2 * m * n * k, rot))
+
     # ---- dequant export (bf16) of the 4096 x 4096 matrix
     if want("dequant"):
         n = k = D_MODEL
@@ -367,7 +384,7 @@ def main():
             r["hbm_frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
         if flop:
             r["tflops"] = round(flop / (us * 1e-6) / 1e12, 2)
-        if name.startswith("gemm_") or name.startswith("sweep_gemm") or name.startswith("q5k_gemm"):
+        if name.startswith("gemm_") or name.startswith("sweep_gemm") or name[3:].startswith("k_gemm"):
             r["mfma_frac"] = round(r["tflops"] / BF16_PEAK_TFLOPS, 4)
         if name.startswith("w8a8_linear"):
             r["tops"] = r.pop("tflops")
@@ -557,6 +574,13 @@ def dispatch_workload(name, threads, lds, hint=""):
         return ("q%sk_gemv_4096x4096" % gp[0]) if threads == 4096 // 16 * 512 else "planes_other"
     if "k_dequant_planes" in name:
         return "planes_dequant"
+    pg = _template_args(name, "k_gemm_planes")
+    if pg:
+        # <FMT, WAVES_M, WAVES_N, TI, TJ>: 128 x 128 tiles, split K in two at M = 512
+        big = pg[1:] == ("4", "1", "1", "4")
+        return ("q%sk_gemm_512x4096x4096" % pg[0]) if big and threads == 128 * 2 * 256 else "planes_other"
+    if "k_zero_planes" in name:
+        return "split_k_zero_fill"
     wg = _template_args(name, "k_w8a8_gemm")
     if wg:
         # <TI, TJ, S, OUT>: 128 x 128 tiles of the 3072-wide output, 256 threads each
@@ -716,6 +740,13 @@ def spot_check(kernels, args, np, torch):
             w, xb, y = (a.cpu().numpy() for a in t)
             cols = np.arange(0, 4096, 256)
             yr, a = oracle.q5k_gemm_cols(w, xb.view(np.uint16), 4096, 4096, cols)
+            res[name] = float((np.abs(y[:, cols] - yr) / (1e-2 * a)).max())
+        elif name in ("q6k_gemm_512x4096x4096", "q3k_gemm_512x4096x4096"):
+            w, xb, y = (a.cpu().numpy() for a in t)
+            cols = np.arange(0, 4096, 256)
+            x = (xb.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+            rows_fn = oracle.q6k_gemv_rows if name.startswith("q6k") else oracle.q3k_gemv_rows
+            yr, a = rows_fn(w, x, 4096, 4096, cols)  # bf16 X is exact in fp32
             res[name] = float((np.abs(y[:, cols] - yr) / (1e-2 * a)).max())
         elif name.startswith("gemm_512"):
             w, xb, y = (a.cpu().numpy() for a in t)
