@@ -360,17 +360,27 @@ __device__ __forceinline__ void plane_fill_decode(const PlaneFill<FMT>& r, int s
       dsc[cb] = d * static_cast<float>(static_cast<int>(low4 | (top2 << 4)) - 32);
     }
   }
+  // Per dword: the low bits shifted to bits 0.. of each byte, the high bits
+  // rotated to their place above them (the bits a rotation carries across
+  // bytes are masked off), merged with one AND-OR.  Q6_K: low nibble at
+  // shift 4 (j / 2), high bits 2j, 2j + 1 to bits 4, 5 (rotate right by
+  // 2j - 4); Q3_K: bits 2j, 2j + 1 to 0, 1, hmask bit 4h + j to bit 2.
+  const uint32_t lshift = FMT == 6 ? 4u * static_cast<uint32_t>(j >> 1) : 2u * static_cast<uint32_t>(j);
+  const uint32_t hrot = FMT == 6 ? static_cast<uint32_t>(2 * j + 28) & 31u
+                                 : static_cast<uint32_t>(4 * h + j + 30) & 31u;
+  constexpr uint32_t lmask = FMT == 6 ? 0x0F0F0F0Fu : 0x03030303u;
+  constexpr uint32_t hmask = FMT == 6 ? 0x30303030u : 0x04040404u;
+  // (d sc) (q - OFF) = fma(d sc, q, -(d sc) OFF): OFF is a power of two, so
+  // (d sc) OFF is exact and the FMA rounds the exact weight once, as the
+  // subtract-then-multiply form does.
+  const float off = Planes<FMT>::Off;
+  const float nb0 = -(dsc[0] * off), nb1 = -(dsc[1] * off);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {  // dword e: weights l = 4e .. 4e + 3
-    uint32_t q;
-    if constexpr (FMT == 6)
-      q = (((j < 2) ? L[e] : (L[e] >> 4)) & 0x0F0F0F0Fu) | (((H[e] >> (2 * j)) & 0x03030303u) << 4);
-    else
-      q = ((L[e] >> (2 * j)) & 0x03030303u) | (((H[e] >> (4 * h + j)) & 0x01010101u) << 2);
-    const float sv = dsc[e >> 2];
-    const float off = Planes<FMT>::Off;
-    out[2 * e] = pack_bf16x2(sv * (ubyte_f32(q, 0) - off), sv * (ubyte_f32(q, 1) - off));
-    out[2 * e + 1] = pack_bf16x2(sv * (ubyte_f32(q, 2) - off), sv * (ubyte_f32(q, 3) - off));
+    const uint32_t q = ((L[e] >> lshift) & lmask) | (__builtin_amdgcn_alignbit(H[e], H[e], hrot) & hmask);
+    const float sv = dsc[e >> 2], nb = e < 4 ? nb0 : nb1;
+    out[2 * e] = pack_bf16x2(__builtin_fmaf(sv, ubyte_f32(q, 0), nb), __builtin_fmaf(sv, ubyte_f32(q, 1), nb));
+    out[2 * e + 1] = pack_bf16x2(__builtin_fmaf(sv, ubyte_f32(q, 2), nb), __builtin_fmaf(sv, ubyte_f32(q, 3), nb));
   }
 }
 
