@@ -126,3 +126,68 @@ def test_graph_split_k_replay_matches_oracle(q4k):
         torch.cuda.synchronize()
         got = y.cpu().numpy()[:, cols].astype(np.float64)
         assert np.all(np.abs(got - Yr) <= 1e-2 * A)
+
+
+def test_graph_sibling_formats_and_w8a8_replay(q4k):
+    # The other families under capture: the scale-flush GEMV, the Q5_K, Q6_K and
+    # Q3_K GEMVs (batched passes), their LDS-dequant GEMMs (split K with its
+    # zeroing kernel, and without), the dequant exports, and the INT8 layer and
+    # row quantizer.  Outputs allocated inside the capture live in the graph's
+    # pool and are rewritten by every replay.
+    ops = []  # (name, outputs, exact)
+    caps = []  # run() -> outputs, called once eagerly and once under capture
+
+    def add(name, run, exact=True):
+        caps.append((name, run, exact))
+
+    n, k = 2048, 1024
+    for fmt, gen, gv in (("q4k", synth.q4k_weights, q4k.gemv), ("q5k", synth.q5k_weights, q4k.q5k_gemv),
+                         ("q6k", synth.q6k_weights, q4k.q6k_gemv), ("q3k", synth.q3k_weights, q4k.q3k_gemv)):
+        w = dev(gen(n, k, seed=61))
+        for m in (1, 6, 9):
+            x = dev(synth.normal_f32((m, k), seed=60 + m))
+            add("%s gemv m=%d" % (fmt, m), lambda w=w, x=x, gv=gv: [gv(w, x)])
+    for fmt, gen, gm in (("q5k", synth.q5k_weights, q4k.q5k_gemm), ("q6k", synth.q6k_weights, q4k.q6k_gemm),
+                         ("q3k", synth.q3k_weights, q4k.q3k_gemm)):
+        for m, nn, kk in ((64, 1000, 1024), (300, 4096, 512)):   # split K; full grid
+            w = dev(gen(nn, kk, seed=m))
+            xb = dev_bf16(synth.normal_bf16((m, kk), seed=m))
+            add("%s gemm %dx%dx%d" % (fmt, m, nn, kk), lambda w=w, xb=xb, gm=gm: [gm(w, xb)], exact=m == 300)
+    for fmt, gen, dq in (("q6k", synth.q6k_weights, q4k.q6k_dequantize_bf16),
+                         ("q3k", synth.q3k_weights, q4k.q3k_dequantize_f32)):
+        w = dev(gen(256, 512, seed=3))
+        add("%s dequant" % fmt, lambda w=w, dq=dq: [dq(w)])
+    x8, xs, w8, ws, b = (dev(a) for a in synth.w8a8_case(256, 512, 1024, seed=5))
+    add("w8a8_linear", lambda: [q4k.w8a8_linear(x8, xs, w8, ws, b)])
+    xq = dev_bf16(synth.normal_bf16((64, 1024), seed=5))
+    add("w8a8_quantize_rows", lambda: list(q4k.w8a8_quantize_rows(xq)))
+
+    torch.cuda.synchronize()
+    eager = []
+    for name, run, _ in caps:
+        eager.append([t.clone() for t in run()])
+        torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    outs = []
+    with torch.cuda.graph(g):
+        for name, run, exact in caps:
+            outs.append(run())
+    torch.cuda.synchronize()
+
+    for replay in range(3):
+        for o in outs:
+            for t in o:
+                t.zero_() if not t.is_floating_point() else t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (name, _, exact), o, ref in zip(caps, outs, eager):
+            for t, r in zip(o, ref):
+                if exact or not t.is_floating_point():
+                    assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), \
+                        "%s: replay %d differs from the eager run" % (name, replay)
+                else:
+                    assert torch.isfinite(t).all(), "%s: replay %d left NaN" % (name, replay)
+                    tol = 1e-5 * r.abs().max().item() + 1e-30
+                    diff = (t - r).abs().max().item()
+                    assert diff <= tol, "%s: replay %d off by %g" % (name, replay, diff)
