@@ -451,7 +451,7 @@ def main():
         out["roofline_gemm"] = {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": gemm["mfma_frac"],
                                 "traffic": traffic("gemm_512x4096x4096"),
-                                "kernel": "k_gemm_q4k_kslice<2, 2>",
+                                "kernel": "k_gemm_q4k_kslice<2, 2, 4>",
                                 "flop_per_launch": 2 * 512 * 4096 * 4096}
     if w8:
         out["roofline_w8a8"] = {"bound": "mfma", "achieved": w8["tops"], "peak": INT8_PEAK_TOPS,
@@ -554,10 +554,16 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "dequant_bf16_4096x4096" if dq == ("true", "4") else "dequant_other"
     if "k_gemm_q4k_128x256" in name:
         return "gemm_512x14336x4096" if threads == 57344 else "gemm_other"
-    if "k_gemm_q4k_kslice<2, 2>" in name:
-        return "gemm_512x4096x4096" if threads == 131072 else "gemm_other"
-    if "k_gemm_q4k_kslice<1, 2>" in name:
-        return "sweep_gemm_14336x4096"
+    ks = _template_args(name, "k_gemm_q4k_kslice")
+    if ks:
+        # <TI, NJ, FMT>: 64 x 128 tiles (TI = 2) at m=512, n=4096; 32 x 64 (TI = 1) for m <= 32
+        if ks == ("2", "2", "4"):
+            return "gemm_512x4096x4096" if threads == 131072 else "gemm_other"
+        if ks == ("2", "2", "5"):
+            return "q5k_gemm_512x4096x4096" if threads == 131072 else "q5k_gemm_other"
+        if ks == ("1", "2", "4"):
+            return "sweep_gemm_14336x4096"
+        return "q5k_gemm_other"
     sk = _template_args(name, "k_gemm_q4k")
     if sk and len(sk) > 5 and sk[5] == "5":
         return "q5k_gemm_512x4096x4096"

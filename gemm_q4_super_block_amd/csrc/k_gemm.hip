@@ -535,23 +535,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __re
 //     quant bytes 16 b + 8 h .. +7.  Every weight is dequantized once per
 //     workgroup; the four K slices are summed through LDS at the end.
 //   * copies as in the 128 x 256 kernel: X (32 TI rows x 64 k) through a
-//     9-slot ring, whole 144-byte super-blocks of the weight rows through a
-//     4-slot ring issued three super-blocks ahead; per wave one X copy per step
-//     and NJ + 1 weight copies per super-block.
+//     9-slot ring, whole super-block records of the weight rows (144 bytes for
+//     Q4_K, 176 for Q5_K) through a 4- or 3-slot ring issued three super-blocks
+//     ahead; per wave one X copy per step and three weight copies per
+//     super-block.  Q5_K lanes also read the 8 high-bit bytes that match their
+//     quant bytes and widen 5-bit bytes exactly (v_cvt_f32_ubyte).
 //   * the sub-block scales of a super-block are decoded once per workgroup
 //     (thread t: row t / 4, group t % 4) into LDS; waves read the (a, b) pairs
 //     of their parity.
 //   * quant bytes are read two steps ahead of their dequantization, which runs
 //     under the MFMAs of the step before their use.
-template <int TI, int NJ>
+template <int TI, int NJ, int FMT = 4>
 struct KSlice {
   static constexpr int BM = 32 * TI, BN = 32 * NJ * TI, Threads = 256 * TI;
-  static constexpr int WCopies = NJ + 1;  // weight copies per wave per super-block
+  static constexpr int BB = block_bytes<FMT>();  // 144 (Q4_K) or 176 (Q5_K)
+  static constexpr int Units = BB / 16;          // 16-byte copy units per record
+  static constexpr int WaveUnits = 8 * NJ * Units;  // weight units copied per wave
+  static constexpr int WCopies = (WaveUnits + 63) / 64;  // copies per wave per super-block
   static constexpr int XSlot = BM * 128;
-  static constexpr int WSlot = BN * kBlockBytes;
+  static constexpr int WSlot = BN * BB;
   static constexpr int XSlots = 9;
+  // Slot S % WSlots holds super-block S.  Its last reads are at phase 1 of S and
+  // super-block S + 3 is copied at phase 3, so three slots suffice; Q4_K keeps
+  // a fourth (the LDS has room for it).
+  static constexpr int WSlots = FMT == 5 ? 3 : 4;
   static constexpr int WOff = XSlots * XSlot;
-  static constexpr int SOff = WOff + 4 * WSlot;
+  static constexpr int SOff = WOff + WSlots * WSlot;
   static constexpr int SSlot = 4 * BN * 16;  // [parity][group pair][row] x (a, b, a', b')
   static constexpr int Lds = SOff + 2 * SSlot;
   static constexpr int ExWave = TI * NJ * 4 * 1024;  // one wave's partial tile
@@ -564,13 +573,19 @@ struct XFragT {
   bf16x8_t a[TI];  // [M block]
 };
 
-template <int TI, int NJ>
+// A lane's quant bytes for one step: 8 quant bytes, and for Q5_K the 8
+// matching high-bit-plane bytes (unused for Q4_K).
+struct QBytes {
+  uint2 q, hb;
+};
+
+template <int TI, int NJ, int FMT = 4>
 __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* __restrict__ w,
                                                                  const uint16_t* __restrict__ x,
                                                                  float* __restrict__ y, int m,
                                                                  int n, int k, int tiles_m,
                                                                  int tiles_n, int xcd_gm) {
-  using C = KSlice<TI, NJ>;
+  using C = KSlice<TI, NJ, FMT>;
   constexpr int kColsPerWave = 32 * NJ;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::Lds];
   const int t = threadIdx.x;
@@ -586,7 +601,7 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   tile_coords(blockIdx.x, tiles_m, tiles_n, xcd_gm, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int nsb = k >> 8, nst = k >> 6;
-  const uint32_t row_bytes = static_cast<uint32_t>(nsb) * kBlockBytes;
+  const uint32_t row_bytes = static_cast<uint32_t>(nsb) * C::BB;
   const int sb_rot = (tn * 7) % nsb;
   auto phys_sb = [&](int S) {
     const int e = min(S, nsb - 1) + sb_rot;
@@ -599,16 +614,17 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
     const int c = (lane & 7) ^ swz(row);
     xsrc = x + static_cast<size_t>(min(m0 + row, m - 1)) * k + 8 * c;
   }
-  // Weight copies of this wave: 16-byte units 72 NJ wave + {0, 64, 80} + lane
-  // (NJ = 2) or {0, 8} + lane (NJ = 1) of the slot; the last copy repeats some
+  // Weight copies of this wave: 16-byte units WaveUnits wave + min(64 i,
+  // WaveUnits - 64) + lane of the slot (Q4_K, NJ = 2: 144 units from
+  // {0, 64, 80}; Q5_K: 176 from {0, 64, 112}); the last copy repeats some
   // units of the one before, with the same data and place.
-  constexpr int kUnit[3] = {0, NJ == 2 ? 64 : 8, 80};
+  auto unit0 = [](int i) { return min(64 * i, C::WaveUnits - 64); };
   uint32_t woff[C::WCopies];
 #pragma unroll
   for (int i = 0; i < C::WCopies; ++i) {
-    const int U = 72 * NJ * wave + kUnit[i] + lane;
-    const int col = (U * 7282) >> 16;  // U / 9 for U < 2304
-    woff[i] = static_cast<uint32_t>(min(n0 + col, n - 1)) * row_bytes + (U - col * 9) * 16;
+    const int U = C::WaveUnits * wave + unit0(i) + lane;
+    const int col = FMT == 5 ? U / C::Units : (U * 7282) >> 16;  // U / 9 for U < 2304
+    woff[i] = static_cast<uint32_t>(min(n0 + col, n - 1)) * row_bytes + (U - col * C::Units) * 16;
   }
   const uint32_t lds0 = lds_address(smem);
   auto copy_x = [&](int s, int slot) {
@@ -618,12 +634,12 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
                   __builtin_amdgcn_readfirstlane(lds0 + slot * C::XSlot + wave * 1024));
   };
   auto copy_w = [&](int S, int slot) {
-    const uint8_t* base = w + static_cast<size_t>(phys_sb(S)) * kBlockBytes;
+    const uint8_t* base = w + static_cast<size_t>(phys_sb(S)) * C::BB;
 #pragma unroll
     for (int i = 0; i < C::WCopies; ++i)
       copy16_to_lds(base + woff[i],
                     __builtin_amdgcn_readfirstlane(lds0 + C::WOff + slot * C::WSlot +
-                                                   (72 * NJ * wave + kUnit[i]) * 16));
+                                                   (C::WaveUnits * wave + unit0(i)) * 16));
   };
   auto read_x = [&](int slot, XFragT<TI>& A) {
     const uint8_t* xb = smem + slot * C::XSlot;
@@ -634,13 +650,19 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
       A.a[i] = *reinterpret_cast<const bf16x8_t*>(xb + r * 128 + ((ch ^ swz(r)) << 4));
     }
   };
-  auto read_q = [&](int slot, int g, uint2 (&Q)[NJ]) {
+  // Quant bytes r = 16 bh + 8 h + (0..7) of group g, and for Q5_K the same
+  // bytes of the high-bit plane (bit 2 g + parity is the fifth bit).
+  auto read_q = [&](int slot, int g, QBytes (&Q)[NJ]) {
     const uint8_t* wb = smem + C::WOff + slot * C::WSlot;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int col = kColsPerWave * wn + 32 * j + c32;
-      const uint4 v = *reinterpret_cast<const uint4*>(wb + col * kBlockBytes + 16 + 32 * g + 16 * bh);
-      Q[j] = h ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
+      const uint8_t* rec = wb + col * C::BB;
+      const uint4 v = *reinterpret_cast<const uint4*>(
+          rec + (FMT == 5 ? kQ5QuantOffset : 16) + 32 * g + 16 * bh);
+      Q[j].q = h ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
+      if constexpr (FMT == 5)
+        Q[j].hb = *reinterpret_cast<const uint2*>(rec + kQ5HighOffset + 16 * bh + 8 * h);
     }
   };
   auto scales_store = [&](int wslot, int ss) {
@@ -649,8 +671,12 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
     // so the step stays one basic block for the scheduling hints below.)
     if (C::Threads / 4 > C::BN && col >= C::BN) return;
     const uint4 hd =
-        *reinterpret_cast<const uint4*>(smem + C::WOff + wslot * C::WSlot + col * kBlockBytes);
-    const GroupScales gs = group_scales(hd, g);
+        *reinterpret_cast<const uint4*>(smem + C::WOff + wslot * C::WSlot + col * C::BB);
+    GroupScales gs = group_scales(hd, g);
+    if constexpr (FMT == 5) {  // 5-bit quants are widened as exact integers, not q * 2^-9
+      gs.a_lo *= 1.0f / kNibbleUnscale;
+      gs.a_hi *= 1.0f / kNibbleUnscale;
+    }
     uint8_t* sp = smem + C::SOff + ss * C::SSlot;
     *reinterpret_cast<f2_t*>(sp + ((g >> 1) * C::BN + col) * 16 + (g & 1) * 8) = f2_t{gs.a_lo, gs.b_lo};
     *reinterpret_cast<f2_t*>(sp + ((2 + (g >> 1)) * C::BN + col) * 16 + (g & 1) * 8) = f2_t{gs.a_hi, gs.b_hi};
@@ -671,10 +697,17 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
     }
   };
   const int nshift = 4 * par;
-  auto dequant = [&](const uint2 (&Q)[NJ], const float (&a)[NJ], const float (&b)[NJ],
+  auto dequant = [&](const QBytes (&Q)[NJ], int g, const float (&a)[NJ], const float (&b)[NJ],
                      bf16x8_t (&B)[NJ]) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) B[j] = dequant8_bf16(Q[j].x, Q[j].y, nshift, a[j], b[j]);
+    for (int j = 0; j < NJ; ++j) {
+      if constexpr (FMT == 5)
+        B[j] = __builtin_bit_cast(
+            bf16x8_t, dequant8_bf16_q5(q5_bytes(Q[j].q.x, Q[j].hb.x, nshift, 2 * g + par),
+                                       q5_bytes(Q[j].q.y, Q[j].hb.y, nshift, 2 * g + par), a[j], b[j]));
+      else
+        B[j] = dequant8_bf16(Q[j].q.x, Q[j].q.y, nshift, a[j], b[j]);
+    }
   };
   f16x_t acc[TI][NJ];
 #pragma unroll
@@ -704,7 +737,7 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   constexpr int CW = C::WCopies;
   wait_copies_barrier<8 + 2 * CW>();  // X(0), W(0) landed
   XFragT<TI> A0, A1;
-  uint2 Q0[NJ], Q1[NJ];
+  QBytes Q0[NJ], Q1[NJ];
   float sa[4][NJ], sb[4][NJ];
   scales_store(0, 0);
   read_q(0, 0, Q0);
@@ -713,7 +746,7 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   wait_copies_barrier<8 + 2 * CW>();
   scales_load(0, sa, sb);
   bf16x8_t B0[NJ], B1[NJ];
-  dequant(Q0, sa[0], sb[0], B0);
+  dequant(Q0, 0, sa[0], sb[0], B0);
 
   int xs = 0;  // X slot of step s
   int ws = 0;  // weight slot of super-block S
@@ -721,22 +754,22 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   // reads the X fragments of step s+1, the quant bytes of step s+2 (into Qb)
   // and at phase 2 decodes the scales of S+1; MFMAs of step s with Bc while
   // Bn = B(s+1) is dequantized from Qa, read one step earlier.
-  auto step = [&](int s, int p, XFragT<TI>& Ac, XFragT<TI>& An, uint2 (&Qa)[NJ], uint2 (&Qb)[NJ],
+  auto step = [&](int s, int p, XFragT<TI>& Ac, XFragT<TI>& An, QBytes (&Qa)[NJ], QBytes (&Qb)[NJ],
                   bf16x8_t (&Bc)[NJ], bf16x8_t (&Bn)[NJ]) {
     const int xn = xs == C::XSlots - 1 ? 0 : xs + 1;
-    const int ws1 = (ws + 1) & 3;
+    const int ws1 = C::WSlots == 4 ? (ws + 1) & 3 : (ws == C::WSlots - 1 ? 0 : ws + 1);
     copy_x(s + C::XSlots, xs);
-    if (p == 3) copy_w((s >> 2) + 3, (ws + 3) & 3);
+    if (p == 3) copy_w((s >> 2) + 3, C::WSlots == 4 ? (ws + 3) & 3 : ws);  // slot of S + 3
     read_x(xn, An);
     read_q(p < 2 ? ws : ws1, (p + 2) & 3, Qb);
     if (p == 2) scales_store(ws1, ((s >> 2) + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(Ac, Bc);
     if (p < 3) {
-      dequant(Qa, sa[p + 1], sb[p + 1], Bn);
+      dequant(Qa, p + 1, sa[p + 1], sb[p + 1], Bn);
     } else {
       scales_load(((s >> 2) + 1) & 1, sa, sb);
-      dequant(Qa, sa[0], sb[0], Bn);
+      dequant(Qa, 0, sa[0], sb[0], Bn);
     }
 #pragma unroll
     for (int q = 0; q < NJ * TI; ++q) {
@@ -853,15 +886,37 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
   return launch<4, 1, 1, 4, 2>(w, x, y, mi, ni, ki, splits_for(tiles, steps), stream);
 }
 
-// Q5_K: the tile kernel that dequantizes each step's weight tile into LDS (the
-// register-dequant kernels read Q4_K's 144-byte records), split K when the
-// tile grid is small.
+// Q5_K: the K-slice kernels on 176-byte records where their grids fill the
+// chip (as for Q4_K), else the tile kernel that dequantizes each step's weight
+// tile into LDS, split K when the tile grid is small.
 hipError_t launch_q5k_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                            int64_t k, hipStream_t stream) {
   const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
   const int steps = ki / kBK;
   const int tiles_n = (ni + kBN - 1) / kBN;
-  if (mi <= 32) return launch<1, 4, 1, 1, 2, 5>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
+  if (mi <= 32) {
+    using Small = KSlice<1, 2, 5>;
+    const int small_n = (ni + Small::BN - 1) / Small::BN;
+    if (small_n >= kGemmSmallTiles) {
+      hipLaunchKernelGGL((k_gemm_q4k_kslice<1, 2, 5>), dim3(small_n), dim3(Small::Threads), 0,
+                         stream, w, x, y, mi, ni, ki, 1, small_n, 0);
+      return hipGetLastError();
+    }
+    return launch<1, 4, 1, 1, 2, 5>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
+  }
+  // The K-slice tiles serve the grids between one and a few waves of
+  // workgroups; grids that Q4_K gives to its 128 x 256 tiles run faster on the
+  // LDS-dequant tiles here (512 x 14336 x 4096: 116 against 152 us).
+  using Mid = KSlice<2, 2, 5>;
+  const int mid_m = (mi + Mid::BM - 1) / Mid::BM, mid_n = (ni + Mid::BN - 1) / Mid::BN;
+  const int big_m = (mi + kWBM - 1) / kWBM, big_n = (ni + kWBN - 1) / kWBN;
+  const bool big_grid = mi >= 2 * kWBM && big_m * big_n >= kGemmBigTiles;
+  if (!big_grid && mid_m * mid_n >= kGemmMidTiles) {
+    hipLaunchKernelGGL((k_gemm_q4k_kslice<2, 2, 5>), dim3(mid_m * mid_n), dim3(Mid::Threads), 0,
+                       stream, w, x, y, mi, ni, ki, mid_m, mid_n,
+                       xcd_groups(mid_m, mid_n, Mid::BM, Mid::BN));
+    return hipGetLastError();
+  }
   const int tiles = ((mi + 127) / 128) * tiles_n;
   return launch<4, 1, 1, 4, 2, 5>(w, x, y, mi, ni, ki, splits_for(tiles, steps), stream);
 }
