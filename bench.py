@@ -414,7 +414,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_k weights, f32 activations and accumulation (GEMV); bf16 MFMA, f32 acc (GEMM)",
+        "dtype": "f32",
+        "dtype_detail": "the decode GEMV computes in f32 (Q4_K weights, f32 x, f32 FMA and "
+                        "accumulation); the prefill GEMM in bf16 MFMA with f32 accumulation",
         "data": "synthetic (seeded; Q4_K fields uniform, d/dmin |N(0,1)|*0.01, activations N(0,1))",
         "config": {
             "workload": "decode GEMV y = W x, W 4096 x 4096 Q4_K (9,437,184 B), x/y fp32, "
