@@ -18,7 +18,8 @@
 //     X and W rows (128 bytes each) from global memory straight into LDS
 //     (global_load_lds_dwordx4) through a ring of S slots, S - 1 steps ahead.
 //     LDS rows keep the XOR-swizzled chunk order of lds_copy.h.  The shipped
-//     128 x 128 tile with S = 2 holds 64 KiB, so two workgroups share a CU.
+//     tiles, 64 x 64 (small grids) and 128 x 128, with S = 2 hold 32 and
+//     64 KiB; two or more workgroups share a CU.
 //   * MFMA slice u (0..3) of a step, lane half h, covers k = 32 u + 16 h +
 //     (0..15) for both operands (the MFMA sums over k, so any common
 //     assignment is the same contraction): one conflict-free ds_read_b128 per
@@ -370,17 +371,35 @@ hipError_t launch_tiles(const int8_t* x, const int8_t* w, const float* xs, const
 
 }  // namespace
 
+namespace {
+
+// Tile shape per grid (3072 x 3072 weights): where 128 x 128 tiles would not
+// give every CU one (M = 512 / 1024: 96 / 192 tiles), 64 x 64 tiles (warm L2:
+// 13.0 / 18.2 us against 20.6 / 22.4; cold inputs at M = 1024: 23.7 against
+// 28.7); otherwise 128 x 128, whose operands are re-read least (cold inputs
+// at M = 8192: 106.5 us against 131 for 64 x 128, which was 1-4% faster on
+// warm ones).
+template <int OUT>
+hipError_t launch_w8a8(const int8_t* x, const int8_t* w, const float* xs, const float* ws,
+                       const float* bias, void* out, int64_t m, int64_t n, int64_t k,
+                       hipStream_t stream) {
+  const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
+  const int64_t tiles128 = ((m + 127) / 128) * ((n + 127) / 128);
+  if (tiles128 <= 256) return launch_tiles<1, 1, 2, OUT>(x, w, xs, ws, bias, out, mi, ni, ki, stream);
+  return launch_tiles<2, 2, 2, OUT>(x, w, xs, ws, bias, out, mi, ni, ki, stream);
+}
+
+}  // namespace
+
 hipError_t launch_w8a8_linear(const int8_t* x, const float* x_scale, const int8_t* w,
                               const float* w_scale, const float* bias, uint16_t* out, int64_t m,
                               int64_t n, int64_t k, hipStream_t stream) {
-  return launch_tiles<2, 2, 2, kW8Bf16>(x, w, x_scale, w_scale, bias, out, static_cast<int>(m),
-                                     static_cast<int>(n), static_cast<int>(k), stream);
+  return launch_w8a8<kW8Bf16>(x, w, x_scale, w_scale, bias, out, m, n, k, stream);
 }
 
 hipError_t launch_w8a8_linear_acc(const int8_t* x, const int8_t* w, int32_t* acc, int64_t m,
                                   int64_t n, int64_t k, hipStream_t stream) {
-  return launch_tiles<2, 2, 2, kW8Acc>(x, w, nullptr, nullptr, nullptr, acc, static_cast<int>(m),
-                                    static_cast<int>(n), static_cast<int>(k), stream);
+  return launch_w8a8<kW8Acc>(x, w, nullptr, nullptr, nullptr, acc, m, n, k, stream);
 }
 
 hipError_t launch_w8a8_epilogue(const int32_t* acc, uint16_t* out, const float* x_scale,
