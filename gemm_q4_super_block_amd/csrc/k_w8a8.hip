@@ -304,8 +304,48 @@ __global__ __launch_bounds__(256) void k_w8a8_epilogue(const int32_t* __restrict
 
 // Row quantizer: one wave per row of bf16 [rows, k] (k % 8 == 0): amax over
 // the row (wave max), scale = amax / 127, codes = clamp(rint(v / scale)).
-// Lane l handles the 8-element groups l, l + 64, ...; the second pass re-reads
-// the row (from cache) to keep register use independent of k.
+// Lane l handles the 8-element groups l, l + 64, ...  With G > 0 (k <= 512 G)
+// a lane loads all its groups at once and keeps them in registers for the
+// second pass; with G = 0 it walks the row twice (the second pass from cache),
+// for any k.
+__device__ __forceinline__ void bf16_pair(uint32_t v, float& lo, float& hi) {
+  lo = __builtin_bit_cast(float, v << 16);
+  hi = __builtin_bit_cast(float, v & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ float group_amax(uint4 v, float amax) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float lo, hi;
+    bf16_pair(u[e], lo, hi);
+    amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+  }
+  return amax;
+}
+
+// Codes of one 8-element group: rint(v / s) clamped to +-127 (0 when s = 0).
+__device__ __forceinline__ uint2 group_codes(uint4 v, float s) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float f[2];
+    bf16_pair(u[e], f[0], f[1]);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      int c = 0;
+      if (s != 0.0f) {
+        const float r = fminf(fmaxf(__builtin_rintf(__fdiv_rn(f[p], s)), -127.0f), 127.0f);
+        c = static_cast<int>(r);
+      }
+      packed[e >> 1] |= (static_cast<uint32_t>(c) & 0xFFu) << (8 * (2 * (e & 1) + p));
+    }
+  }
+  return uint2{packed[0], packed[1]};
+}
+
+template <int G>
 __global__ __launch_bounds__(256) void k_w8a8_quantize_rows(const uint16_t* __restrict__ x,
                                                             int8_t* __restrict__ q,
                                                             float* __restrict__ scale, int rows,
@@ -314,46 +354,35 @@ __global__ __launch_bounds__(256) void k_w8a8_quantize_rows(const uint16_t* __re
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // uniform per wave; no barrier below
   const uint16_t* xr = x + static_cast<size_t>(row) * k;
+  int8_t* qr = q + static_cast<size_t>(row) * k;
   const int groups = k >> 3;
-  auto widen = [](uint32_t v, float& lo, float& hi) {
-    lo = __builtin_bit_cast(float, v << 16);
-    hi = __builtin_bit_cast(float, v & 0xFFFF0000u);
-  };
   float amax = 0.0f;
-  for (int g = lane; g < groups; g += 64) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * g);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  uint4 v[G > 0 ? G : 1];
+  if constexpr (G > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float lo, hi;
-      widen(u[e], lo, hi);
-      amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+    for (int i = 0; i < G; ++i) {
+      const int g = lane + 64 * i;
+      v[i] = g < groups ? *reinterpret_cast<const uint4*>(xr + 8 * g) : uint4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int i = 0; i < G; ++i) amax = group_amax(v[i], amax);
+  } else {
+    for (int g = lane; g < groups; g += 64)
+      amax = group_amax(*reinterpret_cast<const uint4*>(xr + 8 * g), amax);
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
   const float s = __fdiv_rn(amax, 127.0f);
   if (lane == 0) scale[row] = s;
-  int8_t* qr = q + static_cast<size_t>(row) * k;
-  for (int g = lane; g < groups; g += 64) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * g);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-    uint32_t packed[2] = {0u, 0u};
+  if constexpr (G > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float f[2];
-      widen(u[e], f[0], f[1]);
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        int c = 0;
-        if (s != 0.0f) {
-          const float r = fminf(fmaxf(__builtin_rintf(__fdiv_rn(f[p], s)), -127.0f), 127.0f);
-          c = static_cast<int>(r);
-        }
-        packed[e >> 1] |= (static_cast<uint32_t>(c) & 0xFFu) << (8 * (2 * (e & 1) + p));
-      }
+    for (int i = 0; i < G; ++i) {
+      const int g = lane + 64 * i;
+      if (g < groups) *reinterpret_cast<uint2*>(qr + 8 * g) = group_codes(v[i], s);
     }
-    *reinterpret_cast<uint2*>(qr + 8 * g) = uint2{packed[0], packed[1]};
+  } else {
+    for (int g = lane; g < groups; g += 64)
+      *reinterpret_cast<uint2*>(qr + 8 * g) = group_codes(*reinterpret_cast<const uint4*>(xr + 8 * g), s);
   }
 }
 
@@ -422,9 +451,14 @@ hipError_t launch_w8a8_epilogue(const int32_t* acc, uint16_t* out, const float* 
 
 hipError_t launch_w8a8_quantize_rows(const uint16_t* x, int8_t* q, float* scale, int64_t rows,
                                      int64_t k, hipStream_t stream) {
-  const int r = static_cast<int>(rows);
-  hipLaunchKernelGGL(k_w8a8_quantize_rows, dim3((r + 3) / 4), dim3(256), 0, stream, x, q, scale,
-                     r, static_cast<int>(k));
+  const int r = static_cast<int>(rows), ki = static_cast<int>(k);
+  const dim3 grid((r + 3) / 4);
+  if (ki <= 64 * 8 * 8)
+    hipLaunchKernelGGL((k_w8a8_quantize_rows<8>), grid, dim3(256), 0, stream, x, q, scale, r, ki);
+  else if (ki <= 64 * 8 * 16)
+    hipLaunchKernelGGL((k_w8a8_quantize_rows<16>), grid, dim3(256), 0, stream, x, q, scale, r, ki);
+  else
+    hipLaunchKernelGGL((k_w8a8_quantize_rows<0>), grid, dim3(256), 0, stream, x, q, scale, r, ki);
   return hipGetLastError();
 }
 
