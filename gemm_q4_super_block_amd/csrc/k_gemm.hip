@@ -525,8 +525,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __re
 // ------------------------------------------------------------ K-slice tiles
 // (32 TI) x (32 NJ TI) output tiles with K split four ways inside the
 // workgroup, for grids that the 128 x 256 tiles cannot fill without splitting
-// K across workgroups (m=512, n=4096: TI=NJ=2, 256 tiles of 64 x 128; m <= 32,
-// n=14336: TI=1, NJ=2, 224 tiles of 32 x 64).  Splitting K across workgroups would need fp32 atomics (about one per
+// K across workgroups (m=512, n=4096: TI=NJ=2, 256 tiles of 64 x 128; m=256,
+// n=4096: TI=2, NJ=1, 256 tiles of 64 x 64; m <= 32, n=14336: TI=1, NJ=2, 224
+// tiles of 32 x 64).  Splitting K across workgroups would need fp32 atomics (about one per
 // L2 channel per clock, ~25 us for the m=512, n=4096 output) or a second pass.
 //   * 4 TI waves = 4 K slices x TI N halves.  Wave (kq, wn) owns all 32 TI
 //     rows x 32 NJ columns of its half (TI x NJ accumulators) and, in every 64-wide
@@ -879,6 +880,15 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
     hipLaunchKernelGGL((k_gemm_q4k_kslice<2, 2>), dim3(mid_m * mid_n), dim3(Mid::Threads), 0,
                        stream, w, x, y, mi, ni, ki, mid_m, mid_n,
                        xcd_groups(mid_m, mid_n, Mid::BM, Mid::BN));
+    return hipGetLastError();
+  }
+  using Quad = KSlice<2, 1>;
+  const int quad_m = (mi + Quad::BM - 1) / Quad::BM, quad_n = (ni + Quad::BN - 1) / Quad::BN;
+  if (quad_m * quad_n >= kGemmMidTiles) {
+    // 64 x 64 tiles (256 x 4096 x 4096: 23 us against 30 with split K).
+    hipLaunchKernelGGL((k_gemm_q4k_kslice<2, 1>), dim3(quad_m * quad_n), dim3(Quad::Threads), 0,
+                       stream, w, x, y, mi, ni, ki, quad_m, quad_n,
+                       xcd_groups(quad_m, quad_n, Quad::BM, Quad::BN));
     return hipGetLastError();
   }
   // 128 x 128 tiles, two workgroups per CU.

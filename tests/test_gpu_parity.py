@@ -258,10 +258,13 @@ def test_gemm_prefill_sampled(q4k, n):
 #     five M-tiles on the XCD order.
 #   64 x 128 tiles (>= 192 tiles): ragged M and N (325 tiles), N not a multiple
 #     of 128 with 192 tiles, M = 65 (a one-row last M-tile), 256 tiles at K = 4096.
+#   64 x 64 tiles (fewer than 192 of 64 x 128, >= 192 of 64 x 64): 256 tiles,
+#     ragged N with 196 tiles, a one-row last M-tile with 282 tiles.
 #   128 x 128 tiles with split K (fewer tiles): 64 and 32 tiles.
 @pytest.mark.parametrize("m,n,k", [(512, 8192, 256), (257, 16383, 768), (300, 16640, 512),
                                    (640, 12288, 1024), (300, 8200, 512), (384, 4000, 4096),
-                                   (65, 24576, 512), (512, 4096, 4096), (128, 4096, 1024),
+                                   (65, 24576, 512), (512, 4096, 4096), (256, 4096, 512),
+                                   (200, 3100, 768), (129, 6000, 256), (128, 4096, 1024),
                                    (64, 4000, 2048)])
 def test_gemm_tile_kernels(q4k, m, n, k):
     w = synth.q4k_weights(n, k, seed=m + k)
