@@ -927,6 +927,14 @@ hipError_t launch_q5k_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_
                        xcd_groups(mid_m, mid_n, Mid::BM, Mid::BN));
     return hipGetLastError();
   }
+  using Quad = KSlice<2, 1, 5>;
+  const int quad_m = (mi + Quad::BM - 1) / Quad::BM, quad_n = (ni + Quad::BN - 1) / Quad::BN;
+  if (!big_grid && quad_m * quad_n >= kGemmMidTiles) {
+    hipLaunchKernelGGL((k_gemm_q4k_kslice<2, 1, 5>), dim3(quad_m * quad_n), dim3(Quad::Threads), 0,
+                       stream, w, x, y, mi, ni, ki, quad_m, quad_n,
+                       xcd_groups(quad_m, quad_n, Quad::BM, Quad::BN));
+    return hipGetLastError();
+  }
   const int tiles = ((mi + 127) / 128) * tiles_n;
   return launch<4, 1, 1, 4, 2, 5>(w, x, y, mi, ni, ki, splits_for(tiles, steps), stream);
 }

@@ -187,12 +187,13 @@ def test_q5k_gemv_flush_batches(q4k, m, n, k):
 
 
 # Grids that take the K-slice kernels on 176-byte records: m <= 32 with at
-# least 128 tiles of 32 x 64, and m > 32 with at least 192 tiles of 64 x 128
-# (ragged M and N tiles, one to several super-blocks).  The result is the dot
+# least 128 tiles of 32 x 64, and m > 32 with at least 192 tiles of 64 x 128,
+# else of 64 x 64 (ragged M and N tiles, one to several super-blocks).  The result is the dot
 # of the bf16 X with the bf16 weights of the dequant export, up to fp32
 # summation order.
 @pytest.mark.parametrize("m,n,k", [(1, 8192, 1024), (5, 8200, 512), (32, 8192, 768),
-                                   (330, 4000, 512), (384, 4096, 256)])
+                                   (330, 4000, 512), (384, 4096, 256), (256, 4096, 512),
+                                   (129, 6000, 256)])
 def test_q5k_gemm_kslice_bf16_weight_dot(q4k, m, n, k):
     w = synth.q5k_weights(n, k, seed=m + 7)
     xb = synth.normal_bf16((m, k), seed=m + 7)
