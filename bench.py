@@ -384,7 +384,7 @@ def main():
             r["hbm_frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
         if flop:
             r["tflops"] = round(flop / (us * 1e-6) / 1e12, 2)
-        if name.startswith("gemm_") or name.startswith("sweep_gemm") or name[3:].startswith("k_gemm"):
+        if name.startswith("gemm_") or name.startswith("sweep_gemm") or name.startswith(("q5k_gemm", "q6k_gemm", "q3k_gemm")):
             r["mfma_frac"] = round(r["tflops"] / BF16_PEAK_TFLOPS, 4)
         if name.startswith("w8a8_linear"):
             r["tops"] = r.pop("tflops")
