@@ -115,8 +115,8 @@ def main():
         summarize_profile(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
-              "(the path shards by output rows, see DESIGN.md)" % args.gpus, file=sys.stderr)
+        print("bench.py: the benchmark runs on exactly one GPU; --gpus %d is not supported "
+              "(several GPUs would each hold a slice of the weight rows)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
