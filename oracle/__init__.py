@@ -18,6 +18,7 @@ import numpy as np
 from . import build as _build
 
 _lib = None
+_lib_omp = None
 
 _u8p = ctypes.POINTER(ctypes.c_uint8)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
@@ -33,87 +34,119 @@ def lib():
     if _lib is None:
         if not os.path.exists(_build.LIB):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
-        L.oracle_f16_to_f64.restype = ctypes.c_double
-        L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
-        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
-        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
-        L.oracle_bf16_to_f64.restype = ctypes.c_double
-        L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
-        L.oracle_silu.restype = ctypes.c_double
-        L.oracle_silu.argtypes = [ctypes.c_double]
-        L.oracle_quant.restype = ctypes.c_int
-        L.oracle_quant.argtypes = [_u8p, ctypes.c_int]
-        L.oracle_unpack_scales.restype = None
-        L.oracle_unpack_scales.argtypes = [_u8p, _u8p, _u8p]
-        L.oracle_dequant_block.restype = None
-        L.oracle_dequant_block.argtypes = [_u8p, _f32p]
-        L.oracle_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
-        L.oracle_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
-        L.oracle_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
-        L.oracle_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
-                                       _f64p, _f64p]
-        L.oracle_gemm.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _f64p, _f64p]
-        L.oracle_gemm_cols.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _i64p, _i64,
-                                       _f64p, _f64p]
-        L.oracle_swiglu_mlp.argtypes = [_u8p, _u8p, _u8p, _f32p, _i64, _i64,
-                                        _f64p, _f64p, _f64p, _f64p, _f64p, _f64p,
-                                        _f64p]
-        L.oracle_q5k_quant.restype = ctypes.c_int
-        L.oracle_q5k_quant.argtypes = [_u8p, _u8p, ctypes.c_int]
-        L.oracle_q5k_dequant_block.restype = None
-        L.oracle_q5k_dequant_block.argtypes = [_u8p, _f32p]
-        L.oracle_q5k_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
-        L.oracle_q5k_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
-        L.oracle_q5k_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
-        L.oracle_q5k_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
-                                           _f64p, _f64p]
-        L.oracle_q5k_gemm.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _f64p, _f64p]
-        L.oracle_q5k_gemm_cols.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _i64p, _i64,
-                                           _f64p, _f64p]
-        L.oracle_q3k_quant.restype = ctypes.c_int
-        L.oracle_q3k_quant.argtypes = [_u8p, ctypes.c_int]
-        L.oracle_q3k_scale.restype = ctypes.c_int
-        L.oracle_q3k_scale.argtypes = [_u8p, ctypes.c_int]
-        L.oracle_q3k_dequant_block.restype = None
-        L.oracle_q3k_dequant_block.argtypes = [_u8p, _f32p]
-        L.oracle_q3k_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
-        L.oracle_q3k_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
-        L.oracle_q3k_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
-        L.oracle_q3k_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
-                                           _f64p, _f64p]
-        L.oracle_q6k_quant.restype = ctypes.c_int
-        L.oracle_q6k_quant.argtypes = [_u8p, ctypes.c_int]
-        L.oracle_q6k_dequant_block.restype = None
-        L.oracle_q6k_dequant_block.argtypes = [_u8p, _f32p]
-        L.oracle_q6k_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
-        L.oracle_q6k_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
-        L.oracle_q6k_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
-        L.oracle_q6k_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
-                                           _f64p, _f64p]
-        _i8p = ctypes.POINTER(ctypes.c_int8)
-        _i32p = ctypes.POINTER(ctypes.c_int32)
-        L.oracle_w8a8_acc.argtypes = [_i8p, _i8p, _i64, _i64, _i64, _i32p]
-        L.oracle_w8a8_epilogue.argtypes = [_i32p, _f32p, _f32p, _f32p, _i64, _i64, _u16p,
-                                           _f32p]
-        L.oracle_w8a8_linear.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _i64, _i64, _i64,
-                                         _u16p]
-        L.oracle_w8a8_linear_cols.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _i64, _i64,
-                                              _i64, _i64p, _i64, _u16p]
-        L.oracle_w8a8_quantize_rows.argtypes = [_u16p, _i64, _i64, _i8p, _f32p]
-        for name in ("oracle_dequant_f32", "oracle_dequant_bf16", "oracle_gemv",
-                     "oracle_gemv_rows", "oracle_gemm", "oracle_gemm_cols",
-                     "oracle_swiglu_mlp", "oracle_q5k_dequant_f32", "oracle_q5k_dequant_bf16",
-                     "oracle_q5k_gemv", "oracle_q5k_gemv_rows", "oracle_q5k_gemm",
-                     "oracle_q5k_gemm_cols", "oracle_w8a8_acc", "oracle_w8a8_epilogue",
-                     "oracle_w8a8_linear", "oracle_w8a8_linear_cols",
-                     "oracle_w8a8_quantize_rows", "oracle_q6k_dequant_f32",
-                     "oracle_q6k_dequant_bf16", "oracle_q6k_gemv", "oracle_q6k_gemv_rows",
-                     "oracle_q3k_dequant_f32", "oracle_q3k_dequant_bf16", "oracle_q3k_gemv",
-                     "oracle_q3k_gemv_rows"):
-            getattr(L, name).restype = ctypes.c_int
-        _lib = L
+        _lib = _declare(ctypes.CDLL(_build.LIB))
     return _lib
+
+
+def lib_omp():
+    """liboracle_omp.so: the same oracle with its row loops on all host cores
+    (identical results); for the benchmark's all-cores CPU baseline."""
+    global _lib_omp
+    if _lib_omp is None:
+        if not os.path.exists(_build.LIB_OMP):
+            _build.build()
+        _lib_omp = _declare(ctypes.CDLL(_build.LIB_OMP))
+    return _lib_omp
+
+
+def _pick(omp: bool):
+    return lib_omp() if omp else lib()
+
+
+def threads(omp: bool = False) -> int:
+    """Threads the row loops of the chosen build use."""
+    return _pick(omp).oracle_threads()
+
+
+def _declare(L):
+    """Set the ctypes signatures of every oracle entry point on a loaded build."""
+    L.oracle_f16_to_f64.restype = ctypes.c_double
+    L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    L.oracle_bf16_to_f64.restype = ctypes.c_double
+    L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    L.oracle_silu.restype = ctypes.c_double
+    L.oracle_silu.argtypes = [ctypes.c_double]
+    L.oracle_quant.restype = ctypes.c_int
+    L.oracle_quant.argtypes = [_u8p, ctypes.c_int]
+    L.oracle_unpack_scales.restype = None
+    L.oracle_unpack_scales.argtypes = [_u8p, _u8p, _u8p]
+    L.oracle_dequant_block.restype = None
+    L.oracle_dequant_block.argtypes = [_u8p, _f32p]
+    L.oracle_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
+    L.oracle_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
+    L.oracle_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
+    L.oracle_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
+                                   _f64p, _f64p]
+    L.oracle_gemm.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _f64p, _f64p]
+    L.oracle_gemm_cols.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _i64p, _i64,
+                                   _f64p, _f64p]
+    L.oracle_swiglu_mlp.argtypes = [_u8p, _u8p, _u8p, _f32p, _i64, _i64,
+                                    _f64p, _f64p, _f64p, _f64p, _f64p, _f64p,
+                                    _f64p]
+    L.oracle_q5k_quant.restype = ctypes.c_int
+    L.oracle_q5k_quant.argtypes = [_u8p, _u8p, ctypes.c_int]
+    L.oracle_q5k_dequant_block.restype = None
+    L.oracle_q5k_dequant_block.argtypes = [_u8p, _f32p]
+    L.oracle_q5k_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
+    L.oracle_q5k_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
+    L.oracle_q5k_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
+    L.oracle_q5k_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
+                                       _f64p, _f64p]
+    L.oracle_q5k_gemm.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _f64p, _f64p]
+    L.oracle_q5k_gemm_cols.argtypes = [_u8p, _u16p, _i64, _i64, _i64, _i64p, _i64,
+                                       _f64p, _f64p]
+    L.oracle_q3k_quant.restype = ctypes.c_int
+    L.oracle_q3k_quant.argtypes = [_u8p, ctypes.c_int]
+    L.oracle_q3k_scale.restype = ctypes.c_int
+    L.oracle_q3k_scale.argtypes = [_u8p, ctypes.c_int]
+    L.oracle_q3k_dequant_block.restype = None
+    L.oracle_q3k_dequant_block.argtypes = [_u8p, _f32p]
+    L.oracle_q3k_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
+    L.oracle_q3k_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
+    L.oracle_q3k_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
+    L.oracle_q3k_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
+                                       _f64p, _f64p]
+    L.oracle_q6k_quant.restype = ctypes.c_int
+    L.oracle_q6k_quant.argtypes = [_u8p, ctypes.c_int]
+    L.oracle_q6k_dequant_block.restype = None
+    L.oracle_q6k_dequant_block.argtypes = [_u8p, _f32p]
+    L.oracle_q6k_dequant_f32.argtypes = [_u8p, _i64, _i64, _f32p]
+    L.oracle_q6k_dequant_bf16.argtypes = [_u8p, _i64, _i64, _u16p]
+    L.oracle_q6k_gemv.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _f64p, _f64p]
+    L.oracle_q6k_gemv_rows.argtypes = [_u8p, _f32p, _i64, _i64, _i64, _i64p, _i64,
+                                       _f64p, _f64p]
+    for f in ("q6k", "q3k"):
+        getattr(L, "oracle_%s_gemm" % f).argtypes = [_u8p, _u16p, _i64, _i64, _i64,
+                                                     _f64p, _f64p]
+        getattr(L, "oracle_%s_gemm_cols" % f).argtypes = [_u8p, _u16p, _i64, _i64, _i64,
+                                                          _i64p, _i64, _f64p, _f64p]
+    L.oracle_threads.restype = ctypes.c_int
+    L.oracle_threads.argtypes = []
+    _i8p = ctypes.POINTER(ctypes.c_int8)
+    _i32p = ctypes.POINTER(ctypes.c_int32)
+    L.oracle_w8a8_acc.argtypes = [_i8p, _i8p, _i64, _i64, _i64, _i32p]
+    L.oracle_w8a8_epilogue.argtypes = [_i32p, _f32p, _f32p, _f32p, _i64, _i64, _u16p,
+                                       _f32p]
+    L.oracle_w8a8_linear.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _i64, _i64, _i64,
+                                     _u16p]
+    L.oracle_w8a8_linear_cols.argtypes = [_i8p, _f32p, _i8p, _f32p, _f32p, _i64, _i64,
+                                          _i64, _i64p, _i64, _u16p]
+    L.oracle_w8a8_quantize_rows.argtypes = [_u16p, _i64, _i64, _i8p, _f32p]
+    for name in ("oracle_dequant_f32", "oracle_dequant_bf16", "oracle_gemv",
+                 "oracle_gemv_rows", "oracle_gemm", "oracle_gemm_cols",
+                 "oracle_swiglu_mlp", "oracle_q5k_dequant_f32", "oracle_q5k_dequant_bf16",
+                 "oracle_q5k_gemv", "oracle_q5k_gemv_rows", "oracle_q5k_gemm",
+                 "oracle_q5k_gemm_cols", "oracle_w8a8_acc", "oracle_w8a8_epilogue",
+                 "oracle_w8a8_linear", "oracle_w8a8_linear_cols",
+                 "oracle_w8a8_quantize_rows", "oracle_q6k_dequant_f32",
+                 "oracle_q6k_dequant_bf16", "oracle_q6k_gemv", "oracle_q6k_gemv_rows",
+                 "oracle_q3k_dequant_f32", "oracle_q3k_dequant_bf16", "oracle_q3k_gemv",
+                 "oracle_q3k_gemv_rows", "oracle_q6k_gemm", "oracle_q6k_gemm_cols",
+                 "oracle_q3k_gemm", "oracle_q3k_gemm_cols"):
+        getattr(L, name).restype = ctypes.c_int
+    return L
 
 
 def _p(a, t):
@@ -184,15 +217,16 @@ def dequant_bf16(w: np.ndarray, n: int, k: int) -> np.ndarray:
     return out
 
 
-def gemv(w: np.ndarray, x: np.ndarray, n: int, k: int):
-    """y, a = oracle GEMV; x is fp32 [m, k] (or [k]); returns fp64 [m, n]."""
+def gemv(w: np.ndarray, x: np.ndarray, n: int, k: int, omp: bool = False):
+    """y, a = oracle GEMV; x is fp32 [m, k] (or [k]); returns fp64 [m, n].
+    omp=True runs the all-cores build (identical results)."""
     w = _c(w, np.uint8)
     x = _c(x, np.float32).reshape(-1, k)
     m = x.shape[0]
     y = np.zeros((m, n), np.float64)
     a = np.zeros((m, n), np.float64)
-    _check(lib().oracle_gemv(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(y, _f64p),
-                             _p(a, _f64p)), "gemv")
+    _check(_pick(omp).oracle_gemv(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(y, _f64p),
+                                  _p(a, _f64p)), "gemv")
     return y, a
 
 
@@ -221,22 +255,24 @@ def gemm(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int):
     return y, a
 
 
-def gemm_cols(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int, cols):
-    """Oracle GEMM restricted to output columns ``cols``; returns [m, len(cols)]."""
+def gemm_cols(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int, cols, omp: bool = False):
+    """Oracle GEMM restricted to output columns ``cols``; returns [m, len(cols)].
+    omp=True runs the all-cores build (identical results)."""
     w = _c(w, np.uint8)
     x = _c(x_bf16, np.uint16).reshape(-1, k)
     cols = _c(cols, np.int64)
     m = x.shape[0]
     y = np.zeros((m, cols.size), np.float64)
     a = np.zeros((m, cols.size), np.float64)
-    _check(lib().oracle_gemm_cols(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(cols, _i64p),
-                                  cols.size, _p(y, _f64p), _p(a, _f64p)), "gemm_cols")
+    _check(_pick(omp).oracle_gemm_cols(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(cols, _i64p),
+                                       cols.size, _p(y, _f64p), _p(a, _f64p)), "gemm_cols")
     return y, a
 
 
-def swiglu_mlp(w_gate, w_up, w_down, x, d_model: int, d_ff: int):
+def swiglu_mlp(w_gate, w_up, w_down, x, d_model: int, d_ff: int, omp: bool = False):
     """Oracle SwiGLU MLP at one token.  Returns a dict of fp64 arrays:
-    g, ag, u, au, h (length d_ff) and out, aout (length d_model)."""
+    g, ag, u, au, h (length d_ff) and out, aout (length d_model).
+    omp=True runs the all-cores build (identical results)."""
     wg = _c(w_gate, np.uint8)
     wu = _c(w_up, np.uint8)
     wd = _c(w_down, np.uint8)
@@ -244,7 +280,7 @@ def swiglu_mlp(w_gate, w_up, w_down, x, d_model: int, d_ff: int):
     r = {name: np.zeros(d_ff, np.float64) for name in ("g", "ag", "u", "au", "h")}
     r["out"] = np.zeros(d_model, np.float64)
     r["aout"] = np.zeros(d_model, np.float64)
-    _check(lib().oracle_swiglu_mlp(
+    _check(_pick(omp).oracle_swiglu_mlp(
         _p(wg, _u8p), _p(wu, _u8p), _p(wd, _u8p), _p(x, _f32p), d_model, d_ff,
         _p(r["g"], _f64p), _p(r["ag"], _f64p), _p(r["u"], _f64p), _p(r["au"], _f64p),
         _p(r["h"], _f64p), _p(r["out"], _f64p), _p(r["aout"], _f64p)), "swiglu_mlp")
@@ -471,6 +507,33 @@ def q6k_gemv_rows(w: np.ndarray, x: np.ndarray, n: int, k: int, rows):
     return y, a
 
 
+def q6k_gemm(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int):
+    """Y, A = oracle GEMM on Q6_K weights; x_bf16 uint16 [m, k]; fp64 [m, n]."""
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * Q6K_BLOCK_BYTES
+    x = _c(x_bf16, np.uint16).reshape(-1, k)
+    m = x.shape[0]
+    y = np.zeros((m, n), np.float64)
+    a = np.zeros((m, n), np.float64)
+    _check(lib().oracle_q6k_gemm(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(y, _f64p),
+                                 _p(a, _f64p)), "q6k_gemm")
+    return y, a
+
+
+def q6k_gemm_cols(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int, cols):
+    """Oracle Q6_K GEMM at output columns ``cols``; returns [m, len(cols)]."""
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * Q6K_BLOCK_BYTES
+    x = _c(x_bf16, np.uint16).reshape(-1, k)
+    cols = _c(cols, np.int64)
+    m = x.shape[0]
+    y = np.zeros((m, cols.size), np.float64)
+    a = np.zeros((m, cols.size), np.float64)
+    _check(lib().oracle_q6k_gemm_cols(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(cols, _i64p),
+                                      cols.size, _p(y, _f64p), _p(a, _f64p)), "q6k_gemm_cols")
+    return y, a
+
+
 # ---- Q3_K (q3k_oracle.h) ----------------------------------------------------
 
 Q3K_BLOCK_BYTES = 110
@@ -533,4 +596,31 @@ def q3k_gemv_rows(w: np.ndarray, x: np.ndarray, n: int, k: int, rows):
     a = np.zeros((m, rows.size), np.float64)
     _check(lib().oracle_q3k_gemv_rows(_p(w, _u8p), _p(x, _f32p), m, n, k, _p(rows, _i64p),
                                       rows.size, _p(y, _f64p), _p(a, _f64p)), "q3k_gemv_rows")
+    return y, a
+
+
+def q3k_gemm(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int):
+    """Y, A = oracle GEMM on Q3_K weights; x_bf16 uint16 [m, k]; fp64 [m, n]."""
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * Q3K_BLOCK_BYTES
+    x = _c(x_bf16, np.uint16).reshape(-1, k)
+    m = x.shape[0]
+    y = np.zeros((m, n), np.float64)
+    a = np.zeros((m, n), np.float64)
+    _check(lib().oracle_q3k_gemm(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(y, _f64p),
+                                 _p(a, _f64p)), "q3k_gemm")
+    return y, a
+
+
+def q3k_gemm_cols(w: np.ndarray, x_bf16: np.ndarray, n: int, k: int, cols):
+    """Oracle Q3_K GEMM at output columns ``cols``; returns [m, len(cols)]."""
+    w = _c(w, np.uint8)
+    assert w.size == n * (k // 256) * Q3K_BLOCK_BYTES
+    x = _c(x_bf16, np.uint16).reshape(-1, k)
+    cols = _c(cols, np.int64)
+    m = x.shape[0]
+    y = np.zeros((m, cols.size), np.float64)
+    a = np.zeros((m, cols.size), np.float64)
+    _check(lib().oracle_q3k_gemm_cols(_p(w, _u8p), _p(x, _u16p), m, n, k, _p(cols, _i64p),
+                                      cols.size, _p(y, _f64p), _p(a, _f64p)), "q3k_gemm_cols")
     return y, a

@@ -95,3 +95,41 @@ int oracle_q3k_gemv(const uint8_t *w, const float *x, int64_t m, int64_t n,
   free(rows);
   return rc;
 }
+
+/* Y[i, j] = sum_c X[i, c] W[j, c] with X decoded exactly from bf16; each
+ * product is exact in fp64, summed in c order. */
+int oracle_q3k_gemm_cols(const uint8_t *w, const uint16_t *x, int64_t m, int64_t n,
+                         int64_t k, const int64_t *cols, int64_t ncols,
+                         double *y, double *a) {
+  if (!valid_shape(n, k) || m < 0 || ncols < 0) return -1;
+  for (int64_t t = 0; t < ncols; ++t)
+    if (cols[t] < 0 || cols[t] >= n) return -1;
+  float *wrow = (float *)malloc((size_t)(k > 0 ? k : 1) * sizeof(float));
+  if (!wrow) return -1;
+  for (int64_t t = 0; t < ncols; ++t) {
+    dequant_row(w, cols[t], k, wrow);
+    for (int64_t i = 0; i < m; ++i) {
+      double s = 0.0, u = 0.0;
+      for (int64_t c = 0; c < k; ++c) {
+        const double p = oracle_bf16_to_f64(x[i * k + c]) * (double)wrow[c];
+        s += p;
+        u += fabs(p);
+      }
+      y[i * ncols + t] = s;
+      a[i * ncols + t] = u;
+    }
+  }
+  free(wrow);
+  return 0;
+}
+
+int oracle_q3k_gemm(const uint8_t *w, const uint16_t *x, int64_t m, int64_t n,
+                    int64_t k, double *y, double *a) {
+  if (!valid_shape(n, k) || m < 0) return -1;
+  int64_t *cols = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+  if (!cols) return -1;
+  for (int64_t j = 0; j < n; ++j) cols[j] = j;
+  const int rc = oracle_q3k_gemm_cols(w, x, m, n, k, cols, n, y, a);
+  free(cols);
+  return rc;
+}

@@ -14,6 +14,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ---- binary16 -------------------------------------------------------------
  * IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
@@ -158,6 +161,10 @@ static void dot_row(const float *wrow, const float *xrow, int64_t k, double *y,
   *a = t;
 }
 
+/* Output rows are independent: in the OpenMP build (liboracle_omp.so, the
+ * benchmark's all-cores CPU baseline) threads take whole rows, each summed in
+ * the same k order, so both builds return identical bits.  The plain build
+ * ignores the pragmas and runs the loop as written. */
 int oracle_gemv_rows(const uint8_t *w, const float *x, int64_t m, int64_t n,
                      int64_t k, const int64_t *rows, int64_t nrows, double *y,
                      double *a) {
@@ -165,16 +172,25 @@ int oracle_gemv_rows(const uint8_t *w, const float *x, int64_t m, int64_t n,
   for (int64_t t = 0; t < nrows; ++t) {
     if (rows[t] < 0 || rows[t] >= n) return -1;
   }
-  float *wrow = (float *)malloc((size_t)k * sizeof(float));
-  if (!wrow) return -1;
-  for (int64_t t = 0; t < nrows; ++t) {
-    dequant_row(w, rows[t], k, wrow);
-    for (int64_t i = 0; i < m; ++i) {
-      dot_row(wrow, x + i * k, k, &y[i * nrows + t], &a[i * nrows + t]);
+  int rc = 0;
+#pragma omp parallel
+  {
+    float *wrow = (float *)malloc((size_t)k * sizeof(float));
+    if (!wrow) {
+#pragma omp atomic write
+      rc = -1;
     }
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < nrows; ++t) {
+      if (!wrow) continue;
+      dequant_row(w, rows[t], k, wrow);
+      for (int64_t i = 0; i < m; ++i) {
+        dot_row(wrow, x + i * k, k, &y[i * nrows + t], &a[i * nrows + t]);
+      }
+    }
+    free(wrow);
   }
-  free(wrow);
-  return 0;
+  return rc;
 }
 
 int oracle_gemv(const uint8_t *w, const float *x, int64_t m, int64_t n,
@@ -199,24 +215,33 @@ int oracle_gemm_cols(const uint8_t *w, const uint16_t *x, int64_t m, int64_t n,
   for (int64_t t = 0; t < ncols; ++t) {
     if (cols[t] < 0 || cols[t] >= n) return -1;
   }
-  float *wrow = (float *)malloc((size_t)k * sizeof(float));
-  if (!wrow) return -1;
-  for (int64_t t = 0; t < ncols; ++t) {
-    dequant_row(w, cols[t], k, wrow);
-    for (int64_t i = 0; i < m; ++i) {
-      double s = 0.0, u = 0.0;
-      const uint16_t *xrow = x + i * k;
-      for (int64_t c = 0; c < k; ++c) {
-        const double p = oracle_bf16_to_f64(xrow[c]) * (double)wrow[c];
-        s += p;
-        u += fabs(p);
-      }
-      y[i * ncols + t] = s;
-      a[i * ncols + t] = u;
+  int rc = 0;
+#pragma omp parallel
+  {
+    float *wrow = (float *)malloc((size_t)k * sizeof(float));
+    if (!wrow) {
+#pragma omp atomic write
+      rc = -1;
     }
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < ncols; ++t) {
+      if (!wrow) continue;
+      dequant_row(w, cols[t], k, wrow);
+      for (int64_t i = 0; i < m; ++i) {
+        double s = 0.0, u = 0.0;
+        const uint16_t *xrow = x + i * k;
+        for (int64_t c = 0; c < k; ++c) {
+          const double p = oracle_bf16_to_f64(xrow[c]) * (double)wrow[c];
+          s += p;
+          u += fabs(p);
+        }
+        y[i * ncols + t] = s;
+        a[i * ncols + t] = u;
+      }
+    }
+    free(wrow);
   }
-  free(wrow);
-  return 0;
+  return rc;
 }
 
 int oracle_gemm(const uint8_t *w, const uint16_t *x, int64_t m, int64_t n,
@@ -236,6 +261,16 @@ int oracle_gemm(const uint8_t *w, const uint16_t *x, int64_t m, int64_t n,
  * projection of h.  silu is the textbook t * sigmoid(t). */
 double oracle_silu(double t) { return t / (1.0 + exp(-t)); }
 
+/* Threads the row loops use: 1 in the plain build, the OpenMP team size in the
+ * OpenMP build. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 int oracle_swiglu_mlp(const uint8_t *w_gate, const uint8_t *w_up,
                       const uint8_t *w_down, const float *x, int64_t d_model,
                       int64_t d_ff, double *g, double *ag, double *u,
@@ -247,23 +282,34 @@ int oracle_swiglu_mlp(const uint8_t *w_gate, const uint8_t *w_up,
   double *uu = (double *)malloc(nf * sizeof(double));
   double *ua = (double *)malloc(nf * sizeof(double));
   double *hh = (double *)malloc(nf * sizeof(double));
-  float *wrow = (float *)malloc((size_t)(d_ff > d_model ? d_ff : d_model) * sizeof(float));
   int rc = -1;
-  if (!gg || !ga || !uu || !ua || !hh || !wrow) goto done;
+  if (!gg || !ga || !uu || !ua || !hh) goto done;
   if (oracle_gemv(w_gate, x, 1, d_ff, d_model, gg, ga)) goto done;
   if (oracle_gemv(w_up, x, 1, d_ff, d_model, uu, ua)) goto done;
   for (int64_t f = 0; f < d_ff; ++f) hh[f] = oracle_silu(gg[f]) * uu[f];
-  for (int64_t r = 0; r < d_model; ++r) {
-    dequant_row(w_down, r, d_ff, wrow);
-    double s = 0.0, t = 0.0;
-    for (int64_t f = 0; f < d_ff; ++f) {
-      const double p = (double)wrow[f] * hh[f];
-      s += p;
-      t += fabs(p);
+#pragma omp parallel
+  {
+    float *drow = (float *)malloc((size_t)d_ff * sizeof(float));
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < d_model; ++r) {
+      if (!drow) continue;
+      dequant_row(w_down, r, d_ff, drow);
+      double s = 0.0, t = 0.0;
+      for (int64_t f = 0; f < d_ff; ++f) {
+        const double p = (double)drow[f] * hh[f];
+        s += p;
+        t += fabs(p);
+      }
+      out[r] = s;
+      if (aout) aout[r] = t;
     }
-    out[r] = s;
-    if (aout) aout[r] = t;
+    if (!drow) {
+#pragma omp atomic write
+      rc = -2;
+    }
+    free(drow);
   }
+  if (rc == -2) goto done;
   if (g) memcpy(g, gg, nf * sizeof(double));
   if (ag) memcpy(ag, ga, nf * sizeof(double));
   if (u) memcpy(u, uu, nf * sizeof(double));
@@ -276,6 +322,5 @@ done:
   free(uu);
   free(ua);
   free(hh);
-  free(wrow);
   return rc;
 }

@@ -103,6 +103,12 @@ int oracle_swiglu_mlp(const uint8_t *w_gate, const uint8_t *w_up,
                       int64_t d_ff, double *g, double *ag, double *u,
                       double *au, double *h, double *out, double *aout);
 
+/* Threads the GEMV, GEMM and MLP row loops run on: 1 for liboracle.so; for
+ * liboracle_omp.so (the same source built with OpenMP, used only to time the
+ * oracle on all host cores) the OpenMP team size.  Both builds return
+ * identical results: each output row is summed in the same order. */
+int oracle_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,17 @@ int oracle_q6k_gemv_rows(const uint8_t *w, const float *x, int64_t m, int64_t n,
                          int64_t k, const int64_t *rows, int64_t nrows,
                          double *y, double *a);
 
+/* GEMM as oracle_gemm / oracle_gemm_cols (X bf16 bits [m, k], Y = X W^T), on
+ * Q6_K weights: the tile kernel's result ("CPU kernel parity ...":
+ * each k-quant has a decode kernel and a tile kernel), from the fp32 weights
+ * and the exactly decoded bf16 X, products summed in k order in fp64;
+ * a = sum |X W| with the fp32 weights. */
+int oracle_q6k_gemm(const uint8_t *w, const uint16_t *x, int64_t m, int64_t n,
+                    int64_t k, double *y, double *a);
+int oracle_q6k_gemm_cols(const uint8_t *w, const uint16_t *x, int64_t m, int64_t n,
+                         int64_t k, const int64_t *cols, int64_t ncols,
+                         double *y, double *a);
+
 #ifdef __cplusplus
 }
 #endif

@@ -434,3 +434,31 @@ def test_q5k_gemm_matches_library_matmul():
     cols = np.array([3, 0, 23])
     yc, ac = oracle.q5k_gemm_cols(w, xb, n, k, cols)
     assert np.array_equal(yc, y[:, cols]) and np.array_equal(ac, a[:, cols])
+
+
+# ---------------------------------------------------------------- all-cores build
+
+def test_openmp_build_returns_identical_bits():
+    # liboracle_omp.so runs whole output rows per thread in the same k order;
+    # its results must equal the plain build's bit for bit.
+    n, k, m = 96, 1024, 3
+    w = synth.q4k_weights(n, k, seed=41)
+    x = synth.normal_f32((m, k), seed=41)
+    y1, a1 = oracle.gemv(w, x, n, k)
+    y2, a2 = oracle.gemv(w, x, n, k, omp=True)
+    assert np.array_equal(y1, y2) and np.array_equal(a1, a2)
+    xb = synth.normal_bf16((m, k), seed=41)
+    cols = np.arange(0, n, 5)
+    g1, b1 = oracle.gemm_cols(w, xb, n, k, cols)
+    g2, b2 = oracle.gemm_cols(w, xb, n, k, cols, omp=True)
+    assert np.array_equal(g1, g2) and np.array_equal(b1, b2)
+    dm, dff = 256, 512
+    wg = synth.q4k_weights(dff, dm, seed=42, stream=synth.W_GATE)
+    wu = synth.q4k_weights(dff, dm, seed=42, stream=synth.W_UP)
+    wd = synth.q4k_weights(dm, dff, seed=42, stream=synth.W_DOWN)
+    xm = synth.normal_f32(dm, seed=42)
+    r1 = oracle.swiglu_mlp(wg, wu, wd, xm, dm, dff)
+    r2 = oracle.swiglu_mlp(wg, wu, wd, xm, dm, dff, omp=True)
+    for key in r1:
+        assert np.array_equal(r1[key], r2[key]), key
+    assert oracle.threads() == 1 and oracle.threads(omp=True) >= 1

@@ -112,3 +112,41 @@ def test_q6k_gemv_matches_library_matmul():
     rows = np.array([23, 0, 7])
     yr, _ = oracle.q6k_gemv_rows(w, x, n, k, rows)
     np.testing.assert_array_equal(yr, y[:, rows])
+
+
+# ---------------------------------------------------------------- GEMM
+
+def test_q6k_gemm_at_m1_with_bf16_exact_x_equals_gemv():
+    # A bf16 row is exactly an fp32 row, so the GEMM at one row must return
+    # the GEMV's sums bit for bit (same fp32 weights, same k order).
+    n, k = 24, 1024
+    w = synth.q6k_weights(n, k, seed=31)
+    xb = synth.normal_bf16((1, k), seed=31)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    y1, a1 = oracle.q6k_gemm(w, xb, n, k)
+    y2, a2 = oracle.q6k_gemv(w, xf, n, k)
+    assert np.array_equal(y1, y2) and np.array_equal(a1, a2)
+
+
+def test_q6k_gemm_matches_library_matmul():
+    import torch
+    m, n, k = 7, 20, 768
+    w = synth.q6k_weights(n, k, seed=32)
+    xb = synth.normal_bf16((m, k), seed=32)
+    X = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    W = oracle.q6k_dequant_f32(w, n, k).astype(np.float64)
+    y, a = oracle.q6k_gemm(w, xb, n, k)
+    assert np.all(np.abs(y - X @ W.T) <= 1e-12 * a)
+    np.testing.assert_allclose(a, np.abs(X) @ np.abs(W).T, rtol=1e-12)
+    cols = [19, 0, 6]
+    yc, ac = oracle.q6k_gemm_cols(w, xb, n, k, cols)
+    assert np.array_equal(yc, y[:, cols]) and np.array_equal(ac, a[:, cols])
+
+
+def test_q6k_gemm_zero_weights_give_exact_zero():
+    # A matrix whose weights are all zero gives exactly +-0 with A = 0.
+    n, k, m = 3, 256, 4
+    w = np.zeros((n, k // 256 * oracle.Q6K_BLOCK_BYTES), np.uint8)
+    xb = synth.normal_bf16((m, k), seed=33)
+    y, a = oracle.q6k_gemm(w, xb, n, k)
+    assert np.all(y == 0.0) and np.all(a == 0.0)
