@@ -468,7 +468,7 @@ def main():
 # the code of its kernels is unchanged since the counters were taken).
 _COMMON_SOURCES = ("q4k_device.h", "q4k_launch.h")
 KERNEL_SOURCES = {
-    "gemv": ("k_gemv.hip", "k_flush.hip"),
+    "gemv": ("k_gemv.hip", "k_gemv_split.hip"),
     "gemm": ("k_gemm.hip", "lds_copy.h"),
     "dequant": ("k_dequant.hip",),
     "w8a8": ("k_w8a8.hip", "lds_copy.h"),
@@ -575,7 +575,7 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "sweep_gemm_14336x4096"
     if "k_read_probe" in name:
         return "read_probe"
-    if "k_gemv_flush" in name:
+    if "k_gemv_split" in name:
         return "sweep_gemv_14336x4096_flush"
     gp = _template_args(name, "k_gemv_planes")
     if gp:

@@ -21,6 +21,8 @@ Q4K_ERR_LAUNCH = -4
 Q4K_QK = 256
 Q4K_BLOCK_BYTES = 144
 Q4K_GEMV_MAX_M = 32
+Q4K_MAX_N = 2147418111
+Q4K_GEMM_MAX_K = 16777216
 Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
 Q3K_BLOCK_BYTES = 110

@@ -291,6 +291,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __re
   const int nsb = k >> 8;                     // super-blocks along K
   const int nst = k >> 6;                     // 64-wide steps
   const uint32_t row_bytes = static_cast<uint32_t>(nsb) * kBlockBytes;
+  // The tile's first weight row, in 64 bits; offsets inside the tile's 256
+  // rows stay below 2^32 (k <= 2^24, checked by the C ABI).
+  const uint8_t* const wt = w + static_cast<size_t>(n0) * row_bytes;
   const int sb_rot = (tn * 7) % nsb;
   // Super-block of logical super-block S (indices past the end repeat the last).
   auto phys_sb = [&](int S) {
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __re
   for (int i = 0; i < 9; ++i) {
     const int P = (wave * 9 + i) * 64 + lane;
     const int col = (P * 7282) >> 16;  // P / 9 for P < 2304
-    woff[i] = static_cast<uint32_t>(min(n0 + col, n - 1)) * row_bytes + (P - col * 9) * 16;
+    woff[i] = static_cast<uint32_t>(min(col, n - 1 - n0)) * row_bytes + (P - col * 9) * 16;
   }
   const uint32_t lds0 = lds_address(smem);
   auto copy_x = [&](int s, int slot) {
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __re
                     __builtin_amdgcn_readfirstlane(lds0 + slot * kWXSlot + (wave * 4 + q) * 1024));
   };
   auto copy_w = [&](int S, int slot) {
-    const uint8_t* base = w + static_cast<size_t>(phys_sb(S)) * kBlockBytes;
+    const uint8_t* base = wt + static_cast<size_t>(phys_sb(S)) * kBlockBytes;
 #pragma unroll
     for (int i = 0; i < 9; ++i)
       copy16_to_lds(base + woff[i], __builtin_amdgcn_readfirstlane(
@@ -603,6 +606,9 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int nsb = k >> 8, nst = k >> 6;
   const uint32_t row_bytes = static_cast<uint32_t>(nsb) * C::BB;
+  // The tile's first weight row, in 64 bits; offsets inside the tile stay
+  // below 2^32 (k <= 2^24, checked by the C ABI).
+  const uint8_t* const wt = w + static_cast<size_t>(n0) * row_bytes;
   const int sb_rot = (tn * 7) % nsb;
   auto phys_sb = [&](int S) {
     const int e = min(S, nsb - 1) + sb_rot;
@@ -625,7 +631,7 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   for (int i = 0; i < C::WCopies; ++i) {
     const int U = C::WaveUnits * wave + unit0(i) + lane;
     const int col = FMT == 5 ? U / C::Units : (U * 7282) >> 16;  // U / 9 for U < 2304
-    woff[i] = static_cast<uint32_t>(min(n0 + col, n - 1)) * row_bytes + (U - col * C::Units) * 16;
+    woff[i] = static_cast<uint32_t>(min(col, n - 1 - n0)) * row_bytes + (U - col * C::Units) * 16;
   }
   const uint32_t lds0 = lds_address(smem);
   auto copy_x = [&](int s, int slot) {
@@ -635,7 +641,7 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
                   __builtin_amdgcn_readfirstlane(lds0 + slot * C::XSlot + wave * 1024));
   };
   auto copy_w = [&](int S, int slot) {
-    const uint8_t* base = w + static_cast<size_t>(phys_sb(S)) * C::BB;
+    const uint8_t* base = wt + static_cast<size_t>(phys_sb(S)) * C::BB;
 #pragma unroll
     for (int i = 0; i < C::WCopies; ++i)
       copy16_to_lds(base + woff[i],

@@ -22,12 +22,16 @@
 //   * x (MT activation rows, a chunk of K at a time) is staged once per
 //     workgroup in LDS, skewed by 16 bytes every 256 so that the lanes of a
 //     wave -- whose 64-float slices start 256 bytes apart -- hit distinct
-//     banks; the staging pass also forms the 32-wide sub-block sums of x.
-//   * per sub-block j the dot is refactored as
-//       sum_l (a_j q_l - b_j) x_l = a_j * sum_l q_l x_l - b_j * sum_l x_l,
-//     so the scales are applied twice per 32 weights, not per weight.
+//     banks.
+//   * every weight is formed exactly before it meets x: fma(a_j, q_l, -b_j)
+//     rounds d sc q - dmin m once, the same bits as the dequant export, and
+//     the dot is then a plain fp32 FMA chain over exact weights.  (Applying
+//     the scales per sub-block, a_j sum q x - b_j sum x, is one FMA per weight
+//     cheaper but loses the result when a_j q ~ b_j: a block whose weights
+//     cancel to zero would return the rounding noise of two large sums.)
 //   * quants are widened with v_cvt_pk_f32_fp8 (a masked nibble byte is the
-//     fp8 value q * 2^-9), two per instruction, once per weight whatever MT.
+//     fp8 value q * 2^-9), two per instruction, and each weight is formed once
+//     whatever MT.
 //   * lanes reduce with DPP and two cross-row swizzles; lane 0 stores.
 #include <hip/hip_runtime.h>
 
@@ -52,11 +56,11 @@ constexpr int kXChunk = MT == 1 ? 16384 : MT == 2 ? 8192 : 4096;
 
 __device__ __forceinline__ int xs_index(int i) { return i + ((i >> 6) << 2); }
 
-// Floats of LDS per staged activation row (skewed x) and per row of sums.
+// Floats of LDS per staged activation row (x skewed by 16 bytes every 256).
 __host__ __device__ constexpr int xs_stride(int kc) { return kc + kc / 16; }
 
 __host__ __device__ constexpr size_t gemv_lds_bytes(int mt, int kc) {
-  return static_cast<size_t>(mt) * (xs_stride(kc) + kc / 32) * sizeof(float);
+  return static_cast<size_t>(mt) * xs_stride(kc) * sizeof(float);
 }
 
 template <int R, int NW, int FMT>
@@ -68,11 +72,10 @@ struct WRegs {
 // MT activation rows per pass, R weight rows per wave (times NW = 2 weight
 // matrices for the gate/up pair), NWV waves per workgroup.  XREG (batch 1,
 // k <= 4096: one K step, so a lane meets the same 64 x values in every row):
-// each lane holds its x slice and the two sub-block sums in registers, read
-// from LDS once while the first weights are in flight.  FMT: 4 (Q4_K) or 5
-// (Q5_K: a lane also loads the block's 32 high-bit bytes and widens its 5-bit
-// quant bytes exactly with v_cvt_f32_ubyte, so its scale is d*sc without the
-// 2^9 of the fp8 path).
+// each lane holds its x slice in registers, read from LDS once while the
+// first weights are in flight.  FMT: 4 (Q4_K) or 5 (Q5_K: a lane also loads
+// the block's 32 high-bit bytes and widens its 5-bit quant bytes exactly with
+// v_cvt_f32_ubyte, so its scale is d*sc without the 2^9 of the fp8 path).
 template <int MT, int R, bool GLU, int NWV, bool XREG, int FMT = 4>
 __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict__ w,
                                                        const uint8_t* __restrict__ w2,
@@ -86,9 +89,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
   extern __shared__ float smem[];
   const int kc_max = min(k, kXChunk<MT>);
   const int xst = xs_stride(kc_max);
-  const int sst = kc_max / 32;
-  float* xs = smem;             // [MT][xst]
-  float* ssum = smem + MT * xst;  // [MT][sst]
+  float* xs = smem;  // [MT][xst]
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -116,7 +117,6 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
       for (int i = 0; i < MT; ++i) acc[u][r][i] = 0.0f;
 
   f4_t xr[XREG ? 16 : 1];  // x[64g .. 64g+63] of super-block b (XREG)
-  float xsum[2] = {0.0f, 0.0f};  // its two sub-block sums (XREG)
   for (int c0 = 0; c0 < k; c0 += kXChunk<MT>) {
     const int kc = min(kXChunk<MT>, k - c0);
     const int s_begin = c0 >> 12;
@@ -155,6 +155,18 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
       const bool active = st * 16 + b < kb_count;
       const int kb_local = active ? st * 16 + b - (c0 >> 8) : 0;
       const int xo = xs_index(kb_local * kQK + 64 * g);
+      // Scales of the lane's two sub-blocks (2g: low nibbles, 2g+1: high).
+      GroupScales sc[NW][R];
+#pragma unroll
+      for (int u = 0; u < NW; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          sc[u][r] = group_scales(B.hd[u][r], g);
+          if constexpr (FMT == 5) {  // the quants are exact integers, not q * 2^-9
+            sc[u][r].a_lo *= 1.0f / kNibbleUnscale;
+            sc[u][r].a_hi *= 1.0f / kNibbleUnscale;
+          }
+        }
       float pl[NW][R][MT], ph[NW][R][MT];
 #pragma unroll
       for (int u = 0; u < NW; ++u)
@@ -216,19 +228,28 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
               h01 = fp8x2_lo(hi);
               h23 = fp8x2_hi(hi);
             }
+            const GroupScales& s = sc[u][r];
+            const float wl0 = __builtin_fmaf(s.a_lo, l01.x, -s.b_lo);
+            const float wl1 = __builtin_fmaf(s.a_lo, l01.y, -s.b_lo);
+            const float wl2 = __builtin_fmaf(s.a_lo, l23.x, -s.b_lo);
+            const float wl3 = __builtin_fmaf(s.a_lo, l23.y, -s.b_lo);
+            const float wh0 = __builtin_fmaf(s.a_hi, h01.x, -s.b_hi);
+            const float wh1 = __builtin_fmaf(s.a_hi, h01.y, -s.b_hi);
+            const float wh2 = __builtin_fmaf(s.a_hi, h23.x, -s.b_hi);
+            const float wh3 = __builtin_fmaf(s.a_hi, h23.y, -s.b_hi);
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
               float a = pl[u][r][i];
-              a = __builtin_fmaf(l01.x, xl[i].x, a);
-              a = __builtin_fmaf(l01.y, xl[i].y, a);
-              a = __builtin_fmaf(l23.x, xl[i].z, a);
-              a = __builtin_fmaf(l23.y, xl[i].w, a);
+              a = __builtin_fmaf(wl0, xl[i].x, a);
+              a = __builtin_fmaf(wl1, xl[i].y, a);
+              a = __builtin_fmaf(wl2, xl[i].z, a);
+              a = __builtin_fmaf(wl3, xl[i].w, a);
               pl[u][r][i] = a;
               float e = ph[u][r][i];
-              e = __builtin_fmaf(h01.x, xh[i].x, e);
-              e = __builtin_fmaf(h01.y, xh[i].y, e);
-              e = __builtin_fmaf(h23.x, xh[i].z, e);
-              e = __builtin_fmaf(h23.y, xh[i].w, e);
+              e = __builtin_fmaf(wh0, xh[i].x, e);
+              e = __builtin_fmaf(wh1, xh[i].y, e);
+              e = __builtin_fmaf(wh2, xh[i].z, e);
+              e = __builtin_fmaf(wh3, xh[i].w, e);
               ph[u][r][i] = e;
             }
           }
@@ -236,26 +257,11 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int u = 0; u < NW; ++u) {
+      for (int u = 0; u < NW; ++u)
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          GroupScales sc = group_scales(B.hd[u][r], g);
-          if constexpr (FMT == 5) {  // the quants are exact integers, not q * 2^-9
-            sc.a_lo *= 1.0f / kNibbleUnscale;
-            sc.a_hi *= 1.0f / kNibbleUnscale;
-          }
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            const float slo = XREG ? xsum[0] : ssum[i * sst + kb_local * 8 + 2 * g];
-            const float shi = XREG ? xsum[1] : ssum[i * sst + kb_local * 8 + 2 * g + 1];
-            float a = sc.a_lo * pl[u][r][i];
-            a = __builtin_fmaf(sc.a_hi, ph[u][r][i], a);
-            a = __builtin_fmaf(-sc.b_lo, slo, a);
-            a = __builtin_fmaf(-sc.b_hi, shi, a);
-            acc[u][r][i] += active ? a : 0.0f;
-          }
-        }
-      }
+          for (int i = 0; i < MT; ++i) acc[u][r][i] += active ? pl[u][r][i] + ph[u][r][i] : 0.0f;
       if (sl != ns - 1 || (single && !last_chunk)) return;
       // Row set finished (for this chunk): reduce, store, reset.
       const int row0 = (gw + si * tw) * R;
@@ -304,13 +310,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
       dst[1] = v[1];
       dst[2] = v[2];
       dst[3] = v[3];
-      float s = ((v[0].x + v[0].y) + (v[0].z + v[0].w)) + ((v[1].x + v[1].y) + (v[1].z + v[1].w)) +
-                ((v[2].x + v[2].y) + (v[2].z + v[2].w)) + ((v[3].x + v[3].y) + (v[3].z + v[3].w));
-      s += dpp_mov<0xB1>(s);  // thread t ^ 1 holds the other 16 floats of the sub-block
-      if ((t & 1) == 0) ssum[i * sst + (e >> 5)] = s;
     };
-    // Every pass covers whole sub-blocks (MT * kc is a multiple of 32), so a
-    // thread and its partner t ^ 1 take the same passes.
     const bool first = 16 * t < MT * kc;
     f4_t v0[4];
     if (first) load_x16(16 * t, v0);
@@ -334,8 +334,6 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
         xr[c] = *reinterpret_cast<const f4_t*>(xs + xo + 4 * c);
         xr[8 + c] = *reinterpret_cast<const f4_t*>(xs + xo + 32 + 4 * c);
       }
-      xsum[0] = ssum[kb_local * 8 + 2 * g];
-      xsum[1] = ssum[kb_local * 8 + 2 * g + 1];
     }
 
     for (int j = 0; j < jobs; j += 2) {
@@ -410,50 +408,37 @@ hipError_t launch(const uint8_t* w, const uint8_t* w2, const float* x, float* y,
 template <int FMT>
 hipError_t launch_gemv_passes(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                               int64_t k, hipStream_t stream) {
-  // Batches above 8 rows run as passes of 8 over x and y; W is re-streamed.
-  for (int64_t i0 = 0; i0 < m; i0 += 8) {
-    const int mm = static_cast<int>(m - i0 < 8 ? m - i0 : 8);
-    const float* xs = x + i0 * k;
-    float* ys = y + i0 * n;
-    const int ni = static_cast<int>(n), ki = static_cast<int>(k);
-    hipError_t e;
-    if (mm == 1) {
-      // One row per wave; matrices with few rows per CU take 16 waves per
-      // workgroup (x staged once per 16 waves).  Taller ones take 4 waves and,
-      // within one K step (k <= 4096), keep x in registers across their rows;
-      // past one K step, 8 waves.
-      if (n <= kGemvWideRows) {
-        e = launch<1, kGemvRowsPerWave, false, 16, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
-      } else if (k <= 4096) {
-        e = launch<1, kGemvRowsPerWave, false, 4, true, FMT>(w, w, xs, ys, mm, ni, ki, stream);
-      } else {
-        e = launch<1, kGemvRowsPerWave, false, 8, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
-      }
-    } else if (mm == 2) {
-      e = launch<2, 2, false, 4, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
-    } else if (mm <= 4) {
-      e = launch<4, 2, false, 4, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
-    } else {
-      e = launch<8, 1, false, 8, false, FMT>(w, w, xs, ys, mm, ni, ki, stream);
-    }
-    if (e != hipSuccess) return e;
+  // Batches below kGemvSplitMinM rows: one pass over W.
+  const int mm = static_cast<int>(m);
+  const int ni = static_cast<int>(n), ki = static_cast<int>(k);
+  if (mm == 1) {
+    // One row per wave; matrices with few rows per CU take 16 waves per
+    // workgroup (x staged once per 16 waves).  Taller ones take 4 waves and,
+    // within one K step (k <= 4096), keep x in registers across their rows;
+    // past one K step, 8 waves.
+    if (n <= kGemvWideRows)
+      return launch<1, kGemvRowsPerWave, false, 16, false, FMT>(w, w, x, y, mm, ni, ki, stream);
+    if (k <= 4096)
+      return launch<1, kGemvRowsPerWave, false, 4, true, FMT>(w, w, x, y, mm, ni, ki, stream);
+    return launch<1, kGemvRowsPerWave, false, 8, false, FMT>(w, w, x, y, mm, ni, ki, stream);
   }
-  return hipSuccess;
+  if (mm == 2) return launch<2, 2, false, 4, false, FMT>(w, w, x, y, mm, ni, ki, stream);
+  return launch<4, 2, false, 4, false, FMT>(w, w, x, y, mm, ni, ki, stream);
 }
 
 }  // namespace
 
-// Batches from kGemvFlushMinM rows take the scale-flush MFMA kernel
-// (k_flush.hip); smaller ones the fp32 FMA passes.
+// Batches from kGemvSplitMinM rows take the split-bf16 MFMA kernel
+// (k_gemv_split.hip); smaller ones the fp32 FMA passes.
 hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream) {
-  if (gemv_flush_supported(m)) return launch_gemv_flush(w, x, y, m, n, k, stream);
+  if (gemv_split_supported(m)) return launch_gemv_split(w, x, y, m, n, k, stream);
   return launch_gemv_passes<4>(w, x, y, m, n, k, stream);
 }
 
 hipError_t launch_q5k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                            int64_t k, hipStream_t stream) {
-  if (gemv_flush_supported(m)) return launch_q5k_gemv_flush(w, x, y, m, n, k, stream);
+  if (gemv_split_supported(m)) return launch_q5k_gemv_split(w, x, y, m, n, k, stream);
   return launch_gemv_passes<5>(w, x, y, m, n, k, stream);
 }
 

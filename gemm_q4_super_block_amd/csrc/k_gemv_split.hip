@@ -1,27 +1,24 @@
-// k_flush.hip -- Q4_K and Q5_K GEMV for batches of 6 to 32 rows on bf16 MFMA,
-// with the sub-block scales flushed into the fp32 accumulator.
+// k_gemv_split.hip -- Q4_K and Q5_K GEMV for batches of 5 to 32 rows on bf16 MFMA.
 //
 // What it computes is q4k_gemv's y = x W^T (fp32 x, fp32 y, the same
-// tolerance).  The method is the daScript PR page's scale flush ("CPU kernel
-// parity ...", the kernel work: the k-quants "flush their scales fused into
-// the accumulator"): within a 32-weight sub-block every weight is
-// d sc q - dmin m with one (d sc, dmin m) pair, so
-//   sum_i w_i x_i = (d sc) sum_i q_i x_i - (dmin m) sum_i x_i,
-// and the two sums can come from a matrix core working on the raw quants.
+// tolerance, 1e-4 * sum|w x| per output).  At these batch sizes one fp32 FMA
+// per weight per batch row is more VALU work than the weight stream can hide,
+// so the products go to the matrix cores, as the daScript PR page's tile
+// kernels do for batches ("CPU kernel parity ...": token reuse in the tile
+// kernels), with fp32-GEMV accuracy kept by splitting both operands.
 //
 // Design for gfx950:
-//   * v_mfma_f32_16x16x32_bf16: one MFMA is exactly one sub-block (K = 32)
-//     for 16 batch rows (M) and 16 weight rows (N).  The quants (0..15, or
-//     0..31 for Q5_K with the fifth bit from the high-bit plane) are exact in
-//     bf16.  fp32 x is split into x_hi = bf16(x) and x_lo = bf16(x -
-//     x_hi): every product q x_hi, q x_lo is exact in the fp32 accumulator and
-//     x_hi + x_lo is within 2^-17 |x| of x, so the result has fp32-GEMV
-//     accuracy, not bf16 accuracy.
-//   * per sub-block and 16x16 tile: P = sum q x (two MFMAs, hi and lo) and
-//     S = sum x (two MFMAs against a B of ones, shared by every weight tile);
-//     then acc += (d sc) P - (dmin m) S per output, eight VALU FMAs per lane.
-//     The weights are never dequantized: per weight the VALU cost is one
-//     nibble-to-bf16 conversion, shared by all batch rows.
+//   * v_mfma_f32_16x16x32_bf16: one MFMA covers 32 weights (K) of 16 weight
+//     rows (N) for 16 batch rows (M).
+//   * every weight is formed exactly first, w = fma(d sc, q, -dmin m) (the
+//     dequant export's bits), then split w = w_hi + w_lo with w_hi = bf16(w)
+//     and w_lo = bf16(w - w_hi); x likewise (x_hi, x_lo).  Three MFMAs per
+//     tile, w_hi x_hi + w_hi x_lo + w_lo x_hi, leave out w_lo x_lo and the two
+//     residuals, each at most 2^-16 |w x| (bf16 keeps 8 significant bits), so
+//     every product is within 3 * 2^-16 of w x, and every partial product is
+//     exact in the fp32 accumulator.  A weight that is zero contributes
+//     exactly zero: a block whose weights cancel (d sc q = dmin m) gives +-0,
+//     which applying the scales to separate sums of q x and x cannot.
 //   * operand layout (both operands alike, so any internal k order gives the
 //     same contraction): lane l supplies row l % 16 (a batch row of x, or a
 //     weight row) and the 8 consecutive k of its k-group l / 16.  For quant
@@ -32,9 +29,6 @@
 //     wave w takes super-blocks w, w + 4, ... of the rows (prefetching the
 //     next one's header and quants), and the four partial tiles are summed
 //     through LDS at the end.
-//   * measured against the fp32 FMA passes on 4096 and 14336 rows, it is
-//     faster from 6 batch rows on (14336 x 4096, m = 32: 43 us against 127);
-//     below that the passes stay.
 #include <hip/hip_runtime.h>
 
 #include "q4k_device.h"
@@ -44,16 +38,6 @@ namespace q4k {
 namespace {
 
 typedef float f4v_t __attribute__((ext_vector_type(4)));
-
-// bf16x8 of 8 bytes' low (HIGH = false) or high nibbles, in byte order.
-template <bool HIGH>
-__device__ __forceinline__ bf16x8_t nibbles_bf16(uint2 q) {
-  const uint32_t a = HIGH ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
-  const uint32_t b = HIGH ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
-  const uint4 v{pack_bf16x2(ubyte_f32(a, 0), ubyte_f32(a, 1)), pack_bf16x2(ubyte_f32(a, 2), ubyte_f32(a, 3)),
-                pack_bf16x2(ubyte_f32(b, 0), ubyte_f32(b, 1)), pack_bf16x2(ubyte_f32(b, 2), ubyte_f32(b, 3))};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
 
 // 8 fp32 values -> (hi, lo) bf16x8 with hi = bf16(v), lo = bf16(v - hi).
 __device__ __forceinline__ void split_bf16(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
@@ -69,21 +53,38 @@ __device__ __forceinline__ void split_bf16(const float (&v)[8], bf16x8_t& hi, bf
   lo = __builtin_bit_cast(bf16x8_t, uint4{l[0], l[1], l[2], l[3]});
 }
 
-// bf16x8 of 8 five-bit quants: the nibbles of q (low or high half) with the
-// fifth bits taken from bit `bit` of the 8 high-bit bytes h.
-template <bool HIGH>
-__device__ __forceinline__ bf16x8_t quants5_bf16(uint2 q, uint2 h, int bit) {
-  const uint32_t a = (HIGH ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu) |
-                     (((h.x >> bit) & 0x01010101u) << 4);
-  const uint32_t b = (HIGH ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu) |
-                     (((h.y >> bit) & 0x01010101u) << 4);
-  const uint4 v{pack_bf16x2(ubyte_f32(a, 0), ubyte_f32(a, 1)), pack_bf16x2(ubyte_f32(a, 2), ubyte_f32(a, 3)),
-                pack_bf16x2(ubyte_f32(b, 0), ubyte_f32(b, 1)), pack_bf16x2(ubyte_f32(b, 2), ubyte_f32(b, 3))};
-  return __builtin_bit_cast(bf16x8_t, v);
+// The 8 exact weights of 8 quant bytes' low (HIGH = false) or high nibbles,
+// in byte order: fma(a, q * 2^-9, -b) on the fp8-widened nibbles (Q4_K, a =
+// d sc 2^9) or fma(a, q, -b) on exactly widened 5-bit quants (Q5_K, a = d sc,
+// fifth bits from bit `bit` of the 8 high-bit bytes h).
+template <bool HIGH, int FMT>
+__device__ __forceinline__ void weights8(uint2 q, uint2 h, int bit, float a, float b,
+                                         float (&w)[8]) {
+  uint32_t u0 = HIGH ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
+  uint32_t u1 = HIGH ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
+  if constexpr (FMT == 5) {
+    u0 |= ((h.x >> bit) & 0x01010101u) << 4;
+    u1 |= ((h.y >> bit) & 0x01010101u) << 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[e] = __builtin_fmaf(a, ubyte_f32(u0, e), -b);
+      w[4 + e] = __builtin_fmaf(a, ubyte_f32(u1, e), -b);
+    }
+  } else {
+    const f2_t p0 = fp8x2_lo(u0), p1 = fp8x2_hi(u0), p2 = fp8x2_lo(u1), p3 = fp8x2_hi(u1);
+    w[0] = __builtin_fmaf(a, p0.x, -b);
+    w[1] = __builtin_fmaf(a, p0.y, -b);
+    w[2] = __builtin_fmaf(a, p1.x, -b);
+    w[3] = __builtin_fmaf(a, p1.y, -b);
+    w[4] = __builtin_fmaf(a, p2.x, -b);
+    w[5] = __builtin_fmaf(a, p2.y, -b);
+    w[6] = __builtin_fmaf(a, p3.x, -b);
+    w[7] = __builtin_fmaf(a, p3.y, -b);
+  }
 }
 
 template <int MT, int NT, int FMT>
-__global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ w,
+__global__ __launch_bounds__(256) void k_gemv_split(const uint8_t* __restrict__ w,
                                                     const float* __restrict__ x,
                                                     float* __restrict__ y, int m, int n, int k) {
   __shared__ __attribute__((aligned(16))) float red[4][MT][NT][4][64];
@@ -108,7 +109,6 @@ __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ 
     xvalid[t] = 16 * t + nl < m;
   }
 
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   f4v_t acc[MT][NT];
 #pragma unroll
   for (int a = 0; a < MT; ++a)
@@ -153,9 +153,8 @@ __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ 
       }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // x of sub-blocks 2g (s = 0) and 2g + 1 (s = 1)
+      // x of sub-blocks 2g (s = 0) and 2g + 1 (s = 1), split into bf16 hi + lo
       bf16x8_t ahi[MT][2], alo[MT][2];
-      f4v_t sx[MT][2];
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -168,40 +167,31 @@ __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ 
             for (int e = 0; e < 8; ++e) xv[e] = 0.0f;
           }
           split_bf16(xv, ahi[t][s], alo[t][s]);
-          f4v_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][s], ones, z, 0, 0, 0);
-          sx[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t][s], ones, z, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const GroupScales sc = group_scales(cur.hd[nt], g);
-        // d sc without the fp8 widening factor (exact: a power of two)
-        const float dlo = sc.a_lo * (1.0f / kNibbleUnscale), dhi = sc.a_hi * (1.0f / kNibbleUnscale);
-        bf16x8_t blo, bhi;
-        if constexpr (FMT == 5) {
-          blo = quants5_bf16<false>(cur.q[nt][g], cur.qh[nt], 2 * g);
-          bhi = quants5_bf16<true>(cur.q[nt][g], cur.qh[nt], 2 * g + 1);
-        } else {
-          blo = nibbles_bf16<false>(cur.q[nt][g]);
-          bhi = nibbles_bf16<true>(cur.q[nt][g]);
+        GroupScales sc = group_scales(cur.hd[nt], g);
+        if constexpr (FMT == 5) {  // exact 5-bit quants: the scale is d sc, without 2^9
+          sc.a_lo *= 1.0f / kNibbleUnscale;
+          sc.a_hi *= 1.0f / kNibbleUnscale;
         }
+        float wl[8], wh[8];
+        weights8<false, FMT>(cur.q[nt][g], cur.qh[nt], 2 * g, sc.a_lo, sc.b_lo, wl);
+        weights8<true, FMT>(cur.q[nt][g], cur.qh[nt], 2 * g + 1, sc.a_hi, sc.b_hi, wh);
+        bf16x8_t wl_hi, wl_lo, wh_hi, wh_lo;
+        split_bf16(wl, wl_hi, wl_lo);
+        split_bf16(wh, wh_hi, wh_lo);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          f4v_t plo = {0.0f, 0.0f, 0.0f, 0.0f}, phi = {0.0f, 0.0f, 0.0f, 0.0f};
-          plo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][0], blo, plo, 0, 0, 0);
-          plo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t][0], blo, plo, 0, 0, 0);
-          phi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][1], bhi, phi, 0, 0, 0);
-          phi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t][1], bhi, phi, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float a = acc[t][nt][r];
-            a = fmaf(dlo, plo[r], a);
-            a = fmaf(-sc.b_lo, sx[t][0][r], a);
-            a = fmaf(dhi, phi[r], a);
-            a = fmaf(-sc.b_hi, sx[t][1][r], a);
-            acc[t][nt][r] = a;
-          }
+          f4v_t d = acc[t][nt];
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][0], wl_hi, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t][0], wl_hi, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][0], wl_lo, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][1], wh_hi, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t][1], wh_hi, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t][1], wh_lo, d, 0, 0, 0);
+          acc[t][nt] = d;
         }
       }
     }
@@ -233,51 +223,51 @@ __global__ __launch_bounds__(256) void k_gemv_flush(const uint8_t* __restrict__ 
 
 }  // namespace
 
-bool gemv_flush_supported(int64_t m) { return m >= kGemvFlushMinM && m <= 32; }
+bool gemv_split_supported(int64_t m) { return m >= kGemvSplitMinM && m <= 32; }
 
 namespace {
 
 // One 16-row batch tile for m <= 16, two above.  Matrices of at least
-// kFlushWideRows rows give each workgroup two 16-row weight tiles (x's split
+// kSplitWideRows rows give each workgroup two 16-row weight tiles (x's split
 // and its sums shared by both; measured 1.4-1.6x faster at 14336 rows, slower
 // at 4096, where the grid would drop to 128 workgroups).
-constexpr int kFlushWideRows = 8192;
+constexpr int kSplitWideRows = 8192;
 
 template <int MT, int NT, int FMT>
-void launch_flush_tiles(const uint8_t* w, const float* x, float* y, int m, int n, int k,
+void launch_split_tiles(const uint8_t* w, const float* x, float* y, int m, int n, int k,
                         hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemv_flush<MT, NT, FMT>), dim3((n + 16 * NT - 1) / (16 * NT)), dim3(256),
+  hipLaunchKernelGGL((k_gemv_split<MT, NT, FMT>), dim3((n + 16 * NT - 1) / (16 * NT)), dim3(256),
                      0, stream, w, x, y, m, n, k);
 }
 
 template <int FMT>
-hipError_t launch_flush_fmt(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+hipError_t launch_split_fmt(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                             int64_t k, hipStream_t stream) {
   const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
-  if (ni >= kFlushWideRows) {
+  if (ni >= kSplitWideRows) {
     if (mi <= 16)
-      launch_flush_tiles<1, 2, FMT>(w, x, y, mi, ni, ki, stream);
+      launch_split_tiles<1, 2, FMT>(w, x, y, mi, ni, ki, stream);
     else
-      launch_flush_tiles<2, 2, FMT>(w, x, y, mi, ni, ki, stream);
+      launch_split_tiles<2, 2, FMT>(w, x, y, mi, ni, ki, stream);
   } else {
     if (mi <= 16)
-      launch_flush_tiles<1, 1, FMT>(w, x, y, mi, ni, ki, stream);
+      launch_split_tiles<1, 1, FMT>(w, x, y, mi, ni, ki, stream);
     else
-      launch_flush_tiles<2, 1, FMT>(w, x, y, mi, ni, ki, stream);
+      launch_split_tiles<2, 1, FMT>(w, x, y, mi, ni, ki, stream);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemv_flush(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+hipError_t launch_gemv_split(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream) {
-  return launch_flush_fmt<4>(w, x, y, m, n, k, stream);
+  return launch_split_fmt<4>(w, x, y, m, n, k, stream);
 }
 
-hipError_t launch_q5k_gemv_flush(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+hipError_t launch_q5k_gemv_split(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                                  int64_t k, hipStream_t stream) {
-  return launch_flush_fmt<5>(w, x, y, m, n, k, stream);
+  return launch_split_fmt<5>(w, x, y, m, n, k, stream);
 }
 
 }  // namespace q4k

@@ -31,8 +31,10 @@
 //     never the matrix's first) and ends at most 2 bytes past it, inside the
 //     block; d is one 16-bit load.
 //   * The scale multiplies sums of 8 weights: per unit and j the GEMV forms
-//     dot = sum q x and s8 = sum x in fp32 and adds (d sc) (dot - OFF s8)
-//     (OFF = 32 or 4), so the quant offset costs one FMA per 8 weights.
+//     dot = sum (q - OFF) x in fp32 and adds (d sc) dot (OFF = 32 or 4).  q -
+//     OFF is an exact small integer, so a zero weight adds exactly zero; the
+//     offset is not applied to a separate sum of x, whose rounding would not
+//     cancel against that of sum q x when the weights do.
 //   * GEMV: 8 waves per workgroup, 2 rows per wave (16 rows per workgroup;
 //     measured against 4x4, 8x4, 16x1, 4x2 and 8x1, it was 8-14% faster than
 //     4x4 on 4096- and 14336-row matrices).  Per 4096-wide chunk of x a lane
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_planes(const uint8_t* __res
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qf[r][e] = ubyte_f32(wu[r].q[j][e >> 2], e & 3);
+          for (int e = 0; e < 8; ++e) qf[r][e] = ubyte_f32(wu[r].q[j][e >> 2], e & 3) - P::Off;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
           if (i >= mrows) break;
@@ -238,13 +240,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_planes(const uint8_t* __res
           const float4 a = *reinterpret_cast<const float4*>(p);
           const float4 b = *reinterpret_cast<const float4*>(p + 4);
           const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          const float s8 = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
 #pragma unroll
           for (int r = 0; r < RPW; ++r) {
             float dot = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) dot = fmaf(qf[r][e], xv[e], dot);
-            acc[i][r] = fmaf(wu[r].dsc[j], fmaf(-P::Off, s8, dot), acc[i][r]);
+            acc[i][r] = fmaf(wu[r].dsc[j], dot, acc[i][r]);
           }
         }
       }

@@ -125,7 +125,7 @@ static int gemv_checks(const char* what, const void* w, const float* x, const fl
   if (m < 1 || m > Q4K_GEMV_MAX_M)
     return fail(Q4K_ERR_INVALID_ARG, "%s: m=%lld outside 1..%d", what, (long long)m,
                 Q4K_GEMV_MAX_M);
-  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
+  if (n < 1 || n > Q4K_MAX_N) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
   if (!valid_k(k))
     return fail(Q4K_ERR_INVALID_ARG, "%s: k=%lld is not a positive multiple of 256", what,
                 (long long)k);
@@ -175,10 +175,13 @@ static int gemm_checks(const char* what, const void* w, const uint16_t* x_bf16, 
                        int64_t m, int64_t n, int64_t k, size_t block) {
   if (!w || !x_bf16 || !y) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
   if (m < 1 || m > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: m=%lld", what, (long long)m);
-  if (n < 1 || n > INT32_MAX) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
+  if (n < 1 || n > Q4K_MAX_N) return fail(Q4K_ERR_INVALID_ARG, "%s: n=%lld", what, (long long)n);
   if (!valid_k(k))
     return fail(Q4K_ERR_INVALID_ARG, "%s: k=%lld is not a positive multiple of 256", what,
                 (long long)k);
+  if (k > Q4K_GEMM_MAX_K)
+    return fail(Q4K_ERR_INVALID_ARG, "%s: k=%lld is above Q4K_GEMM_MAX_K=%d", what,
+                (long long)k, Q4K_GEMM_MAX_K);
   if (!aligned16(w) || !aligned16(x_bf16) || !aligned16(y))
     return fail(Q4K_ERR_ALIGN, "%s: w, x and y must be 16-byte aligned", what);
   const size_t ny = static_cast<size_t>(m) * static_cast<size_t>(n) * 4;

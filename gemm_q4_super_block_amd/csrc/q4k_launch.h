@@ -25,17 +25,18 @@ constexpr int kGemmSmallTiles = 128;
 // Batch-1 matrices of at most this many rows run 16 waves per workgroup.
 constexpr int64_t kGemvWideRows = 8192;
 // Q4_K and Q5_K GEMV batches of at least this many rows (up to 32) take the
-// scale-flush MFMA kernel (k_flush.hip) instead of the fp32 FMA passes.
-constexpr int kGemvFlushMinM = 6;
+// split-bf16 MFMA kernel (k_gemv_split.hip) instead of the fp32 FMA passes
+// (which handle 1 to kGemvSplitMinM - 1 rows in one pass).
+constexpr int kGemvSplitMinM = 5;
 
 hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);
 
-// Scale-flush MFMA GEMV for kGemvFlushMinM <= m <= 32 (Q4_K, Q5_K).
-bool gemv_flush_supported(int64_t m);
-hipError_t launch_gemv_flush(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+// Split-bf16 MFMA GEMV for kGemvSplitMinM <= m <= 32 (Q4_K, Q5_K).
+bool gemv_split_supported(int64_t m);
+hipError_t launch_gemv_split(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream);
-hipError_t launch_q5k_gemv_flush(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
+hipError_t launch_q5k_gemv_split(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                                  int64_t k, hipStream_t stream);
 
 hipError_t launch_gateup_swiglu(const uint8_t* w_gate, const uint8_t* w_up, const float* x,

@@ -35,6 +35,24 @@ def _dev_tensor(t: torch.Tensor, dtype, what: str) -> torch.Tensor:
     return t
 
 
+def _out_tensor(t: torch.Tensor, dtype, shape, device: torch.device, what: str) -> torch.Tensor:
+    """A caller-supplied output: dtype, contiguity, exact shape and device are
+    checked before the kernels get its pointer (a short buffer would be
+    written past its end)."""
+    _dev_tensor(t, dtype, what)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (what, tuple(t.shape), tuple(shape)))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (what, t.device, device))
+    return t
+
+
+def _same_device(device: torch.device, *named):
+    for what, t in named:
+        if t.device != device:
+            raise ValueError("%s is on %s, expected %s" % (what, t.device, device))
+
+
 def gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """y = x W^T for fp32 x [k] or [m, k] (m <= 32); returns fp32 [n] or [m, n]."""
     return _gemv(w, x, out, Q4K_BLOCK_BYTES, _lib.q4k_gemv)
@@ -58,15 +76,17 @@ def q3k_gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) 
 def _gemv(w, x, out, block, fn):
     n, k = _q4k_shape(w, block)
     _dev_tensor(x, torch.float32, "x")
+    _same_device(w.device, ("x", x))
     squeeze = x.dim() == 1
     x2 = x.view(1, -1) if squeeze else x
     if x2.dim() != 2 or x2.shape[1] != k:
         raise ValueError("x has shape %s, expected [..., %d]" % (tuple(x.shape), k))
     m = x2.shape[0]
-    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=w.device)
-    _dev_tensor(y, torch.float32, "out")
+    shape = (n,) if squeeze else (m, n)
+    y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=w.device)
+    _out_tensor(y, torch.float32, shape, w.device, "out")
     check(fn(w.data_ptr(), x2.data_ptr(), y.data_ptr(), m, n, k, _stream(w.device)))
-    return y.view(n) if squeeze else y
+    return y
 
 
 def gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -92,11 +112,12 @@ def q3k_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) 
 def _gemm(w, x, out, block, fn):
     n, k = _q4k_shape(w, block)
     _dev_tensor(x, torch.bfloat16, "x")
+    _same_device(w.device, ("x", x))
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x has shape %s, expected [m, %d]" % (tuple(x.shape), k))
     m = x.shape[0]
     y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=w.device)
-    _dev_tensor(y, torch.float32, "out")
+    _out_tensor(y, torch.float32, (m, n), w.device, "out")
     check(fn(w.data_ptr(), x.data_ptr(), y.data_ptr(), m, n, k, _stream(w.device)))
     return y
 
@@ -109,14 +130,15 @@ def swiglu_mlp(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
     if _q4k_shape(w_up) != (d_ff, d_model) or _q4k_shape(w_down) != (d_model, d_ff):
         raise ValueError("gate/up must be [d_ff, d_model] and down [d_model, d_ff]")
     _dev_tensor(x, torch.float32, "x")
-    if x.numel() != d_model:
-        raise ValueError("x must have d_model = %d elements" % d_model)
+    _same_device(w_gate.device, ("w_up", w_up), ("w_down", w_down), ("x", x))
+    if x.dim() != 1 or x.numel() != d_model:
+        raise ValueError("x must be [d_model = %d]" % d_model)
     if h is None:
         h = torch.empty(d_ff, dtype=torch.float32, device=x.device)
     if out is None:
         out = torch.empty(d_model, dtype=torch.float32, device=x.device)
-    _dev_tensor(h, torch.float32, "h")
-    _dev_tensor(out, torch.float32, "out")
+    _out_tensor(h, torch.float32, (d_ff,), x.device, "h")
+    _out_tensor(out, torch.float32, (d_model,), x.device, "out")
     check(_lib.q4k_swiglu_mlp(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(),
                               x.data_ptr(), h.data_ptr(), out.data_ptr(), d_model, d_ff,
                               _stream(x.device)))
@@ -189,8 +211,10 @@ def q3k_dequantize_bf16(w: torch.Tensor) -> torch.Tensor:
 
 # ---------------------------------------------------------------- INT8 W8A8
 
-def _vec(t, n, what):
+def _vec(t, n, what, device=None):
     _dev_tensor(t, torch.float32, what)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (what, t.device, device))
     if t.dim() != 1 or t.shape[0] != n:
         raise ValueError("%s has shape %s, expected [%d]" % (what, tuple(t.shape), n))
     return t.data_ptr()
@@ -199,6 +223,7 @@ def _vec(t, n, what):
 def _w8_operands(x, w):
     _dev_tensor(x, torch.int8, "x")
     _dev_tensor(w, torch.int8, "w")
+    _same_device(x.device, ("w", w))
     if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
         raise ValueError("x [m, k] and w [n, k] expected, got %s and %s"
                          % (tuple(x.shape), tuple(w.shape)))
@@ -209,11 +234,11 @@ def w8a8_linear(x: torch.Tensor, x_scale: torch.Tensor, w: torch.Tensor, w_scale
                 bias: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
     """bf16 [m, n] = (x w^T) * x_scale[:, None] * w_scale[None, :] + bias, int8 x and w."""
     m, n, k = _w8_operands(x, w)
-    xs = _vec(x_scale, m, "x_scale")
-    ws = _vec(w_scale, n, "w_scale")
-    b = None if bias is None else _vec(bias, n, "bias")
+    xs = _vec(x_scale, m, "x_scale", x.device)
+    ws = _vec(w_scale, n, "w_scale", x.device)
+    b = None if bias is None else _vec(bias, n, "bias", x.device)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
-    _dev_tensor(y, torch.bfloat16, "out")
+    _out_tensor(y, torch.bfloat16, (m, n), x.device, "out")
     check(_lib.w8a8_linear(x.data_ptr(), xs, w.data_ptr(), ws, b, y.data_ptr(), m, n, k,
                            _stream(x.device)))
     return y
@@ -224,7 +249,7 @@ def w8a8_linear_acc(x: torch.Tensor, w: torch.Tensor,
     """int32 [m, n] = x w^T, exact, for int8 x [m, k] and w [n, k]."""
     m, n, k = _w8_operands(x, w)
     acc = out if out is not None else torch.empty((m, n), dtype=torch.int32, device=x.device)
-    _dev_tensor(acc, torch.int32, "out")
+    _out_tensor(acc, torch.int32, (m, n), x.device, "out")
     check(_lib.w8a8_linear_acc(x.data_ptr(), w.data_ptr(), acc.data_ptr(), m, n, k,
                                _stream(x.device)))
     return acc
@@ -237,11 +262,11 @@ def w8a8_dequant(acc: torch.Tensor, x_scale: torch.Tensor, w_scale: torch.Tensor
     if acc.dim() != 2:
         raise ValueError("acc must be [m, n]")
     m, n = acc.shape
-    xs = _vec(x_scale, m, "x_scale")
-    ws = _vec(w_scale, n, "w_scale")
-    b = None if bias is None else _vec(bias, n, "bias")
+    xs = _vec(x_scale, m, "x_scale", acc.device)
+    ws = _vec(w_scale, n, "w_scale", acc.device)
+    b = None if bias is None else _vec(bias, n, "bias", acc.device)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=acc.device)
-    _dev_tensor(y, torch.bfloat16, "out")
+    _out_tensor(y, torch.bfloat16, (m, n), acc.device, "out")
     check(_lib.w8a8_dequant_epilogue(acc.data_ptr(), y.data_ptr(), xs, ws, b, m, n,
                                      _stream(acc.device)))
     return y

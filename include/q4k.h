@@ -65,6 +65,13 @@ extern "C" {
 #define Q4K_QK 256
 #define Q4K_BLOCK_BYTES 144
 #define Q4K_GEMV_MAX_M 32
+/* Largest n (weight rows) of any GEMV or GEMM: tile indices stay in int32. */
+#define Q4K_MAX_N 2147418111 /* 2^31 - 1 - 65536 */
+/* Largest k of the GEMMs (q4k_, q5k_, q6k_, q3k_gemm): a 256-row weight tile
+ * spans less than 4 GiB, so in-tile byte offsets fit 32 bits; the tile's base
+ * and every other offset are 64-bit.  Matrices of any total size (above
+ * 4 GiB included) are addressed correctly. */
+#define Q4K_GEMM_MAX_K 16777216
 /* Bytes per Q5_K super-block (the q5k_ entry points). */
 #define Q5K_BLOCK_BYTES 176
 /* Bytes per Q6_K block (the q6k_ entry points). */
@@ -95,8 +102,11 @@ int q4k_version(void);
  *   x: fp32 [m, k] row-major, 16-byte aligned.
  *   y: fp32 [m, n] row-major, 16-byte aligned.
  *   1 <= m <= Q4K_GEMV_MAX_M, n >= 1, k >= 256 with k % 256 == 0.
- * The dequantization is fused into an fp32 FMA dot product; each output
- * lies within 1e-4 * sum_c |W[j,c] x[i,c]| of the exact value.
+ * Each weight is formed exactly (the dequant export's fp32 value) before it
+ * meets x: for m <= 4 in an fp32 FMA dot product, for 5 <= m <= 32 on bf16
+ * MFMA with weight and x each split into bf16 hi + lo parts.  Each output
+ * lies within 1e-4 * sum_c |W[j,c] x[i,c]| of the exact value, and is +-0
+ * when every product W[j,c] x[i,c] is zero.
  * [P1 "Getting Q4_K Right"; P3 decode kernels.] */
 int q4k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
@@ -148,7 +158,8 @@ int q4k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
 int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /* ---- Q5_K, the 5-bit sibling ------------------------------------------------
- * [P3, the kernel work: the 4-bit and 5-bit k-quants "share one fused form".]
+ * [P3, the kernel work: the 4-bit and 5-bit k-quants are decoded by the same
+ * fused kernel shape.]
  * The pages print no Q5_K layout either; the library reads the Q4_K
  * super-block with one high-bit plane added:
  *   176 bytes encode 256 weights.
@@ -161,7 +172,8 @@ int q4k_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream)
  * A matrix is laid out as for Q4_K with 176-byte blocks. */
 
 /* Decode GEMV on Q5_K weights: as q4k_gemv (same x, y, m, n, k, tolerance
- * and errors) with w a Q5_K matrix [n, k], 16-byte aligned. */
+ * and errors; the same two kernel families by m) with w a Q5_K matrix
+ * [n, k], 16-byte aligned. */
 int q5k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
 
@@ -196,7 +208,8 @@ int q5k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
 
 /* Decode GEMV on Q6_K weights: as q4k_gemv (same x, y, m, n, k, tolerance
  * and errors) with w a Q6_K matrix [n, k], 16-byte aligned.  A batch (m > 1)
- * streams W once per 4 x rows. */
+ * streams W once per 4 x rows.  Each sub-block's scale multiplies a sum of
+ * exact (q - 32) x products, so a zero weight adds exactly zero. */
 int q6k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
 
@@ -231,7 +244,8 @@ int q6k_dequantize_bf16(const void* w, uint16_t* out, int64_t n, int64_t k,
 
 /* Decode GEMV on Q3_K weights: as q4k_gemv (same x, y, m, n, k, tolerance
  * and errors) with w a Q3_K matrix [n, k], 16-byte aligned.  A batch (m > 1)
- * streams W once per 4 x rows. */
+ * streams W once per 4 x rows.  Each sub-block's scale multiplies a sum of
+ * exact (q - 4) x products, so a zero weight adds exactly zero. */
 int q3k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
 

@@ -51,7 +51,7 @@ def test_header_constants_match_binding():
     for name in ("Q4K_OK", "Q4K_ERR_INVALID_ARG", "Q4K_ERR_ALIGN", "Q4K_ERR_DEVICE",
                  "Q4K_ERR_LAUNCH", "Q4K_QK", "Q4K_BLOCK_BYTES", "Q4K_GEMV_MAX_M",
                  "Q5K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "Q3K_BLOCK_BYTES", "W8A8_K_STEP",
-                 "W8A8_MAX_K"):
+                 "W8A8_MAX_K", "Q4K_MAX_N", "Q4K_GEMM_MAX_K"):
         mm = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
         assert mm, name
         assert int(mm.group(1)) == getattr(_lib, name), name
@@ -249,3 +249,52 @@ def test_plane_gemms_reject_bad_arguments():
         assert fn(A, 2 * A, 3 * A, 8, 16, 300, None) == _lib.Q4K_ERR_INVALID_ARG
         assert fn(A + 2, 2 * A, 3 * A, 8, 16, 256, None) == _lib.Q4K_ERR_ALIGN
         assert fn(A, 2 * A, A + 16 * blk - 16, 8, 16, 256, None) == _lib.Q4K_ERR_INVALID_ARG  # y in w
+
+
+def test_gemms_reject_k_past_the_stated_limit():
+    # A 256-row weight tile must span < 4 GiB (in-tile offsets are 32-bit, the
+    # tile base 64-bit): k above Q4K_GEMM_MAX_K is refused for every format.
+    big_k = _lib.Q4K_GEMM_MAX_K + 256
+    for name in ("q4k_gemm", "q5k_gemm", "q6k_gemm", "q3k_gemm"):
+        fn = getattr(_lib, name)
+        assert fn(A, 2 * A, 3 * A, 8, 16, big_k, None) == _lib.Q4K_ERR_INVALID_ARG, name
+        assert "Q4K_GEMM_MAX_K" in _lib.q4k_last_error()
+    assert 256 * (_lib.Q4K_GEMM_MAX_K // 256) * 176 < 2 ** 32  # largest record, Q5_K
+
+
+def test_n_past_the_stated_limit_is_rejected():
+    n = _lib.Q4K_MAX_N + 1
+    assert _lib.q4k_gemv(A, 2 * A, 3 * A, 1, n, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.q4k_gemm(A, 2 * A, 3 * A, 8, n, 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert _lib.Q4K_MAX_N + 65536 == 2 ** 31 - 1
+
+
+def test_gemm_weight_offsets_are_tile_relative():
+    # The LDS-copy GEMM kernels form each weight row's byte offset from a
+    # 64-bit tile base, never as a 32-bit row * row_bytes over the whole matrix.
+    src = open(os.path.join(ROOT, "gemm_q4_super_block_amd", "csrc", "k_gemm.hip")).read()
+    assert "static_cast<uint32_t>(min(n0 + col" not in src
+    assert src.count("w + static_cast<size_t>(n0) * row_bytes") == 2
+
+
+class _FakeTensor:
+    """Stands in for a CUDA tensor so the binding's output checks run on the CPU."""
+
+    def __init__(self, shape, dtype=torch.float32, device="cuda:0"):
+        self.shape = torch.Size(shape)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.is_cuda = True
+
+    def is_contiguous(self):
+        return True
+
+
+def test_binding_output_checks():
+    from gemm_q4_super_block_amd import ops
+    dev = torch.device("cuda:0")
+    ops._out_tensor(_FakeTensor((3, 64)), torch.float32, (3, 64), dev, "out")
+    for bad in (_FakeTensor((3, 63)), _FakeTensor((192,)), _FakeTensor((3, 64), torch.float64),
+                _FakeTensor((3, 64), device="cuda:1")):
+        with pytest.raises(ValueError):
+            ops._out_tensor(bad, torch.float32, (3, 64), dev, "out")

@@ -129,7 +129,7 @@ def test_graph_split_k_replay_matches_oracle(q4k):
 
 
 def test_graph_sibling_formats_and_w8a8_replay(q4k):
-    # The other families under capture: the scale-flush GEMV, the Q5_K, Q6_K and
+    # The other families under capture: the split-bf16 MFMA GEMV, the Q5_K, Q6_K and
     # Q3_K GEMVs (batched passes), their LDS-dequant GEMMs (split K with its
     # zeroing kernel, and without), the dequant exports, and the INT8 layer and
     # row quantizer.  Outputs allocated inside the capture live in the graph's

@@ -1,0 +1,73 @@
+"""A Q4_K weight matrix larger than 4 GiB through the GEMV and GEMM kernels.
+
+The pages warn of 32-bit offsets on large tensors ("Writing an ESIMD Fused
+Kernel From Reverse-Engineered Assembly", "The ABI Adapter and the int32
+Overflow").  Here W has 1,900,000 rows of k = 4096 (4.38 GB): rows past the
+4 GiB byte boundary (row 1,864,136 on) are checked against the oracle at
+sampled columns, with the batch shapes that take each kernel family.  The
+matrix is a 10,007-row seeded block (a prime period, so a row offset that
+wrapped at 2^32 -- which lands mid-row -- cannot alias a correct row) tiled
+on the device.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+N, K, PERIOD = 1_900_000, 4096, 10_007
+ROW_BYTES = K // 256 * 144
+FIRST_ROW_PAST_4G = (1 << 32) // ROW_BYTES + 1
+
+
+@pytest.fixture(scope="module")
+def big():
+    if torch.cuda.device_count() == 0:
+        pytest.skip("no GPU")
+    import gemm_q4_super_block_amd as lib
+    lib.load_library()
+    torch.cuda.set_device(0)
+    base = synth.q4k_weights(PERIOD, K, seed=11)
+    wd = torch.empty((N, ROW_BYTES), dtype=torch.uint8, device="cuda")
+    bd = torch.from_numpy(base).cuda()
+    for r0 in range(0, N, PERIOD):
+        r1 = min(N, r0 + PERIOD)
+        wd[r0:r1].copy_(bd[: r1 - r0])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, FIRST_ROW_PAST_4G - 1, FIRST_ROW_PAST_4G, N - 1],
+                                     np.random.default_rng(5).integers(FIRST_ROW_PAST_4G, N, 12)]))
+    yield lib, wd, base, rows
+    del wd, bd
+    torch.cuda.empty_cache()
+
+
+def test_matrix_is_past_4gib(big):
+    _, wd, _, _ = big
+    assert wd.numel() > (1 << 32)
+    assert FIRST_ROW_PAST_4G * ROW_BYTES >= (1 << 32) > (FIRST_ROW_PAST_4G - 1) * ROW_BYTES
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_gemv_rows_past_4gib(big, m):
+    lib, wd, base, rows = big
+    x = synth.normal_f32((m, K), seed=m)
+    y = lib.gemv(wd, torch.from_numpy(x).cuda()).cpu().numpy()
+    yr, a = oracle.gemv_rows(base, x, PERIOD, K, rows % PERIOD)
+    err = np.abs(y[:, rows] - yr)
+    assert np.all(err <= 1e-4 * a), "worst %g" % (err / (1e-4 * a)).max()
+
+
+@pytest.mark.parametrize("m", [8, 256])
+def test_gemm_rows_past_4gib(big, m):
+    lib, wd, base, rows = big
+    xb = synth.normal_bf16((m, K), seed=m)
+    xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    y = lib.gemm(wd, xt).cpu().numpy()
+    yr, a = oracle.gemm_cols(base, xb, PERIOD, K, rows % PERIOD)
+    err = np.abs(y[:, rows] - yr)
+    assert np.all(err <= 1e-2 * a), "worst %g" % (err / (1e-2 * a)).max()

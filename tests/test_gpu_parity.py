@@ -118,13 +118,14 @@ def test_gemv_config_small(q4k, seed):
     assert_within(y, yr[0], a[0], GEMV_TOL, "gemv 256x1024 seed %d" % seed)
 
 
-def test_gemv_decode_4096(q4k):
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gemv_decode_4096(q4k, seed):
     n = k = 4096
-    w = synth.q4k_weights(n, k, seed=0)
-    x = synth.normal_f32(k, seed=0)
+    w = synth.q4k_weights(n, k, seed=seed)
+    x = synth.normal_f32(k, seed=seed)
     y = q4k.gemv(dev(w), dev(x)).cpu().numpy()
     yr, a = oracle.gemv(w, x, n, k)
-    assert_within(y, yr[0], a[0], GEMV_TOL, "gemv 4096x4096")
+    assert_within(y, yr[0], a[0], GEMV_TOL, "gemv 4096x4096 seed %d" % seed)
 
 
 # Batch 1 runs three launch shapes: up to 8192 rows (16 waves per workgroup),
@@ -152,17 +153,18 @@ def test_gemv_batched(q4k, m):
     assert_within(y, yr, a, GEMV_TOL, "gemv m=%d" % m)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
-def test_gemv_sweep_shape_sampled(q4k, m):
+def test_gemv_sweep_shape_sampled(q4k, m, seed):
     # 14336 x 4096 weights, fp32 X [m, 4096]; oracle on sampled output rows
     n, k = 14336, 4096
-    w = synth.q4k_weights(n, k, seed=0)
-    x = synth.normal_f32((m, k), seed=0)
+    w = synth.q4k_weights(n, k, seed=seed)
+    x = synth.normal_f32((m, k), seed=seed)
     y = q4k.gemv(dev(w), dev(x)).cpu().numpy()
     rows = np.unique(np.concatenate([[0, 1, n - 1, n - 2],
-                                     np.random.default_rng(m).integers(0, n, 96)]))
+                                     np.random.default_rng(m + seed).integers(0, n, 96)]))
     yr, a = oracle.gemv_rows(w, x, n, k, rows)
-    assert_within(y[:, rows], yr, a, GEMV_TOL, "sweep gemv m=%d" % m)
+    assert_within(y[:, rows], yr, a, GEMV_TOL, "sweep gemv m=%d seed %d" % (m, seed))
 
 
 def test_gemv_unit_vectors_give_columns(q4k):
@@ -176,6 +178,22 @@ def test_gemv_unit_vectors_give_columns(q4k):
         x[c] = 1.0
         y = q4k.gemv(wd, dev(x)).cpu().numpy()
         assert np.array_equal(y, W[:, c]), c
+
+
+def test_gemv_split_unit_vectors_within_weight_split(q4k):
+    # Batches of 5..32 rows take the split-bf16 MFMA kernel: for x = e_c the
+    # output is w_hi + w_lo of each weight of column c, within 2^-16 |w|
+    # (and exactly 0 where the weight is 0).
+    n, k = 40, 512
+    w = synth.q4k_weights(n, k, seed=22)
+    W = oracle.dequant_f32(w, n, k).astype(np.float64)
+    cols = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 300, 511]
+    x = np.zeros((len(cols), k), np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    y = q4k.gemv(dev(w), dev(x)).cpu().numpy()
+    for i, c in enumerate(cols):
+        assert np.all(np.abs(y[i] - W[:, c]) <= 2.0 ** -16 * np.abs(W[:, c])), c
 
 
 # ------------------------------------------------------------------ SwiGLU MLP
@@ -214,9 +232,10 @@ def test_swiglu_mlp_small(q4k, dm, dff, seed):
     _mlp_check(q4k, dm, dff, seed)
 
 
-def test_swiglu_mlp_llama_shape(q4k):
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_swiglu_mlp_llama_shape(q4k, seed):
     # d_model 4096, d_ff 14336 (the decode MLP configuration), full oracle
-    _mlp_check(q4k, 4096, 14336, 0)
+    _mlp_check(q4k, 4096, 14336, seed)
 
 
 def test_swiglu_mlp_large_activations(q4k):
@@ -237,17 +256,18 @@ def test_gemm_small_shapes(q4k, m, n, k):
     assert_within(Y, Yr, A, GEMM_TOL, "gemm %dx%dx%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("n", [4096, 14336])
-def test_gemm_prefill_sampled(q4k, n):
+def test_gemm_prefill_sampled(q4k, n, seed):
     # X bf16 [512, 4096], W [n, 4096]: all 512 rows at 64 sampled columns
     m, k = 512, 4096
-    w = synth.q4k_weights(n, k, seed=0)
-    xb = synth.normal_bf16((m, k), seed=0)
+    w = synth.q4k_weights(n, k, seed=seed)
+    xb = synth.normal_bf16((m, k), seed=seed)
     Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
     cols = np.unique(np.concatenate([[0, 1, 127, 128, n - 1],
-                                     np.random.default_rng(n).integers(0, n, 59)]))
+                                     np.random.default_rng(n + seed).integers(0, n, 59)]))
     Yr, A = oracle.gemm_cols(w, xb, n, k, cols)
-    assert_within(Y[:, cols], Yr, A, GEMM_TOL, "gemm 512x%dx4096" % n)
+    assert_within(Y[:, cols], Yr, A, GEMM_TOL, "gemm 512x%dx4096 seed %d" % (n, seed))
     assert np.all(np.isfinite(Y))
 
 
@@ -324,15 +344,17 @@ def test_gemm_xcd_blocked_grids_full_output(q4k, m, n, k):
     assert_within(Y, Yr, A, GEMM_TOL, "gemm %dx%dx%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
-def test_gemm_sweep_shape_sampled(q4k, m):
+def test_gemm_sweep_shape_sampled(q4k, m, seed):
     n, k = 14336, 4096
-    w = synth.q4k_weights(n, k, seed=0)
-    xb = synth.bf16_bits(synth.normal_f32((m, k), seed=0))
+    w = synth.q4k_weights(n, k, seed=seed)
+    xb = synth.bf16_bits(synth.normal_f32((m, k), seed=seed))
     Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
-    cols = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(m).integers(0, n, 62)]))
+    cols = np.unique(np.concatenate([[0, n - 1],
+                                     np.random.default_rng(m + seed).integers(0, n, 62)]))
     Yr, A = oracle.gemm_cols(w, xb, n, k, cols)
-    assert_within(Y[:, cols], Yr, A, GEMM_TOL, "sweep gemm m=%d" % m)
+    assert_within(Y[:, cols], Yr, A, GEMM_TOL, "sweep gemm m=%d seed %d" % (m, seed))
 
 
 def test_gemm_m1_equals_bf16_weight_dot(q4k):
@@ -398,30 +420,30 @@ def test_gemm_long_k(q4k):
     assert_within(Y[:, cols], Yr, A, GEMM_TOL, "gemm 64x512x16384")
 
 
-# ------------------------------------------------------------------ scale flush
+# ------------------------------------------------------------------ split-bf16 MFMA GEMV
 
-# Q4_K batches of 4..32 rows run on bf16 MFMA with x split into bf16 hi + lo
-# and the sub-block scales flushed into the fp32 accumulator.  Edges: one
+# Q4_K batches of 5..32 rows run on bf16 MFMA with the exact fp32 weights and
+# x each split into bf16 hi + lo (three MFMAs per tile).  Edges: one
 # super-block (only the first of the four K-split waves has work), a block
 # count not divisible by four, single and ragged 16-row weight tiles, batch
 # sizes around the 16-row MFMA tile, matrices past 8192 rows (two weight
 # tiles per workgroup, ragged), and x spanning six decades.
-@pytest.mark.parametrize("m,n,k", [(6, 1, 256), (15, 17, 256), (16, 33, 1280), (17, 16, 4352),
-                                   (32, 15, 768), (7, 4096, 4096), (24, 500, 2048),
-                                   (6, 8200, 512), (20, 8192, 256)])
-def test_gemv_flush_edges(q4k, m, n, k):
+@pytest.mark.parametrize("m,n,k", [(5, 1, 256), (6, 1, 256), (15, 17, 256), (16, 33, 1280),
+                                   (17, 16, 4352), (32, 15, 768), (7, 4096, 4096),
+                                   (24, 500, 2048), (5, 8200, 512), (20, 8192, 256)])
+def test_gemv_split_edges(q4k, m, n, k):
     w = synth.q4k_weights(n, k, seed=m + n)
     x = synth.normal_f32((m, k), seed=m + n)
     y = q4k.gemv(dev(w), dev(x)).cpu().numpy()
     yr, a = oracle.gemv(w, x, n, k)
-    assert_within(y, yr, a, GEMV_TOL, "flush gemv m=%d %dx%d" % (m, n, k))
+    assert_within(y, yr, a, GEMV_TOL, "split gemv m=%d %dx%d" % (m, n, k))
 
 
-def test_gemv_flush_wide_dynamic_range(q4k):
+def test_gemv_split_wide_dynamic_range(q4k):
     m, n, k = 8, 64, 1024
     w = synth.q4k_weights(n, k, seed=77)
     g = synth.rng(77, synth.X)
     x = (synth.normal_f32((m, k), seed=77) * 10.0 ** g.uniform(-3, 3, (m, k))).astype(np.float32)
     y = q4k.gemv(dev(w), dev(x)).cpu().numpy()
     yr, a = oracle.gemv(w, x, n, k)
-    assert_within(y, yr, a, GEMV_TOL, "flush gemv, x over six decades")
+    assert_within(y, yr, a, GEMV_TOL, "split gemv, x over six decades")

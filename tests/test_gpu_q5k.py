@@ -110,17 +110,25 @@ def test_q5k_gemv_batched(q4k, m):
 
 
 def test_q5k_gemv_unit_vectors_give_columns(q4k):
-    # y(e_c) is column c of the dequantized W (one non-zero product per row)
+    # y(e_c) is column c of the dequantized W (one non-zero product per row):
+    # exactly on the fp32 FMA path (batches of up to 4 rows); on the split-bf16
+    # MFMA path (5 rows and more) it is w_hi + w_lo, within 2^-16 |w| of w.
     n, k = 40, 512
     w = synth.q5k_weights(n, k, seed=3)
     W = oracle.q5k_dequant_f32(w, n, k)
+    wd = dev(w)
     cols = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 300, 511]
     x = np.zeros((len(cols), k), np.float32)
     for i, c in enumerate(cols):
         x[i, c] = 1.0
-    y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
+    for i0 in range(0, len(cols), 4):
+        y = q4k.q5k_gemv(wd, dev(x[i0:i0 + 4])).cpu().numpy()
+        for i, c in enumerate(cols[i0:i0 + 4]):
+            assert np.array_equal(y[i], W[:, c]), c
+    y = q4k.q5k_gemv(wd, dev(x)).cpu().numpy()
     for i, c in enumerate(cols):
-        assert np.array_equal(y[i], W[:, c]), c
+        err = np.abs(y[i].astype(np.float64) - W[:, c])
+        assert np.all(err <= 2.0 ** -16 * np.abs(W[:, c])), c
 
 
 GEMM_TOL = 1e-2
@@ -177,13 +185,13 @@ def test_q5k_gemv_multi_chunk_k(q4k):
 
 
 @pytest.mark.parametrize("m,n,k", [(6, 8200, 512), (17, 40, 1280), (32, 4096, 1024)])
-def test_q5k_gemv_flush_batches(q4k, m, n, k):
-    # batches of 6..32 rows take the scale-flush MFMA kernel (5-bit quants in bf16)
+def test_q5k_gemv_split_batches(q4k, m, n, k):
+    # batches of 5..32 rows take the split-bf16 MFMA kernel
     w = synth.q5k_weights(n, k, seed=m + 3)
     x = synth.normal_f32((m, k), seed=m + 3)
     y = q4k.q5k_gemv(dev(w), dev(x)).cpu().numpy()
     yr, a = oracle.q5k_gemv(w, x, n, k)
-    assert_within(y, yr, a, GEMV_TOL, "q5k flush gemv m=%d %dx%d" % (m, n, k))
+    assert_within(y, yr, a, GEMV_TOL, "q5k split gemv m=%d %dx%d" % (m, n, k))
 
 
 # Grids that take the K-slice kernels on 176-byte records: m <= 32 with at
