@@ -23,6 +23,7 @@ Q4K_BLOCK_BYTES = 144
 Q4K_GEMV_MAX_M = 32
 Q4K_MAX_N = 2147418111
 Q4K_GEMM_MAX_K = 16777216
+Q4K_NOALLOC_MAX_D_FF = 65536
 Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
 Q3K_BLOCK_BYTES = 110
@@ -40,6 +41,7 @@ SIGNATURES = {
     "q4k_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q4k_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q4k_swiglu_mlp": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp]),
+    "q4k_swiglu_mlp_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "q4k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q4k_dequantize_bf16": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "q4k_read_probe": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
@@ -135,6 +137,10 @@ def q4k_gemm(w, x_bf16, y, m, n, k, stream) -> int:
 
 def q4k_swiglu_mlp(w_gate, w_up, w_down, x, h, out, d_model, d_ff, stream) -> int:
     return load().q4k_swiglu_mlp(w_gate, w_up, w_down, x, h, out, d_model, d_ff, stream)
+
+
+def q4k_swiglu_mlp_noalloc(w_gate, w_up, w_down, x, out, d_model, d_ff, stream) -> int:
+    return load().q4k_swiglu_mlp_noalloc(w_gate, w_up, w_down, x, out, d_model, d_ff, stream)
 
 
 def q4k_dequantize_f32(w, out, n, k, stream) -> int:

@@ -223,31 +223,107 @@ int q3k_gemm(const void* w, const uint16_t* x_bf16, float* y, int64_t m, int64_t
                   "q3k_gemm");
 }
 
-int q4k_swiglu_mlp(const void* w_gate, const void* w_up, const void* w_down, const float* x,
-                   float* h, float* out, int64_t d_model, int64_t d_ff, void* stream) {
+// Host checks of the SwiGLU MLP's arguments (h may be the library's own
+// scratch, in which case the caller passes h_bytes = 0 to skip its overlap
+// checks: the device array overlaps no caller buffer).
+static int mlp_checks(const char* what, const void* w_gate, const void* w_up, const void* w_down,
+                      const float* x, const float* h, size_t h_bytes, const float* out,
+                      int64_t d_model, int64_t d_ff) {
   if (!w_gate || !w_up || !w_down || !x || !h || !out)
-    return fail(Q4K_ERR_INVALID_ARG, "q4k_swiglu_mlp: null pointer");
+    return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
   if (!valid_k(d_model) || !valid_k(d_ff))
     return fail(Q4K_ERR_INVALID_ARG,
-                "q4k_swiglu_mlp: d_model=%lld and d_ff=%lld must be positive multiples of 256",
+                "%s: d_model=%lld and d_ff=%lld must be positive multiples of 256", what,
                 (long long)d_model, (long long)d_ff);
   if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(x) ||
       !aligned16(h) || !aligned16(out))
-    return fail(Q4K_ERR_ALIGN, "q4k_swiglu_mlp: all pointers must be 16-byte aligned");
-  const size_t nh = static_cast<size_t>(d_ff) * 4, no = static_cast<size_t>(d_model) * 4;
+    return fail(Q4K_ERR_ALIGN, "%s: all pointers must be 16-byte aligned", what);
+  const size_t no = static_cast<size_t>(d_model) * 4;
   const size_t nw = q4k_bytes(d_ff, d_model);
-  if (overlap(h, nh, x, no) || overlap(h, nh, w_gate, nw) || overlap(h, nh, w_up, nw) ||
-      overlap(h, nh, w_down, nw) || overlap(out, no, x, no) || overlap(out, no, h, nh) ||
-      overlap(out, no, w_gate, nw) || overlap(out, no, w_up, nw) || overlap(out, no, w_down, nw))
-    return fail(Q4K_ERR_INVALID_ARG, "q4k_swiglu_mlp: h or out overlaps another buffer");
-  if (int rc = check_device()) return rc;
+  if (overlap(h, h_bytes, x, no) || overlap(h, h_bytes, w_gate, nw) ||
+      overlap(h, h_bytes, w_up, nw) || overlap(h, h_bytes, w_down, nw) ||
+      overlap(out, no, x, no) || overlap(out, no, h, h_bytes) || overlap(out, no, w_gate, nw) ||
+      overlap(out, no, w_up, nw) || overlap(out, no, w_down, nw))
+    return fail(Q4K_ERR_INVALID_ARG, "%s: h or out overlaps another buffer", what);
+  return Q4K_OK;
+}
+
+// Gate/up + SwiGLU into h, then the down projection of h into out.
+static int mlp_launch(const char* what, const void* w_gate, const void* w_up, const void* w_down,
+                      const float* x, float* h, float* out, int64_t d_model, int64_t d_ff,
+                      void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = q4k::launch_gateup_swiglu(static_cast<const uint8_t*>(w_gate),
                                            static_cast<const uint8_t*>(w_up), x, h, d_model,
                                            d_ff, s);
-  if (e != hipSuccess) return launched(e, "q4k_swiglu_mlp (gate/up)");
+  if (e != hipSuccess) return launched(e, what);
   e = q4k::launch_gemv(static_cast<const uint8_t*>(w_down), h, out, 1, d_model, d_ff, s);
-  return launched(e, "q4k_swiglu_mlp (down)");
+  return launched(e, what);
+}
+
+int q4k_swiglu_mlp(const void* w_gate, const void* w_up, const void* w_down, const float* x,
+                   float* h, float* out, int64_t d_model, int64_t d_ff, void* stream) {
+  const char* what = "q4k_swiglu_mlp";
+  if (int rc = mlp_checks(what, w_gate, w_up, w_down, x, h, static_cast<size_t>(d_ff) * 4, out,
+                          d_model, d_ff))
+    return rc;
+  if (int rc = check_device()) return rc;
+  return mlp_launch(what, w_gate, w_up, w_down, x, h, out, d_model, d_ff, stream);
+}
+
+// ---- the SwiGLU MLP without allocation -------------------------------------
+// h lives in `scratch`, a file-scope device array (each device holds its own
+// copy for the life of the process).  Host code never passes the array's name
+// to a kernel: the name is a host-side stand-in.  The device address is read
+// once per device with hipGetSymbolAddress and kept in g_scratch[dev].
+}  // extern "C"
+
+namespace {
+static __device__ __align__(256) float scratch[Q4K_NOALLOC_MAX_D_FF];
+std::atomic<float*> g_scratch[kMaxDevices];
+
+// This device's address of `scratch`, resolved on first use with the device
+// current; nullptr (and the last-error string set) if the runtime refuses.
+float* scratch_address(int dev) {
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* a = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !a) {
+    (void)hipGetLastError();
+    fail(Q4K_ERR_DEVICE, "q4k_swiglu_mlp_noalloc: hipGetSymbolAddress failed on device %d: %s",
+         dev, hipGetErrorString(e));
+    return nullptr;
+  }
+  p = static_cast<float*>(a);
+  g_scratch[dev].store(p, std::memory_order_release);  // same value if two threads race
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+int q4k_swiglu_mlp_noalloc(const void* w_gate, const void* w_up, const void* w_down,
+                           const float* x, float* out, int64_t d_model, int64_t d_ff,
+                           void* stream) {
+  const char* what = "q4k_swiglu_mlp_noalloc";
+  if (d_ff > Q4K_NOALLOC_MAX_D_FF)
+    return fail(Q4K_ERR_INVALID_ARG, "%s: d_ff=%lld is above Q4K_NOALLOC_MAX_D_FF=%d", what,
+                (long long)d_ff, Q4K_NOALLOC_MAX_D_FF);
+  // The scratch address stands in for h in the pointer checks (it is aligned
+  // and overlaps no caller buffer); resolve it only after the device check.
+  static const float kAligned[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  if (int rc = mlp_checks(what, w_gate, w_up, w_down, x, kAligned, 0, out, d_model, d_ff))
+    return rc;
+  if (int rc = check_device()) return rc;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(Q4K_ERR_DEVICE, "%s: cannot query the current HIP device", what);
+  }
+  float* h = scratch_address(dev);
+  if (!h) return Q4K_ERR_DEVICE;
+  return mlp_launch(what, w_gate, w_up, w_down, x, h, out, d_model, d_ff, stream);
 }
 
 static int dequant_checks(const char* what, const void* w, const void* out, int64_t n,

@@ -145,6 +145,26 @@ def swiglu_mlp(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
     return out, h
 
 
+def swiglu_mlp_noalloc(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                       x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """swiglu_mlp() with h in the library's device scratch: the entry point
+    allocates nothing, and `out` [d_model] is the caller's (so a call under
+    graph capture allocates nothing either).  Calls that overlap on one GPU
+    share the scratch and race."""
+    d_ff, d_model = _q4k_shape(w_gate)
+    if _q4k_shape(w_up) != (d_ff, d_model) or _q4k_shape(w_down) != (d_model, d_ff):
+        raise ValueError("gate/up must be [d_ff, d_model] and down [d_model, d_ff]")
+    _dev_tensor(x, torch.float32, "x")
+    _same_device(w_gate.device, ("w_up", w_up), ("w_down", w_down), ("x", x))
+    if x.dim() != 1 or x.numel() != d_model:
+        raise ValueError("x must be [d_model = %d]" % d_model)
+    _out_tensor(out, torch.float32, (d_model,), x.device, "out")
+    check(_lib.q4k_swiglu_mlp_noalloc(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(),
+                                      x.data_ptr(), out.data_ptr(), d_model, d_ff,
+                                      _stream(x.device)))
+    return out
+
+
 def dequantize_f32(w: torch.Tensor) -> torch.Tensor:
     """Dequantized W as fp32 [n, k]."""
     n, k = _q4k_shape(w)

@@ -139,6 +139,28 @@ int q4k_swiglu_mlp(const void* w_gate, const void* w_up, const void* w_down,
                    const float* x, float* h, float* out, int64_t d_model,
                    int64_t d_ff, void* stream);
 
+/* Largest d_ff of q4k_swiglu_mlp_noalloc (the size of its device scratch). */
+#define Q4K_NOALLOC_MAX_D_FF 65536
+
+/* The SwiGLU MLP for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * as q4k_swiglu_mlp, but h lives in the library's own scratch, a static
+ * device array of Q4K_NOALLOC_MAX_D_FF floats (256 KiB) that each GPU the
+ * library runs on holds until the process ends.  Nothing is allocated or
+ * freed on any call; the scratch address is resolved once per device
+ * (hipGetSymbolAddress) on the first call with that device current.
+ *   out fp32 [d_model]; the other arguments as for q4k_swiglu_mlp;
+ *   d_ff <= Q4K_NOALLOC_MAX_D_FF, else Q4K_ERR_INVALID_ARG.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (different streams, or threads without ordering) race on h and
+ * give wrong results; calls in one stream are ordered and safe.  h is written
+ * in full before it is read, so nothing needs clearing between calls.
+ * Errors as for q4k_swiglu_mlp, plus Q4K_ERR_DEVICE if the runtime cannot
+ * give the scratch address. */
+int q4k_swiglu_mlp_noalloc(const void* w_gate, const void* w_up, const void* w_down,
+                           const float* x, float* out, int64_t d_model, int64_t d_ff,
+                           void* stream);
+
 /* Diagnostic dequantization of W [n, k] to fp32 / to bf16 bit patterns,
  * row-major [n, k], through the same device routine the GEMM fills LDS with.
  * The fp32 result is the exact weight rounded once to nearest even; the bf16

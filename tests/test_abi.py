@@ -298,3 +298,13 @@ def test_binding_output_checks():
                 _FakeTensor((3, 64), device="cuda:1")):
         with pytest.raises(ValueError):
             ops._out_tensor(bad, torch.float32, (3, 64), dev, "out")
+
+
+def test_noalloc_mlp_rejects_bad_arguments():
+    fn = _lib.q4k_swiglu_mlp_noalloc
+    good = (A, 2 * A, 3 * A, 4 * A, 5 * A, 256, 512)
+    assert fn(0, *good[1:], None) == _lib.Q4K_ERR_INVALID_ARG
+    assert fn(*good[:5], 256, _lib.Q4K_NOALLOC_MAX_D_FF + 256, None) == _lib.Q4K_ERR_INVALID_ARG
+    assert "Q4K_NOALLOC_MAX_D_FF" in _lib.q4k_last_error()
+    assert fn(*good[:4], 5 * A + 4, 256, 512, None) == _lib.Q4K_ERR_ALIGN
+    assert fn(*good[:4], 4 * A, 256, 512, None) == _lib.Q4K_ERR_INVALID_ARG  # out == x
