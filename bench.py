@@ -17,15 +17,17 @@ the 256 MB MALL and the 4 MB L2 per XCD), so each launch reads cold HBM.
 Timing: W warm-up steps, then K steps bracketed by a device synchronize.  The
 K launches of one kernel run back to back on the launch stream between two
 HIP events; the per-launch average is that kernel's duration (launch gaps
-included).  The K launches are captured once into a HIP graph and the replay
-is timed, so that the host's per-launch cost (Python, ctypes, argument
-checks) does not throttle kernels of a few microseconds; the same launches
-enqueued one by one are timed as well and reported as ``eager_us``.
+included) and the roofline figures use it.  Beside it, per kernel: the
+per-dispatch device durations (median, p10, p90 of the K dispatches, from the
+runtime's activity trace through torch.profiler -- the timestamps rocprofv3's
+kernel trace reads) and the same K launches replayed from one HIP graph.
 ``value`` is the decode GEMV's effective HBM bandwidth (algorithmic bytes /
-average duration).  The parity spot check reads the outputs the last graph
-replay wrote.
+average duration).  The parity spot check reads the outputs of the last
+launch.  The CPU baseline times the oracle on the host's cores (one thread and
+all of them) on the decode GEMV, the MLP and the prefill GEMM.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--only LIST] [--eager-only] [--no-dispatch-trace]
 """
 from __future__ import annotations
 
@@ -52,6 +54,21 @@ W8A8_N = W8A8_K = 3072
 W8A8_M = (1024, 8192)
 
 
+# The source pages' own numbers for this computation, on their hardware: context for the
+# reader, not targets (no page reports a Q4_K GB/s or TFLOP/s, so vs_baseline is null).
+PAGES_CONTEXT = [
+    {"figure": "2.04 -> 2.21 tokens/s decode after the improved Q4_K quant loading",
+     "hardware": "Intel Arc GPUs (ESIMD/SYCL)",
+     "source": "Writing an ESIMD Fused Kernel From Reverse-Engineered Assembly, Getting Q4_K Right"},
+    {"figure": "pp512 1.18x and tg128 1.04x of llama.cpp (gemma-4-12B Q4_K_M)",
+     "hardware": "AMD zen2 Threadripper 3990X (CPU)",
+     "source": "CPU kernel parity: decode and tile kernels at llama.cpp speed, Validation"},
+    {"figure": "INT8 W8A8 linear 15-17% faster than BF16 at M = 1024 (K = N = 3072)",
+     "hardware": "Intel Arc B580 (Xe2)",
+     "source": "xpu-kernels, Headline result"},
+]
+
+
 def q4k_bytes(n, k):
     return n * (k // 256) * 144
 
@@ -75,6 +92,8 @@ def parse():
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
     p.add_argument("--eager-only", action="store_true",
                    help="time only the eagerly enqueued launches (no HIP graph replay)")
+    p.add_argument("--no-dispatch-trace", action="store_true",
+                   help="skip the per-dispatch device-duration pass (torch.profiler)")
     p.add_argument("--summarize-profile", nargs="+", metavar="DIR",
                    help="summarize rocprofv3 output directories (kernel trace, then optional "
                         "FETCH_SIZE and WRITE_SIZE counter runs) instead of benchmarking")
@@ -317,6 +336,12 @@ def main():
             rot = Rotor(torch, [synth.q4k_weights(n, k, seed=0)], nbytes)
             kernels.append(("read_probe_%d" % nbytes, read_probe_runner(_lib, rot, nbytes, torch),
                             nbytes, 0, rot))
+        # 1 GiB, four times the MALL: the rate HBM sustains once launch and ramp costs
+        # are amortized (the asymptotic read ceiling)
+        nbytes = 1 << 30
+        rot = Rotor(torch, [np.full(nbytes, 3, np.uint8)], nbytes)
+        kernels.append(("read_probe_%d" % nbytes, read_probe_runner(_lib, rot, nbytes, torch),
+                        nbytes, 0, rot))
 
     if args.copy_probe:
         # one elementwise kernel that reads 256 MiB and writes 256 MiB: the reference
@@ -335,27 +360,18 @@ def main():
             run(s, sp)
     torch.cuda.synchronize()
 
-    # Timed region, two ways, each kernel's K launches back to back between two
-    # HIP events on the launch stream:
-    #   * graph (reported): the K launches are captured once into a HIP graph
-    #     and replayed, so host-side launch cost does not throttle short kernels;
-    #   * eager: the K launches are enqueued one by one from Python.
-    # The per-launch average (launch gaps included) is the kernel's duration.
-    graphs = []
-    if not args.eager_only:
-        cap = torch.cuda.Stream()
-        for name, run, *_ in kernels:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                for s in range(args.steps):
-                    run(args.warmup + s, cap.cuda_stream)
-            graphs.append(g)
-        for g in graphs:  # first replay uploads the graph
-            g.replay()
-        torch.cuda.synchronize()
+    # Timed region: each kernel's K launches back to back on the launch stream
+    # (torch's current stream), between two HIP events recorded on that stream.
+    # The per-launch average (launch gaps included) is the kernel's duration,
+    # the figure the roofline fractions use.  Besides it:
+    #   * the same K launches captured once into a HIP graph and replayed
+    #     (graph_us: what a caller that records its decode step pays);
+    #   * per-dispatch device durations (start to end timestamps of every
+    #     dispatch, from the runtime's activity trace through torch.profiler,
+    #     the same timestamps rocprofv3's kernel trace reads): median, p10 and
+    #     p90 over the K launches (dispatch_us).
     ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa: E731
     eager_ev = [ev() for _ in kernels]
-    graph_ev = [ev() for _ in kernels]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for (name, run, *_), (e0, e1) in zip(kernels, eager_ev):
@@ -364,21 +380,43 @@ def main():
             run(args.warmup + s, sp)
         e1.record(stream)
     torch.cuda.synchronize()
-    for g, (e0, e1) in zip(graphs, graph_ev):
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    graph_ms = [None] * len(kernels)
+    if not args.eager_only:
+        cap = torch.cuda.Stream()
+        graph_ev = [ev() for _ in kernels]
+        for i, (name, run, *_) in enumerate(kernels):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for s in range(args.steps):
+                    run(args.warmup + s, cap.cuda_stream)
+            g.replay()  # the first replay uploads the graph
+            torch.cuda.synchronize()
+            e0, e1 = graph_ev[i]
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            graph_ms[i] = e0.elapsed_time(e1)
+            del g
+    dispatch = [None] * len(kernels)
+    if not args.no_dispatch_trace:
+        for i, (name, run, *_) in enumerate(kernels):
+            dispatch[i] = dispatch_durations(torch, lambda run=run: [
+                run(args.warmup + s, sp) for s in range(args.steps)], args.steps)
 
     per = {}
     total_ms = 0.0
     for i, (name, run, nbytes, flop, rot) in enumerate(kernels):
-        eager_ms = eager_ev[i][0].elapsed_time(eager_ev[i][1])
-        ms = graph_ev[i][0].elapsed_time(graph_ev[i][1]) if graphs else eager_ms
+        ms = eager_ev[i][0].elapsed_time(eager_ev[i][1])
         total_ms += ms
         us = ms * 1e3 / args.steps
-        r = {"us": round(us, 3), "eager_us": round(eager_ms * 1e3 / args.steps, 3), "copies": rot.count}
+        r = {"us": round(us, 3), "copies": rot.count}
+        if graph_ms[i] is not None:
+            r["graph_us"] = round(graph_ms[i] * 1e3 / args.steps, 3)
+        if dispatch[i]:
+            r["dispatch_us"] = dispatch[i]
         if nbytes:
             r["gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
             r["hbm_frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
@@ -395,6 +433,7 @@ def main():
 
     head = per.get("gemv_4096x4096")
     gemm = per.get("gemm_512x4096x4096")
+    mlp = per.get("swiglu_mlp_4096_14336")
     w8 = per.get("w8a8_linear_%dx%dx%d" % (W8A8_M[0], W8A8_N, W8A8_K))
     value = head["gbs"] if head else None
     cpu = None if args.no_cpu_baseline or not head else cpu_baseline(args, np)
@@ -402,6 +441,14 @@ def main():
     if all(("sweep_gemv_m%d" % m) in per and ("sweep_gemm_m%d" % m) in per for m in SWEEP_M):
         crossover = next((m for m in SWEEP_M
                           if per["sweep_gemm_m%d" % m]["us"] < per["sweep_gemv_m%d" % m]["us"]), None)
+
+    def timing(r):
+        t = {"eager_us": r["us"]}
+        if "graph_us" in r:
+            t["graph_us"] = r["graph_us"]
+        if "dispatch_us" in r:
+            t["dispatch_us"] = {key: r["dispatch_us"][key] for key in ("median", "p10", "p90", "n")}
+        return t
 
     out = {
         "metric": "Q4_K GEMV eff. HBM GB/s (% of peak); M=512 GEMM TFLOP/s (% MFMA peak)",
@@ -427,6 +474,11 @@ def main():
             "w8a8": "INT8 W8A8 linear, int8 x [M, 3072] and w [3072, 3072] with fp32 row scales "
                     "and bias -> bf16, M in %s; bf16 row quantizer at M = %d" % (list(W8A8_M), W8A8_M[0]),
         },
+        "timing_note": "us / gbs / tflops: the per-launch average of K back-to-back launches "
+                       "between HIP events on the launch stream (the roofline figures use it); "
+                       "dispatch_us: per-dispatch device durations (median, p10, p90) from the "
+                       "runtime's activity trace; graph_us: the same K launches replayed from "
+                       "one HIP graph",
         "percent_of_peak": {
             "gemv_hbm": round(100 * head["hbm_frac"], 2) if head else None,
             "gemm_m512_mfma_bf16": round(100 * gemm["mfma_frac"], 2) if gemm else None,
@@ -436,8 +488,10 @@ def main():
                              if name.startswith("read_probe_")} or None,
         "roofline": None,
         "roofline_gemm": None,
+        "roofline_mlp": None,
         "roofline_w8a8": None,
         "cpu_baseline": cpu,
+        "context": PAGES_CONTEXT,
         "kernels": per,
         "sweep_crossover_m": crossover,
         "parity_spot_check": check,
@@ -448,19 +502,26 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": head["hbm_frac"], "traffic": traffic("gemv_4096x4096"),
                            "kernel": "k_gemv_q4k<1, 1, false, 16, false, 4>",
-                           "bytes_per_launch": 9469952}
+                           "bytes_per_launch": 9469952, **timing(head)}
     if gemm:
         out["roofline_gemm"] = {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": gemm["mfma_frac"],
                                 "traffic": traffic("gemm_512x4096x4096"),
                                 "kernel": "k_gemm_q4k_kslice<2, 2, 4>",
-                                "flop_per_launch": 2 * 512 * 4096 * 4096}
+                                "flop_per_launch": 2 * 512 * 4096 * 4096, **timing(gemm)}
+    if mlp:
+        out["roofline_mlp"] = {"bound": "hbm", "achieved": mlp["gbs"], "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": mlp["hbm_frac"],
+                               "kernels": "k_gemv_q4k<1, 1, true, 8, false, 4> (gate/up + SwiGLU), "
+                                          "k_gemv_q4k<1, 1, false, 16, false, 4> (down)",
+                               "bytes_per_launch": 3 * q4k_bytes(D_FF, D_MODEL) + 4 * D_MODEL
+                               + 2 * 4 * D_FF + 4 * D_MODEL, **timing(mlp)}
     if w8:
         out["roofline_w8a8"] = {"bound": "mfma", "achieved": w8["tops"], "peak": INT8_PEAK_TOPS,
                                 "unit": "TOP/s", "frac": w8["mfma_frac"],
                                 "traffic": traffic("w8a8_linear_%dx%dx%d" % (W8A8_M[0], W8A8_N, W8A8_K)),
                                 "kernel": "k_w8a8_gemm<1, 1, 2, 1>",
-                                "op_per_launch": 2 * W8A8_M[0] * W8A8_N * W8A8_K}
+                                "op_per_launch": 2 * W8A8_M[0] * W8A8_N * W8A8_K, **timing(w8)}
     print(json.dumps(out))
 
 
@@ -781,37 +842,111 @@ def spot_check(kernels, args, np, torch):
     return {"max_err_over_tol": res}
 
 
-def cpu_baseline(args, np):
-    """The oracle's decode GEMV on the same 4096 x 4096 inputs, single-threaded, timed."""
-    import oracle
-    import synth
-    n = k = D_MODEL
-    w = synth.q4k_weights(n, k, seed=0)
-    x = synth.normal_f32(k, seed=0)
-    oracle.gemv(w[:16], x, 16, k)  # load and warm the library
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.gemv(w, x, n, k)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds:
-            break
-    per = el / passes
-    nbytes = q4k_bytes(n, k) + 4 * k + 4 * n
-    cpu_model = ""
+def dispatch_durations(torch, launch_all, launches):
+    """Run launch_all() (which enqueues `launches` launches of one bench kernel)
+    under torch.profiler and return the per-dispatch device durations in us:
+    per HIP kernel name, and per launch (the sum over a launch's kernels, e.g.
+    the MLP's gate/up and down), as median / p10 / p90.  None if the trace
+    holds no kernel dispatches."""
+    import statistics
+    from torch.autograd import DeviceType
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        launch_all()
+        torch.cuda.synchronize()
+    evs = [e for e in prof.profiler.kineto_results.events()
+           if e.device_type() == DeviceType.CUDA and not e.name().startswith(("Memcpy", "Memset"))]
+    if not evs or len(evs) % launches:
+        return None
+    evs.sort(key=lambda e: e.start_ns())
+    per_launch = len(evs) // launches
+
+    def stats(v):
+        v = sorted(v)
+        return {"median": round(statistics.median(v), 3), "p10": round(v[len(v) // 10], 3),
+                "p90": round(v[(9 * len(v)) // 10], 3), "n": len(v)}
+    by_name = {}
+    for e in evs:
+        by_name.setdefault(_short_name(e.name()), []).append(e.duration_ns() / 1e3)
+    launch_sums = [sum(e.duration_ns() for e in evs[j * per_launch:(j + 1) * per_launch]) / 1e3
+                   for j in range(launches)]
+    out = stats(launch_sums)
+    out["kernels_per_launch"] = per_launch
+    if per_launch > 1:
+        out["by_kernel"] = {k: stats(v) for k, v in by_name.items()}
+    return out
+
+
+def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full passes of the oracle decode GEMV (4096 x 4096 Q4_K, fp64 dot) "
-                      "in %.1f s, %.3f s per pass; host %s, %d CPUs visible"
-                      % (passes, el, per, cpu_model, len(os.sched_getaffinity(0)))}
+    return "unknown"
+
+
+def cpu_baseline(args, np):
+    """The oracle, as it stands, timed on this host's cores on the workloads the GPU runs:
+    the decode GEMV (4096 x 4096, every output), the SwiGLU MLP (4096 -> 14336 -> 4096,
+    every output) and the M = 512 prefill GEMM (N = K = 4096, a sample of 64 output
+    columns, scaled to the full output), each single-threaded (the plain build) and on all
+    cores (the OpenMP build: whole output rows per thread, identical results).  Each leg
+    repeats whole passes for about cpu_seconds / 6 (at least one pass)."""
+    import oracle
+    import synth
+    budget = max(0.5, args.cpu_seconds / 6.0)
+    n = k = D_MODEL
+    w = synth.q4k_weights(n, k, seed=0)
+    x = synth.normal_f32(k, seed=0)
+    wg = synth.q4k_weights(D_FF, D_MODEL, seed=0, stream=synth.W_GATE)
+    wu = synth.q4k_weights(D_FF, D_MODEL, seed=0, stream=synth.W_UP)
+    wdn = synth.q4k_weights(D_MODEL, D_FF, seed=0, stream=synth.W_DOWN)
+    xb = synth.normal_bf16((512, k), seed=0)
+    cols = np.arange(0, n, n // 64)
+    threads_all = oracle.threads(omp=True)
+
+    def timed(fn):
+        fn()  # load and warm the library
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return el / passes, passes
+
+    legs = []
+    for omp in (False, True):
+        cores = threads_all if omp else 1
+        per, p = timed(lambda: oracle.gemv(w, x, n, k, omp=omp))
+        legs.append({"workload": "decode_gemv_4096x4096", "cores": cores, "s_per_pass": round(per, 5),
+                     "passes": p, "gbs": round((q4k_bytes(n, k) + 4 * k + 4 * n) / per / 1e9, 4),
+                     "gflops": round(2 * n * k / per / 1e9, 4)})
+        per, p = timed(lambda: oracle.swiglu_mlp(wg, wu, wdn, x, D_MODEL, D_FF, omp=omp))
+        mlp_bytes = 3 * q4k_bytes(D_FF, D_MODEL) + 4 * D_MODEL + 2 * 4 * D_FF + 4 * D_MODEL
+        legs.append({"workload": "swiglu_mlp_4096_14336", "cores": cores, "s_per_pass": round(per, 5),
+                     "passes": p, "gbs": round(mlp_bytes / per / 1e9, 4),
+                     "gflops": round(6 * D_FF * D_MODEL / per / 1e9, 4)})
+        per, p = timed(lambda: oracle.gemm_cols(w, xb, n, k, cols, omp=omp))
+        full = per * n / len(cols)
+        legs.append({"workload": "gemm_512x4096x4096", "cores": cores,
+                     "s_per_pass": round(per, 5), "passes": p,
+                     "sample": "%d of %d output columns" % (len(cols), n),
+                     "s_full_output_est": round(full, 4),
+                     "tflops": round(2 * 512 * n * k / full / 1e12, 6)})
+    head = next(l for l in legs if l["workload"] == "decode_gemv_4096x4096" and l["cores"] == threads_all)
+    return {"value": head["gbs"], "unit": "GB/s", "cores": threads_all, "kind": "oracle",
+            "sample": "decode GEMV 4096 x 4096 Q4_K, every output, %d passes on %d threads "
+                      "(OpenMP over output rows); single-thread and the MLP and GEMM legs in "
+                      "'legs'" % (head["passes"], threads_all),
+            "host": {"cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+                     "affinity_cpus": len(os.sched_getaffinity(0)),
+                     "omp_num_threads": os.environ.get("OMP_NUM_THREADS")},
+            "legs": legs}
 
 
 if __name__ == "__main__":
