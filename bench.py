@@ -50,6 +50,7 @@ Q5K_BLOCK = 176               # bytes per Q5_K super-block
 Q6K_BLOCK = 210               # bytes per Q6_K block
 Q3K_BLOCK = 110               # bytes per Q3_K block
 SWEEP_M = (1, 2, 4, 8, 16, 32)
+LAYERS = 8                    # decode GEMVs per q4k_gemv_layers launch in the bench
 W8A8_N = W8A8_K = 3072
 W8A8_M = (1024, 8192)
 
@@ -86,7 +87,8 @@ def parse():
                    help="also run one device copy of 256 MiB (counter calibration)")
     p.add_argument("--only", default="",
                    help="comma list of kernels to run "
-                        "(gemv,q5k_gemv,q6k_gemv,q3k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,q5k_gemm,q6k_gemm,q3k_gemm,"
+                        "(gemv,layers,q5k_gemv,q6k_gemv,q3k_gemv,sweep_gemv,sweep_gemm,mlp,gemm,q5k_gemm,"
+                        "q6k_gemm,q3k_gemm,"
                         "dequant,w8a8,"
                         "read_probe)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run parity spot check")
@@ -169,6 +171,33 @@ def main():
             wd, xd, yd = rot[i]
             _lib.check(_lib.q4k_gemv(wd.data_ptr(), xd.data_ptr(), yd.data_ptr(), 1, n, k, sp))
         kernels.append(("gemv_4096x4096", run_gemv, nbytes, 2 * n * k, rot))
+
+    # ---- several decode GEMVs per launch: LAYERS independent 4096 x 4096 layers (each its
+    #      own W, x, y) in one q4k_gemv_layers launch, against the same layers as separate
+    #      q4k_gemv launches (eager, and replayed from one graph as graph_us)
+    if want("layers"):
+        n = k = D_MODEL
+        ws = [synth.q4k_weights(n, k, seed=10 + l) for l in range(LAYERS)]
+        xs = [synth.normal_f32(k, seed=10 + l) for l in range(LAYERS)]
+        ys = [np.zeros(n, np.float32) for _ in range(LAYERS)]
+        nbytes = LAYERS * (q4k_bytes(n, k) + 4 * k + 4 * n)
+        rot = Rotor(torch, ws + xs + ys, nbytes)
+
+        def run_layers(i, sp, rot=rot, n=n, k=k):
+            t = rot[i]
+            _lib.check(_lib.q4k_gemv_layers([a.data_ptr() for a in t[:LAYERS]],
+                                            [a.data_ptr() for a in t[LAYERS:2 * LAYERS]],
+                                            [a.data_ptr() for a in t[2 * LAYERS:]], n, k, sp))
+
+        def run_separate(i, sp, rot=rot, n=n, k=k):
+            t = rot[i]
+            for l in range(LAYERS):
+                _lib.check(_lib.q4k_gemv(t[l].data_ptr(), t[LAYERS + l].data_ptr(),
+                                         t[2 * LAYERS + l].data_ptr(), 1, n, k, sp))
+        kernels.append(("gemv_layers_%dx4096x4096" % LAYERS, run_layers, nbytes,
+                        LAYERS * 2 * n * k, rot))
+        kernels.append(("gemv_separate_%dx4096x4096" % LAYERS, run_separate, nbytes,
+                        LAYERS * 2 * n * k, rot))
 
     # ---- decode GEMV on the Q5_K sibling format, 4096 x 4096
     if want("q5k_gemv"):
@@ -491,6 +520,7 @@ def main():
         "roofline_mlp": None,
         "roofline_w8a8": None,
         "cpu_baseline": cpu,
+        "layers": layers_summary(per),
         "context": PAGES_CONTEXT,
         "kernels": per,
         "sweep_crossover_m": crossover,
@@ -599,6 +629,8 @@ def _template_args(name, kernel):
 # Dispatch signatures of the timed kernels -> workload.  Grid sizes (total work-items) and
 # LDS sizes follow from the launch code for these shapes.
 def dispatch_workload(name, threads, lds, hint=""):
+    if _template_args(name, "k_gemv_layers"):
+        return "gemv_layers_%dx4096x4096" % LAYERS
     gv = _template_args(name, "k_gemv_q4k")
     if gv:
         # <MT, R, GLU, NWV, XREG, FMT>
@@ -637,7 +669,7 @@ def dispatch_workload(name, threads, lds, hint=""):
     if "k_read_probe" in name:
         return "read_probe"
     if "k_gemv_split" in name:
-        return "sweep_gemv_14336x4096_flush"
+        return "sweep_gemv_14336x4096_split"
     gp = _template_args(name, "k_gemv_planes")
     if gp:
         return ("q%sk_gemv_4096x4096" % gp[0]) if threads == 4096 // 16 * 512 else "planes_other"
@@ -791,6 +823,15 @@ def spot_check(kernels, args, np, torch):
             rows = np.arange(0, 4096, 37)
             yr, a = oracle.gemv_rows(w, x, 4096, 4096, rows)
             res[name] = float((np.abs(y[rows] - yr[0]) / (1e-4 * a[0])).max())
+        elif name.startswith("gemv_layers_"):
+            arrs = [a.cpu().numpy() for a in t]
+            worst = 0.0
+            for l in range(LAYERS):
+                w, x, y = arrs[l], arrs[LAYERS + l], arrs[2 * LAYERS + l]
+                rows = np.arange(l, 4096, 97)
+                yr, a = oracle.gemv_rows(w, x, 4096, 4096, rows)
+                worst = max(worst, float((np.abs(y[rows] - yr[0]) / (1e-4 * a[0])).max()))
+            res[name] = worst
         elif name == "q5k_gemv_4096x4096":
             w, x, y = (a.cpu().numpy() for a in t)
             rows = np.arange(0, 4096, 37)
@@ -840,6 +881,23 @@ def spot_check(kernels, args, np, torch):
             yr, a = oracle.gemv(d.reshape(4096, -1), h, 4096, D_FF)
             res[name + "_down_stage"] = float((np.abs(o - yr[0]) / (1e-4 * a[0])).max())
     return {"max_err_over_tol": res}
+
+
+def layers_summary(per):
+    """The decode GEMVs of LAYERS independent 4096 x 4096 layers: one q4k_gemv_layers launch
+    against the same layers launched one by one (eager) and replayed from a graph."""
+    one = per.get("gemv_layers_%dx4096x4096" % LAYERS)
+    sep = per.get("gemv_separate_%dx4096x4096" % LAYERS)
+    if not one or not sep:
+        return None
+    r = {"layers": LAYERS, "bytes_per_launch": LAYERS * 9469952,
+         "one_launch_us": one["us"], "one_launch_gbs": one["gbs"], "one_launch_hbm_frac": one["hbm_frac"],
+         "separate_us": sep["us"], "separate_gbs": sep["gbs"],
+         "speedup_vs_separate": round(sep["us"] / one["us"], 3)}
+    if "graph_us" in sep:
+        r["separate_graph_us"] = sep["graph_us"]
+        r["speedup_vs_separate_graph"] = round(sep["graph_us"] / one["us"], 3)
+    return r
 
 
 def dispatch_durations(torch, launch_all, launches):

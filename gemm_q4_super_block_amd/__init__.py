@@ -5,13 +5,13 @@ The compute lives in ``libq4k.so`` (hand-written HIP kernels behind a C ABI,
 torch tensors.
 """
 from ._lib import Q4KError, Q4KLibraryError, load as load_library  # noqa: F401
-from .ops import (dequantize_bf16, dequantize_f32, gemm, gemv, q3k_dequantize_bf16,  # noqa: F401
+from .ops import (dequantize_bf16, dequantize_f32, gemm, gemv, gemv_layers, q3k_dequantize_bf16,  # noqa: F401
                   q3k_dequantize_f32, q3k_gemm, q3k_gemv, q5k_dequantize_bf16,
                   prepare_weight, q5k_dequantize_f32, q5k_gemm, q5k_gemv, q6k_dequantize_bf16,
                   q6k_dequantize_f32, q6k_gemm, q6k_gemv, swiglu_mlp, swiglu_mlp_noalloc,
                   w8a8_dequant, w8a8_linear, w8a8_linear_acc, w8a8_quantize_rows)
 
-__all__ = ["gemv", "gemm", "swiglu_mlp", "swiglu_mlp_noalloc", "dequantize_f32", "dequantize_bf16",
+__all__ = ["gemv", "gemv_layers", "gemm", "swiglu_mlp", "swiglu_mlp_noalloc", "dequantize_f32", "dequantize_bf16",
            "q5k_gemv", "q5k_gemm", "q5k_dequantize_f32", "q5k_dequantize_bf16",
            "q6k_gemv", "q6k_gemm", "q6k_dequantize_f32", "q6k_dequantize_bf16",
            "q3k_gemv", "q3k_gemm", "q3k_dequantize_f32", "q3k_dequantize_bf16",

@@ -24,6 +24,8 @@ Q4K_GEMV_MAX_M = 32
 Q4K_MAX_N = 2147418111
 Q4K_GEMM_MAX_K = 16777216
 Q4K_NOALLOC_MAX_D_FF = 65536
+Q4K_LAYERS_MAX = 32
+Q4K_LAYERS_MAX_K = 16384
 Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
 Q3K_BLOCK_BYTES = 110
@@ -40,6 +42,7 @@ SIGNATURES = {
     "q4k_version": (ctypes.c_int, []),
     "q4k_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q4k_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q4k_gemv_layers": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q4k_swiglu_mlp": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "q4k_swiglu_mlp_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "q4k_dequantize_f32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
@@ -129,6 +132,15 @@ def q4k_version() -> int:
 
 def q4k_gemv(w, x, y, m, n, k, stream) -> int:
     return load().q4k_gemv(w, x, y, m, n, k, stream)
+
+
+def q4k_gemv_layers(w_ptrs, x_ptrs, y_ptrs, n, k, stream) -> int:
+    """w_ptrs, x_ptrs, y_ptrs: sequences of device pointers (ints), one per layer."""
+    layers = len(w_ptrs)
+    if not (len(x_ptrs) == len(y_ptrs) == layers):
+        raise ValueError("one w, x and y pointer per layer")
+    arr = ctypes.c_void_p * max(1, layers)
+    return load().q4k_gemv_layers(arr(*w_ptrs), arr(*x_ptrs), arr(*y_ptrs), layers, n, k, stream)
 
 
 def q4k_gemm(w, x_bf16, y, m, n, k, stream) -> int:

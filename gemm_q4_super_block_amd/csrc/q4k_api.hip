@@ -117,9 +117,9 @@ const char* q4k_device_name(void) {
 
 const char* q4k_last_error(void) { return g_last_error.c_str(); }
 
-// Argument checks shared by the Q4_K and Q5_K GEMVs (block: bytes per
-// super-block of the format).
-static int gemv_checks(const char* what, const void* w, const float* x, const float* y,
+// Argument checks shared by the GEMVs of every format (block: bytes per
+// super-block of the format), before the device check.
+static int gemv_args(const char* what, const void* w, const float* x, const float* y,
                        int64_t m, int64_t n, int64_t k, size_t block) {
   if (!w || !x || !y) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer", what);
   if (m < 1 || m > Q4K_GEMV_MAX_M)
@@ -135,6 +135,12 @@ static int gemv_checks(const char* what, const void* w, const float* x, const fl
   if (overlap(y, ny, x, static_cast<size_t>(m * k) * 4) ||
       overlap(y, ny, w, q4k_bytes(n, k, block)))
     return fail(Q4K_ERR_INVALID_ARG, "%s: y overlaps an input", what);
+  return Q4K_OK;
+}
+
+static int gemv_checks(const char* what, const void* w, const float* x, const float* y,
+                       int64_t m, int64_t n, int64_t k, size_t block) {
+  if (int rc = gemv_args(what, w, x, y, m, n, k, block)) return rc;
   return check_device();
 }
 
@@ -144,6 +150,37 @@ int q4k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int6
   return launched(q4k::launch_gemv(static_cast<const uint8_t*>(w), x, y, m, n, k,
                                    static_cast<hipStream_t>(stream)),
                   "q4k_gemv");
+}
+
+int q4k_gemv_layers(const void* const* w, const float* const* x, float* const* y,
+                    int64_t layers, int64_t n, int64_t k, void* stream) {
+  const char* what = "q4k_gemv_layers";
+  if (!w || !x || !y) return fail(Q4K_ERR_INVALID_ARG, "%s: null pointer array", what);
+  if (layers < 1 || layers > Q4K_LAYERS_MAX)
+    return fail(Q4K_ERR_INVALID_ARG, "%s: layers=%lld outside 1..%d", what, (long long)layers,
+                Q4K_LAYERS_MAX);
+  if (k > Q4K_LAYERS_MAX_K)
+    return fail(Q4K_ERR_INVALID_ARG, "%s: k=%lld is above Q4K_LAYERS_MAX_K=%d", what,
+                (long long)k, Q4K_LAYERS_MAX_K);
+  for (int64_t l = 0; l < layers; ++l) {
+    // each layer is a batch-1 GEMV with its own checks
+    if (int rc = gemv_args(what, w[l], x[l], y[l], 1, n, k, 144u)) return rc;
+  }
+  // The layers run concurrently: no output may overlap another layer's
+  // inputs or output either.
+  const size_t ny = static_cast<size_t>(n) * 4, nx = static_cast<size_t>(k) * 4;
+  const size_t nw = q4k_bytes(n, k);
+  for (int64_t l = 0; l < layers; ++l)
+    for (int64_t j = 0; j < layers; ++j) {
+      if (overlap(y[l], ny, x[j], nx) || overlap(y[l], ny, w[j], nw) ||
+          (j != l && overlap(y[l], ny, y[j], ny)))
+        return fail(Q4K_ERR_INVALID_ARG, "%s: y[%lld] overlaps an input or output of layer %lld",
+                    what, (long long)l, (long long)j);
+    }
+  if (int rc = check_device()) return rc;
+  return launched(q4k::launch_gemv_layers(reinterpret_cast<const uint8_t* const*>(w), x, y,
+                                          layers, n, k, static_cast<hipStream_t>(stream)),
+                  what);
 }
 
 int q5k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n, int64_t k,

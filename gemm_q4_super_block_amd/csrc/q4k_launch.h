@@ -32,6 +32,13 @@ constexpr int kGemvSplitMinM = 5;
 hipError_t launch_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);
 
+// Independent batch-1 GEMVs of one shape in one launch (1 <= layers <= kGemvMaxLayers,
+// k <= kGemvLayersMaxK): y[l] = W[l] x[l]; w, x, y are host arrays of device pointers.
+constexpr int kGemvMaxLayers = 32;
+constexpr int kGemvLayersMaxK = 16384;
+hipError_t launch_gemv_layers(const uint8_t* const* w, const float* const* x, float* const* y,
+                              int64_t layers, int64_t n, int64_t k, hipStream_t stream);
+
 // Split-bf16 MFMA GEMV for kGemvSplitMinM <= m <= 32 (Q4_K, Q5_K).
 bool gemv_split_supported(int64_t m);
 hipError_t launch_gemv_split(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,

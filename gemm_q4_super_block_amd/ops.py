@@ -89,6 +89,29 @@ def _gemv(w, x, out, block, fn):
     return y
 
 
+def gemv_layers(ws, xs, outs=None):
+    """Independent batch-1 GEMVs of one shape in one launch: y[l] = W[l] x[l]
+    for lists of Q4_K weights [n, k/256*144] and fp32 x [k]; returns the list
+    of fp32 y [n]."""
+    if not ws or len(ws) != len(xs) or (outs is not None and len(outs) != len(ws)):
+        raise ValueError("one weight, x (and out) per layer")
+    n, k = _q4k_shape(ws[0])
+    dev = ws[0].device
+    for l, (w, x) in enumerate(zip(ws, xs)):
+        if _q4k_shape(w) != (n, k):
+            raise ValueError("layer %d: every weight must be [%d, %d]" % (l, n, k))
+        _dev_tensor(x, torch.float32, "x[%d]" % l)
+        _same_device(dev, ("w[%d]" % l, w), ("x[%d]" % l, x))
+        if x.dim() != 1 or x.shape[0] != k:
+            raise ValueError("x[%d] must be [%d]" % (l, k))
+    ys = outs if outs is not None else [torch.empty(n, dtype=torch.float32, device=dev) for _ in ws]
+    for l, y in enumerate(ys):
+        _out_tensor(y, torch.float32, (n,), dev, "out[%d]" % l)
+    check(_lib.q4k_gemv_layers([w.data_ptr() for w in ws], [x.data_ptr() for x in xs],
+                               [y.data_ptr() for y in ys], n, k, _stream(dev)))
+    return ys
+
+
 def gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X W^T for bf16 X [m, k]; returns fp32 [m, n]."""
     return _gemm(w, x, out, Q4K_BLOCK_BYTES, _lib.q4k_gemm)

@@ -111,6 +111,28 @@ int q4k_version(void);
 int q4k_gemv(const void* w, const float* x, float* y, int64_t m, int64_t n,
              int64_t k, void* stream);
 
+/* Largest layer count and largest k of q4k_gemv_layers. */
+#define Q4K_LAYERS_MAX 32
+#define Q4K_LAYERS_MAX_K 16384
+
+/* Several independent decode GEMVs of one shape in one launch.
+ *   y[l][j] = sum_c W[l][j, c] * x[l][c]   for l < layers, j < n, c < k.
+ *   w, x, y: host arrays of `layers` device pointers (read during the call;
+ *   the caller keeps ownership): w[l] a Q4_K matrix [n, k], x[l] fp32 [k],
+ *   y[l] fp32 [n], each 16-byte aligned.  Layers may share x (the Q, K and V
+ *   projections of one token) or not (the experts a token routes to).
+ *   1 <= layers <= Q4K_LAYERS_MAX, n >= 1, 256 <= k <= Q4K_LAYERS_MAX_K with
+ *   k % 256 == 0.
+ * Each y[l] is what q4k_gemv(w[l], x[l], y[l], 1, n, k) computes (the same
+ * tolerance and the same per-row arithmetic).  Recording the work of a decode
+ * step so that launch overhead is paid once is the lever of [P1 "SLM-Tiled
+ * GEMM and Graph Recording"]; here one persistent dispatch streams every
+ * layer's weights back to back, the next layer's rows in flight while the
+ * current ones are computed.  No y[l] may overlap any w, x or other y.
+ * Errors as for q4k_gemv, reported for the first layer that fails. */
+int q4k_gemv_layers(const void* const* w, const float* const* x, float* const* y,
+                    int64_t layers, int64_t n, int64_t k, void* stream);
+
 /* Prefill GEMM.
  *   Y[i, j] = sum_c X[i, c] * W[j, c]   for i < m, j < n  (Y = X W^T).
  *   w: Q4_K matrix [n, k], 16-byte aligned.

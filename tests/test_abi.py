@@ -51,7 +51,8 @@ def test_header_constants_match_binding():
     for name in ("Q4K_OK", "Q4K_ERR_INVALID_ARG", "Q4K_ERR_ALIGN", "Q4K_ERR_DEVICE",
                  "Q4K_ERR_LAUNCH", "Q4K_QK", "Q4K_BLOCK_BYTES", "Q4K_GEMV_MAX_M",
                  "Q5K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "Q3K_BLOCK_BYTES", "W8A8_K_STEP",
-                 "W8A8_MAX_K", "Q4K_MAX_N", "Q4K_GEMM_MAX_K"):
+                 "W8A8_MAX_K", "Q4K_MAX_N", "Q4K_GEMM_MAX_K", "Q4K_NOALLOC_MAX_D_FF",
+                 "Q4K_LAYERS_MAX", "Q4K_LAYERS_MAX_K"):
         mm = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
         assert mm, name
         assert int(mm.group(1)) == getattr(_lib, name), name
@@ -308,3 +309,22 @@ def test_noalloc_mlp_rejects_bad_arguments():
     assert "Q4K_NOALLOC_MAX_D_FF" in _lib.q4k_last_error()
     assert fn(*good[:4], 5 * A + 4, 256, 512, None) == _lib.Q4K_ERR_ALIGN
     assert fn(*good[:4], 4 * A, 256, 512, None) == _lib.Q4K_ERR_INVALID_ARG  # out == x
+
+
+def test_gemv_layers_rejects_bad_arguments():
+    f = _lib.q4k_gemv_layers
+    W = [A, A + (1 << 16)]
+    X = [2 * A, 2 * A + 4096]
+    Y = [3 * A, 3 * A + 4096]
+    E = _lib.Q4K_ERR_INVALID_ARG
+    assert f([], [], [], 16, 256, None) == E                              # no layers
+    assert "layers" in _lib.q4k_last_error()
+    assert f([A] * 33, [2 * A] * 33, [3 * A + 256 * i for i in range(33)], 16, 256, None) == E
+    assert f([A, 0], X, Y, 16, 256, None) == E                            # null w[1]
+    assert f(W, X, Y, 16, 300, None) == E                                 # k % 256
+    assert f(W, X, Y, 16, _lib.Q4K_LAYERS_MAX_K + 256, None) == E         # k past the limit
+    assert f(W, [2 * A, 2 * A + 8], Y, 16, 256, None) == _lib.Q4K_ERR_ALIGN
+    assert f(W, X, [3 * A, 3 * A + 32], 16, 256, None) == E               # y[0] and y[1] overlap
+    assert f(W, X, [3 * A, 2 * A + 4096], 16, 256, None) == E             # y[1] is x[1]
+    assert f(W, X, [3 * A, W[0] + 64], 16, 256, None) == E                # y[1] inside w[0]
+    assert _lib.q4k_last_error().startswith("q4k_gemv_layers")

@@ -26,7 +26,8 @@ CASES = [
     ("k_gemm_planes<3, 4, 1, 1, 4>", 128 * 2 * 256, 36864, "", "q3k_gemm_512x4096x4096"),
     ("k_gemv_planes<6, 8, 2, 1>", 4096 // 16 * 512, 16384, "", "q6k_gemv_4096x4096"),
     ("k_gemv_planes<3, 8, 2, 1>", 4096 // 16 * 512, 16384, "", "q3k_gemv_4096x4096"),
-    ("k_gemv_split<1, 2, 4>", 0, 0, "", "sweep_gemv_14336x4096_flush"),
+    ("k_gemv_split<1, 2, 4>", 0, 0, "", "sweep_gemv_14336x4096_split"),
+    ("k_gemv_layers<16, false>", 8 * 4096 // 16 * 1024, 0, "", "gemv_layers_8x4096x4096"),
     ("k_w8a8_gemm<1, 1, 2, 1>", 48 * 16 * 256, 32768, "", "w8a8_linear_1024x3072x3072"),
     ("k_w8a8_gemm<2, 2, 2, 1>", 24 * 64 * 256, 65536, "", "w8a8_linear_8192x3072x3072"),
     ("k_w8a8_quantize_rows<8>", 1024 * 64, 0, "", "w8a8_quantize_1024x3072"),
@@ -49,7 +50,7 @@ def test_template_arguments_parse():
 
 @pytest.mark.parametrize("workload,family", [
     ("gemv_4096x4096", "gemv"), ("swiglu_mlp_down_4096x14336", "gemv"),
-    ("sweep_gemv_14336x4096_flush", "gemv"), ("gemm_512x4096x4096", "gemm"),
+    ("sweep_gemv_14336x4096_split", "gemv"), ("gemv_layers_8x4096x4096", "gemv"), ("gemm_512x4096x4096", "gemm"),
     ("q5k_gemm_512x4096x4096", "gemm"), ("sweep_gemm_14336x4096", "gemm"),
     ("q6k_gemm_512x4096x4096", "planes"), ("q3k_gemv_4096x4096", "planes"),
     ("dequant_bf16_4096x4096", "dequant"), ("w8a8_linear_1024x3072x3072", "w8a8"),

@@ -4,7 +4,8 @@ Every entry point enqueues kernels only (no memset nodes, no allocation, no
 host synchronization), so a captured sequence must replay to the eager
 results.  The sequence covers every kernel family: batch-1 and batched GEMV,
 the four GEMM kernels (128 x 256, 64 x 128 and 32 x 64 K-slice, split K with
-its zeroing kernel), the SwiGLU MLP and the dequant export.  Between replays
+its zeroing kernel), the SwiGLU MLP (also without allocation), the layered
+GEMV and the dequant export.  Between replays
 the outputs are overwritten eagerly with NaN, and every replay is compared
 with the eager run: bit for bit where the kernel's summation order is fixed,
 and within the oracle tolerance where split K adds partial tiles with fp32
@@ -71,6 +72,13 @@ def test_graph_replays_match_eager(q4k):
     h = torch.empty(dff, dtype=torch.float32, device="cuda")
     o = torch.empty(dm, dtype=torch.float32, device="cuda")
     ops.append(("mlp", lambda: q4k.swiglu_mlp(wg, wu, wd, xm, h=h, out=o), [h, o], True))
+    o2 = torch.empty(dm, dtype=torch.float32, device="cuda")
+    ops.append(("mlp without allocation", lambda: q4k.swiglu_mlp_noalloc(wg, wu, wd, xm, o2),
+                [o2], True))
+    lw = [dev(synth.q4k_weights(1024, 512, seed=60 + l)) for l in range(3)]
+    lx = [dev(synth.normal_f32(512, seed=60 + l)) for l in range(3)]
+    ly = [torch.empty(1024, dtype=torch.float32, device="cuda") for _ in range(3)]
+    ops.append(("gemv layers", lambda: q4k.gemv_layers(lw, lx, ly), ly, True))
 
     torch.cuda.synchronize()
     eager = []
