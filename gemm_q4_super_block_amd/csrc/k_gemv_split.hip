@@ -83,11 +83,12 @@ __device__ __forceinline__ void weights8(uint2 q, uint2 h, int bit, float a, flo
   }
 }
 
-template <int MT, int NT, int FMT>
-__global__ __launch_bounds__(256) void k_gemv_split(const uint8_t* __restrict__ w,
-                                                    const float* __restrict__ x,
-                                                    float* __restrict__ y, int m, int n, int k) {
-  __shared__ __attribute__((aligned(16))) float red[4][MT][NT][4][64];
+template <int MT, int NT, int WV, int FMT>
+__global__ __launch_bounds__(64 * WV) void k_gemv_split(const uint8_t* __restrict__ w,
+                                                        const float* __restrict__ x,
+                                                        float* __restrict__ y, int m, int n,
+                                                        int k) {
+  __shared__ __attribute__((aligned(16))) float red[WV][MT][NT][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nl = lane & 15, kg = lane >> 4;
@@ -138,8 +139,8 @@ __global__ __launch_bounds__(256) void k_gemv_split(const uint8_t* __restrict__ 
   WBlock cur, nxt;
   int b = wave;
   if (b < nb) load_w(b, cur);
-  for (; b < nb; b += 4) {
-    if (b + 4 < nb) load_w(b + 4, nxt);
+  for (; b < nb; b += WV) {
+    if (b + WV < nb) load_w(b + WV, nxt);
     // x of the whole super-block, this lane's 8 k of each of its 8 sub-blocks:
     // issued together so that one L2 round trip serves the four quant groups.
     float4 xr[MT][8][2];
@@ -198,8 +199,9 @@ __global__ __launch_bounds__(256) void k_gemv_split(const uint8_t* __restrict__ 
     cur = nxt;
   }
 
-  // Sum the four waves' partial tiles; wave 0 stores.  Tile register r holds
-  // batch row 4 kg + r, weight row nl.
+  // Sum the waves' partial tiles: wave v finishes the (t, nt) tiles with
+  // (t * NT + nt) % WV == v and stores them.  Tile register r holds batch row
+  // 4 kg + r, weight row nl.
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -207,18 +209,20 @@ __global__ __launch_bounds__(256) void k_gemv_split(const uint8_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wave][t][nt][r][lane] = acc[t][nt][r];
   __syncthreads();
-  if (wave != 0) return;
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt) {
+      if ((t * NT + nt) % WV != wave) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = ((red[0][t][nt][r][lane] + red[1][t][nt][r][lane]) + red[2][t][nt][r][lane]) +
-                        red[3][t][nt][r][lane];
+        float v = red[0][t][nt][r][lane];
+#pragma unroll
+        for (int src = 1; src < WV; ++src) v += red[src][t][nt][r][lane];
         const int row = 16 * t + 4 * kg + r, col = n0 + 16 * nt + nl;
         if (row < m && col < n) y[static_cast<size_t>(row) * n + col] = v;
       }
+    }
 }
 
 }  // namespace
@@ -227,33 +231,35 @@ bool gemv_split_supported(int64_t m) { return m >= kGemvSplitMinM && m <= 32; }
 
 namespace {
 
-// One 16-row batch tile for m <= 16, two above.  Matrices of at least
-// kSplitWideRows rows give each workgroup two 16-row weight tiles (x's split
-// and its sums shared by both; measured 1.4-1.6x faster at 14336 rows, slower
-// at 4096, where the grid would drop to 128 workgroups).
-constexpr int kSplitWideRows = 8192;
+// One 16-row batch tile for m <= 16, two above.  A workgroup owns 16 NT
+// weight rows and its WV waves split K (wave v takes super-blocks v, v + WV,
+// ...), so each x split serves NT weight tiles.  Matrices of at least
+// kSplitTallRows rows take 64-row tiles on 8 waves (224 workgroups at 14336
+// rows); smaller ones 16-row tiles on 8 waves (256 at 4096 rows), so that
+// the grid still covers the CUs.
+constexpr int kSplitTallRows = 8192;
 
-template <int MT, int NT, int FMT>
+template <int MT, int NT, int WV, int FMT>
 void launch_split_tiles(const uint8_t* w, const float* x, float* y, int m, int n, int k,
                         hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemv_split<MT, NT, FMT>), dim3((n + 16 * NT - 1) / (16 * NT)), dim3(256),
-                     0, stream, w, x, y, m, n, k);
+  hipLaunchKernelGGL((k_gemv_split<MT, NT, WV, FMT>), dim3((n + 16 * NT - 1) / (16 * NT)),
+                     dim3(64 * WV), 0, stream, w, x, y, m, n, k);
 }
 
 template <int FMT>
 hipError_t launch_split_fmt(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                             int64_t k, hipStream_t stream) {
   const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
-  if (ni >= kSplitWideRows) {
+  if (ni >= kSplitTallRows) {
     if (mi <= 16)
-      launch_split_tiles<1, 2, FMT>(w, x, y, mi, ni, ki, stream);
+      launch_split_tiles<1, 4, 8, FMT>(w, x, y, mi, ni, ki, stream);
     else
-      launch_split_tiles<2, 2, FMT>(w, x, y, mi, ni, ki, stream);
+      launch_split_tiles<2, 4, 8, FMT>(w, x, y, mi, ni, ki, stream);
   } else {
     if (mi <= 16)
-      launch_split_tiles<1, 1, FMT>(w, x, y, mi, ni, ki, stream);
+      launch_split_tiles<1, 1, 8, FMT>(w, x, y, mi, ni, ki, stream);
     else
-      launch_split_tiles<2, 1, FMT>(w, x, y, mi, ni, ki, stream);
+      launch_split_tiles<2, 1, 8, FMT>(w, x, y, mi, ni, ki, stream);
   }
   return hipGetLastError();
 }
