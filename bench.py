@@ -629,7 +629,7 @@ def _template_args(name, kernel):
 # Dispatch signatures of the timed kernels -> workload.  Grid sizes (total work-items) and
 # LDS sizes follow from the launch code for these shapes.
 def dispatch_workload(name, threads, lds, hint=""):
-    if _template_args(name, "k_gemv_layers"):
+    if "k_gemv_layers" in name:
         return "gemv_layers_%dx4096x4096" % LAYERS
     gv = _template_args(name, "k_gemv_q4k")
     if gv:
