@@ -7,8 +7,8 @@
  *
  * Source: "CPU kernel parity: decode and tile kernels at llama.cpp speed ..."
  * (daScript PR page), section on the kernel work: the 4-bit and 5-bit
- * k-quants ("k4 and k5") share one fused dequant-and-dot form.  The pages
- * print no Q5_K layout.  The reading used here is the GGUF convention, the
+ * k-quants ("k4", "k5") are decoded by the same fused dequant-and-dot kernel
+ * shape.  The pages print no Q5_K layout.  The reading used here is the GGUF convention, the
  * Q4_K super-block plus one high bit per weight:
  *   176 bytes = fp16 d at 0, fp16 dmin at 2, the 12 packed 6-bit scale/min
  *   bytes of Q4_K at 4, 32 high-bit bytes qh at 16, 128 nibble bytes qs at 48.
