@@ -560,7 +560,7 @@ def main():
 _COMMON_SOURCES = ("q4k_device.h", "q4k_launch.h")
 KERNEL_SOURCES = {
     "gemv": ("k_gemv.hip", "k_gemv_split.hip"),
-    "gemm": ("k_gemm.hip", "lds_copy.h"),
+    "gemm": ("k_gemm.hip", "k_gemm_stream.hip", "lds_copy.h"),
     "dequant": ("k_dequant.hip",),
     "w8a8": ("k_w8a8.hip", "lds_copy.h"),
     "planes": ("k_planes.hip",),
@@ -647,6 +647,8 @@ def dispatch_workload(name, threads, lds, hint=""):
     dq = _template_args(name, "k_dequant_q4k")
     if dq:
         return "dequant_bf16_4096x4096" if dq == ("true", "4") else "dequant_other"
+    if _template_args(name, "k_gemm_q4k_stream"):
+        return "sweep_gemm_14336x4096"
     if "k_gemm_q4k_128x256" in name:
         return "gemm_512x14336x4096" if threads == 57344 else "gemm_other"
     ks = _template_args(name, "k_gemm_q4k_kslice")

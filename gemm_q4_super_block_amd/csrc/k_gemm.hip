@@ -861,14 +861,8 @@ hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
   const int steps = ki / kBK;
   const int tiles_n = (ni + kBN - 1) / kBN;
   if (mi <= 32) {
-    using Small = KSlice<1, 2>;
-    const int small_n = (ni + Small::BN - 1) / Small::BN;
-    if (small_n >= kGemmSmallTiles) {
-      // One 32 x 64 tile per workgroup, K split inside the workgroup.
-      hipLaunchKernelGGL((k_gemm_q4k_kslice<1, 2>), dim3(small_n), dim3(Small::Threads), 0,
-                         stream, w, x, y, mi, ni, ki, 1, small_n, 0);
-      return hipGetLastError();
-    }
+    // 64 weight rows per workgroup, each wave streaming its own super-blocks.
+    if (gemm_stream_tiles(ni) >= kGemmSmallTiles) return launch_gemm_stream(w, x, y, m, n, k, stream);
     // Small batch: one 32-row slice, the four waves split the 128 weight rows.
     return launch<1, 4, 1, 1, 2>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
   }

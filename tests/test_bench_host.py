@@ -21,6 +21,8 @@ CASES = [
     ("k_gemm_q4k_kslice<2, 2, 4>", 131072, 163840, "", "gemm_512x4096x4096"),
     ("k_gemm_q4k_kslice<2, 2, 5>", 131072, 157696, "", "q5k_gemm_512x4096x4096"),
     ("k_gemm_q4k_kslice<1, 2, 4>", 224 * 256, 81920, "", "sweep_gemm_14336x4096"),
+    ("k_gemm_q4k_stream<1, 8>", 448 * 256, 57344, "", "sweep_gemm_14336x4096"),
+    ("k_gemm_q4k_stream<2, 32>", 224 * 256, 155648, "", "sweep_gemm_14336x4096"),
     ("k_gemm_q4k_128x256", 57344, 155648, "", "gemm_512x14336x4096"),
     ("k_gemm_planes<6, 4, 1, 1, 4>", 128 * 2 * 256, 36864, "", "q6k_gemm_512x4096x4096"),
     ("k_gemm_planes<3, 4, 1, 1, 4>", 128 * 2 * 256, 36864, "", "q3k_gemm_512x4096x4096"),

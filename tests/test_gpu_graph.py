@@ -3,8 +3,8 @@
 Every entry point enqueues kernels only (no memset nodes, no allocation, no
 host synchronization), so a captured sequence must replay to the eager
 results.  The sequence covers every kernel family: batch-1 and batched GEMV,
-the four GEMM kernels (128 x 256, 64 x 128 and 32 x 64 K-slice, split K with
-its zeroing kernel), the SwiGLU MLP (also without allocation), the layered
+the GEMM kernels (128 x 256, 64 x 128 K-slice, the streaming kernel for
+small batches at each X staging size, split K with its zeroing kernel), the SwiGLU MLP (also without allocation), the layered
 GEMV and the dequant export.  Between replays
 the outputs are overwritten eagerly with NaN, and every replay is compared
 with the eager run: bit for bit where the kernel's summation order is fixed,
@@ -44,7 +44,9 @@ def dev_bf16(bits: np.ndarray) -> torch.Tensor:
 # (m, n, k, exact): GEMM shapes per kernel family
 GEMMS = [(512, 8192, 256, True),    # 128 x 256 tiles (4 x 32 = 128)
          (384, 4096, 256, True),    # 64 x 128 K-slice (6 x 32 = 192)
-         (8, 8192, 256, True),      # 32 x 64 K-slice (128 tiles)
+         (8, 8192, 256, True),      # streaming, X staged for 8 rows
+         (16, 8192, 768, True),     # streaming, 16 rows
+         (32, 8192, 1024, True),    # streaming, 32 rows, 64-row weight tiles
          (64, 4000, 2048, False),   # split K over 128 x 128 tiles
          (5, 1000, 1024, False)]    # small batch, split K
 

@@ -297,28 +297,33 @@ def test_gemm_tile_kernels(q4k, m, n, k):
     assert np.all(np.isfinite(Y))
 
 
-# Batches of at most 32 rows with >= 128 weight tiles of 64 rows run the 32 x 64
-# K-slice kernel: ragged N (one 8-row last tile) at one super-block of K, three
-# super-blocks with 17 rows, and every output of a 7-row batch.
-@pytest.mark.parametrize("m,n,k", [(5, 8200, 256), (17, 9000, 768), (32, 16384, 512)])
-def test_gemm_small_batch_kslice(q4k, m, n, k):
+# Batches of at most 32 rows with >= 128 weight tiles of 64 rows run the
+# streaming kernel: X staged for 8 rows (m <= 8), 16 rows (m <= 16) or 32, with
+# 32- or 64-row weight tiles; each wave of a workgroup takes every fourth
+# super-block, so K of 1, 3, 5, 9 and 17 super-blocks leaves waves idle or with
+# odd counts.  Ragged N (8200: an 8-row last tile) and the batch sizes at each
+# staging switch.
+@pytest.mark.parametrize("m,n,k", [(1, 8200, 256), (5, 8200, 256), (8, 8224, 1280),
+                                   (9, 9000, 768), (16, 8192, 2304), (17, 9000, 768),
+                                   (32, 16384, 512), (32, 8200, 4352)])
+def test_gemm_small_batch_stream(q4k, m, n, k):
     w = synth.q4k_weights(n, k, seed=m + n)
     xb = synth.normal_bf16((m, k), seed=m + n)
     Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
-    cols = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, n - 65, n - 64, n - 9, n - 1],
-                                     np.random.default_rng(n).integers(0, n, 54)]))
+    cols = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, n - 65, n - 64, n - 33, n - 32,
+                                      n - 9, n - 1], np.random.default_rng(n).integers(0, n, 52)]))
     Yr, A = oracle.gemm_cols(w, xb, n, k, cols)
     assert_within(Y[:, cols], Yr, A, GEMM_TOL, "gemm %dx%dx%d" % (m, n, k))
     assert np.all(np.isfinite(Y))
 
 
-def test_gemm_small_batch_kslice_full_output(q4k):
-    m, n, k = 7, 8192, 256
-    w = synth.q4k_weights(n, k, seed=78)
-    xb = synth.normal_bf16((m, k), seed=78)
+@pytest.mark.parametrize("m,n,k", [(7, 8192, 256), (13, 8192, 1024)])
+def test_gemm_small_batch_stream_full_output(q4k, m, n, k):
+    w = synth.q4k_weights(n, k, seed=78 + m)
+    xb = synth.normal_bf16((m, k), seed=78 + m)
     Y = q4k.gemm(dev(w), dev_bf16(xb)).cpu().numpy()
     Yr, A = oracle.gemm(w, xb, n, k)
-    assert_within(Y, Yr, A, GEMM_TOL, "gemm 7x8192x256")
+    assert_within(Y, Yr, A, GEMM_TOL, "gemm %dx%dx%d" % (m, n, k))
 
 
 def test_gemm_mid_tile_kernel_full_output(q4k):

@@ -247,10 +247,12 @@ def test_q3k_gemv_structured(q4k, m, n, k):
 
 # ------------------------------------------------------------------ GEMMs
 
-# Split-K tiles, the 32 x 64 and 64 x 64 / 64 x 128 K-slice tiles and the
-# 128 x 256 tiles, all on structured weights.
-@pytest.mark.parametrize("m,n,k", [(1, 130, 1024), (7, 8200, 256), (40, 300, 768),
-                                   (200, 6144, 256), (512, 4096, 512), (512, 8192, 256)])
+# Split-K tiles, the streaming small-batch kernel (8, 16 and 32 staged X
+# rows), the 64 x 64 / 64 x 128 K-slice tiles and the 128 x 256 tiles, all on
+# structured weights.
+@pytest.mark.parametrize("m,n,k", [(1, 130, 1024), (7, 8200, 256), (12, 8192, 1280),
+                                   (30, 8256, 768), (40, 300, 768), (200, 6144, 256),
+                                   (512, 4096, 512), (512, 8192, 256)])
 def test_q4k_gemm_structured(q4k, m, n, k):
     w = tile(q4k_kinds(), n, k, seed=m + n)
     xb = synth.normal_bf16((m, k), seed=m + k)
