@@ -665,9 +665,10 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
     for (int j = 0; j < NJ; ++j) {
       const int col = kColsPerWave * wn + 32 * j + c32;
       const uint8_t* rec = wb + col * C::BB;
-      const uint4 v = *reinterpret_cast<const uint4*>(
-          rec + (FMT == 5 ? kQ5QuantOffset : 16) + 32 * g + 16 * bh);
-      Q[j].q = h ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
+      // 8 bytes per lane: the two lane halves read different addresses (a
+      // 16-byte read that both halves share costs LDS bank conflicts).
+      Q[j].q = *reinterpret_cast<const uint2*>(
+          rec + (FMT == 5 ? kQ5QuantOffset : 16) + 32 * g + 16 * bh + 8 * h);
       if constexpr (FMT == 5)
         Q[j].hb = *reinterpret_cast<const uint2*>(rec + kQ5HighOffset + 16 * bh + 8 * h);
     }
