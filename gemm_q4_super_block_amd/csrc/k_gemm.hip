@@ -906,13 +906,8 @@ hipError_t launch_q5k_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_
   const int steps = ki / kBK;
   const int tiles_n = (ni + kBN - 1) / kBN;
   if (mi <= 32) {
-    using Small = KSlice<1, 2, 5>;
-    const int small_n = (ni + Small::BN - 1) / Small::BN;
-    if (small_n >= kGemmSmallTiles) {
-      hipLaunchKernelGGL((k_gemm_q4k_kslice<1, 2, 5>), dim3(small_n), dim3(Small::Threads), 0,
-                         stream, w, x, y, mi, ni, ki, 1, small_n, 0);
-      return hipGetLastError();
-    }
+    if (gemm_stream_tiles(ni) >= kGemmSmallTiles)
+      return launch_q5k_gemm_stream(w, x, y, m, n, k, stream);
     return launch<1, 4, 1, 1, 2, 5>(w, x, y, mi, ni, ki, splits_for(tiles_n, steps), stream);
   }
   // The K-slice tiles serve the grids between one and a few waves of

@@ -1,7 +1,7 @@
-// k_gemm_stream.hip -- Q4_K GEMM for batches of at most 32 rows (bf16 X).
+// k_gemm_stream.hip -- Q4_K and Q5_K GEMM for batches of at most 32 rows (bf16 X).
 //
-// What it computes is q4k_gemm's Y = X W^T (fp32 accumulate, the same
-// per-weight dequantization as the prefill tiles).  With 32 rows or fewer the
+// What it computes is q4k_gemm's (q5k_gemm's) Y = X W^T (fp32 accumulate,
+// the same per-weight dequantization as the prefill tiles).  With 32 rows or fewer the
 // work is a weight stream: every weight is used by at most 32 products, and a
 // launch is as fast as the weight bytes reach the CUs and get dequantized.
 // The K-slice tiles share one LDS ring among the four waves of a workgroup
@@ -14,16 +14,17 @@
 //     sum their partial tiles through LDS once, at the end.
 //   * each wave copies only what it reads, into its own part of LDS, with
 //     direct global -> LDS copies: its super-block of the workgroup's rows
-//     (32 NB records of 144 bytes, contiguous per row) into a 2-slot ring one
-//     super-block ahead, and the 64-wide K step of the first XR batch rows of
-//     X that each quant group needs (XR rows x 128 bytes, XOR-swizzled rows)
-//     into a 5-slot ring four steps ahead.  A wave waits only for its own
+//     (32 NB records of 144 or 176 bytes, contiguous per row) into a 2-slot
+//     ring one super-block ahead, and the 64-wide K step of the first XR batch
+//     rows of X that each quant group needs (XR rows x 128 bytes, XOR-swizzled
+//     rows) into a 5-slot ring four steps ahead (Q5_K with XR >= 16: 4 slots,
+//     three ahead).  A wave waits only for its own
 //     copies (s_waitcnt vmcnt): no barrier until the partial tiles are summed.
 //     The copies take a scalar base and a fixed per-lane 32-bit offset, so
 //     the stream costs no vector instructions beyond the copies themselves.
 //   * XR = 8 or 16 rows (m <= 16): 32-row weight tiles (NB = 1), two
-//     workgroups per CU (78 KiB of LDS each); XR = 32: 64-row tiles (NB = 2),
-//     one workgroup per CU.
+//     workgroups per CU (at most 78 KiB of LDS each); XR = 32: 64-row tiles
+//     (NB = 2), one workgroup per CU.
 //   * v_mfma_f32_32x32x16_bf16 with X as A (batch rows) and W as B (weight
 //     rows).  Lane (c, h) = (lane % 32, lane / 32) of quant group g reads the
 //     16 quant bytes 16 h .. 16 h + 15 of weight row c and the X chunks of the
@@ -31,8 +32,9 @@
 //     16 h + 8 u .. +7, k = 64 g + 32 p + 16 h + 8 u + (0..7) in both operands
 //     (any k order gives the same contraction, as long as both use it).
 //     A rows at or past XR repeat row XR - 1; their outputs are not stored.
-//   * weights as in the other GEMM kernels: fma(d sc 2^9, q 2^-9, -dmin m),
-//     one rounding, then bf16; a cancelling block gives exact zeros.
+//   * weights as in the other GEMM kernels: fma(d sc 2^9, q 2^-9, -dmin m)
+//     (Q5_K: fma(d sc, q, -dmin m) on the exactly widened 5-bit quant), one
+//     rounding, then bf16; a cancelling block gives exact zeros.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -46,25 +48,34 @@ namespace {
 
 typedef float f16x_t __attribute__((ext_vector_type(16)));
 
-template <int NB, int XR>
+template <int NB, int XR, int FMT>
 struct Stream {
+  static constexpr int BB = block_bytes<FMT>();       // 144 (Q4_K) or 176 (Q5_K)
+  static constexpr int Units = BB / 16;              // 16-byte units per record
   static constexpr int RW = 32 * NB;                 // weight rows per workgroup
-  static constexpr int WUnits = RW * 9;              // 16-byte units of one super-block of them
+  static constexpr int WUnits = RW * Units;          // 16-byte units of one super-block of them
   static constexpr int WC = (WUnits + 63) / 64;      // weight copies per super-block
   static constexpr int WSlot = WUnits * 16;
   static constexpr int WSlots = 2;
   static constexpr int XSlot = XR * 128;             // XR batch rows x 64 k of bf16
   static constexpr int XC = XR / 8;                  // X copies per step (8 rows each)
-  static constexpr int XSlots = 5;
+  // X issued XSlots - 1 steps ahead (Q5_K's larger records leave room for one
+  // step less at 16 and 32 rows).
+  static constexpr int XSlots = FMT == 5 && XR >= 16 ? 4 : 5;
   static constexpr int XOff = WSlots * WSlot;
   static constexpr int WaveLds = XOff + XSlots * XSlot;
   static constexpr int Lds = 4 * WaveLds;
   static constexpr int MinBlocks = NB == 1 ? 2 : 1;  // workgroups per CU
   static_assert(Lds * MinBlocks <= 160 * 1024, "LDS budget of the workgroups of one CU");
   static_assert(NB * 4 * 1024 <= WaveLds, "a wave's partial tile fits its own LDS part");
-  // Copies issued after X(i + 1) when step i waits for it: the X copies of
-  // three later steps, and a weight super-block unless g = 3.
-  static_assert(3 * XC + WC <= 63, "vmcnt range");
+  // W(t + 1) is issued at step 4 t, before X(4 t + XSlots - 1): waiting for
+  // X(i + 1) covers the weights step i + 1 reads.
+  static_assert(XSlots + 3 <= 4 * WSlots, "weight ring depth");
+  // Copies issued after X(i + 1) when step i (group g) waits for it: the X
+  // copies of XSlots - 2 later steps, and a weight super-block when one of
+  // those steps starts a super-block (g < XSlots - 2).
+  static constexpr int wait_count(int g) { return (XSlots - 2) * XC + (g < XSlots - 2 ? WC : 0); }
+  static_assert((XSlots - 2) * XC + WC <= 63, "vmcnt range");
 };
 
 // Direct global -> LDS copy of 16 bytes per lane from sbase + voff (sbase
@@ -89,18 +100,20 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Sub-block scales of one super-block header: a = d sc 2^9, b = dmin m for
-// sub-blocks 0..7.
+// Sub-block scales of one super-block header: a = d sc 2^9 (Q5_K: d sc),
+// b = dmin m for sub-blocks 0..7.
 struct SbScales {
   float a[8], b[8];
 };
 
+template <int FMT>
 __device__ __forceinline__ void sb_scales(const uint4 h, SbScales& s) {
   const uint32_t sc_lo = h.y & 0x3F3F3F3Fu;
   const uint32_t mn_lo = h.z & 0x3F3F3F3Fu;
   const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
   const uint32_t mn_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-  const float d = half_bits_to_float(h.x & 0xFFFFu) * kNibbleUnscale;
+  // Q4_K nibbles are widened as fp8 (q 2^-9); Q5_K quants exactly.
+  const float d = half_bits_to_float(h.x & 0xFFFFu) * (FMT == 5 ? 1.0f : kNibbleUnscale);
   const float dmin = half_bits_to_float(h.x >> 16);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -111,12 +124,12 @@ __device__ __forceinline__ void sb_scales(const uint4 h, SbScales& s) {
   }
 }
 
-template <int NB, int XR>
+template <int NB, int XR, int FMT>
 __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const uint8_t* __restrict__ w,
                                                             const uint16_t* __restrict__ x,
                                                             float* __restrict__ y, int m, int n,
                                                             int k) {
-  using C = Stream<NB, XR>;
+  using C = Stream<NB, XR, FMT>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::Lds];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -127,7 +140,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const 
   // This wave's super-blocks: wave, wave + 4, ...; cnt of them, 4 cnt steps.
   const int cnt = nsb > wave ? (nsb - wave + 3) >> 2 : 0;
   const int steps = 4 * cnt;
-  const uint32_t row_bytes = static_cast<uint32_t>(nsb) * kBlockBytes;
+  const uint32_t row_bytes = static_cast<uint32_t>(nsb) * C::BB;
   // The tile's first weight row, in 64 bits; offsets inside its 32 NB rows
   // stay below 2^32 (k <= 2^24, checked by the C ABI).
   const uint8_t* const wt = w + static_cast<size_t>(n0) * row_bytes;
@@ -135,14 +148,14 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const 
   const uint32_t lds_mine = lds_address(mine);
 
   // Weight copy i: units min(64 i, WUnits - 64) + lane of the slot, unit U =
-  // part U % 9 of row U / 9 (the last copy repeats some units of the one
-  // before, with the same data and place).  Rows past n read row n - 1.
+  // part U % Units of row U / Units (the last copy repeats some units of the
+  // one before, with the same data and place).  Rows past n read row n - 1.
   uint32_t woff[C::WC];
 #pragma unroll
   for (int i = 0; i < C::WC; ++i) {
     const int U = min(64 * i, C::WUnits - 64) + lane;
-    const int r = (U * 7282) >> 16;  // U / 9 for U < 2304
-    woff[i] = static_cast<uint32_t>(min(r, n - 1 - n0)) * row_bytes + (U - r * 9) * 16;
+    const int r = U / C::Units;
+    woff[i] = static_cast<uint32_t>(min(r, n - 1 - n0)) * row_bytes + (U - r * C::Units) * 16;
   }
   // X copy q fills slot rows 8 q .. 8 q + 7; lane -> (row, LDS chunk lane % 8)
   // holding X chunk (lane % 8) ^ swz(row).  Rows past m read row m - 1 (their
@@ -157,7 +170,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const 
   // Super-block of this wave's t-th step group (indices past the end repeat the last).
   auto sb_of = [&](int t) { return wave + 4 * min(t, cnt - 1); };
   auto copy_w = [&](int t) {
-    const uint8_t* base = wt + static_cast<size_t>(sb_of(t)) * kBlockBytes;
+    const uint8_t* base = wt + static_cast<size_t>(sb_of(t)) * C::BB;
     const uint32_t dst = lds_mine + (t & 1) * C::WSlot;
 #pragma unroll
     for (int i = 0; i < C::WC; ++i)
@@ -173,18 +186,23 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const 
   };
 
   // Fragments of one step: the quant bytes of group g of each weight row
-  // block, and the four X chunks of batch row c.
+  // block (Q5_K: and the high-bit bytes of the same positions, bit 2 g + p of
+  // each holding the fifth bit), and the four X chunks of batch row c.
+  constexpr int kQOff = FMT == 5 ? kQ5QuantOffset : 16;
   struct Frag {
     uint4 q[NB];
+    uint4 qh[FMT == 5 ? NB : 1];
     bf16x8_t xa[4];  // [2 p + u]
   };
   auto read_frag = [&](int i, Frag& f) {
     const uint8_t* ws = mine + ((i >> 2) & 1) * C::WSlot;
     const int g = i & 3;
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      f.q[j] = *reinterpret_cast<const uint4*>(ws + (32 * j + c) * kBlockBytes + 16 + 32 * g +
-                                               16 * h);
+    for (int j = 0; j < NB; ++j) {
+      const uint8_t* rec = ws + (32 * j + c) * C::BB;
+      f.q[j] = *reinterpret_cast<const uint4*>(rec + kQOff + 32 * g + 16 * h);
+      if constexpr (FMT == 5) f.qh[j] = *reinterpret_cast<const uint4*>(rec + kQ5HighOffset + 16 * h);
+    }
     const int xr = min(c, XR - 1);
     const uint8_t* xs = mine + C::XOff + (i % C::XSlots) * C::XSlot + xr * 128;
 #pragma unroll
@@ -197,7 +215,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const 
     const uint8_t* ws = mine + (t & 1) * C::WSlot;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      hd[j] = *reinterpret_cast<const uint4*>(ws + (32 * j + c) * kBlockBytes);
+      hd[j] = *reinterpret_cast<const uint4*>(ws + (32 * j + c) * C::BB);
   };
 
   f16x_t acc[NB];
@@ -218,7 +236,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const 
     read_hdr(0, hd);
     read_frag(0, fa);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) sb_scales(hd[j], sc[j]);
+    for (int j = 0; j < NB; ++j) sb_scales<FMT>(hd[j], sc[j]);
 
     // Step i (group g of super-block t): issue W(t + 1) at g = 0 and X(i + 4);
     // dequantize and multiply step i from fc; wait for X(i + 1) (and with it
@@ -230,7 +248,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const 
       copy_x(i + C::XSlots - 1);
       if (g == 0 && i > 0) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) sb_scales(hd[j], sc[j]);
+        for (int j = 0; j < NB; ++j) sb_scales<FMT>(hd[j], sc[j]);
       }
 #pragma unroll
       for (int p = 0; p < 2; ++p)
@@ -238,15 +256,21 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const 
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
-            const bf16x8_t b = dequant8_bf16(u ? fc.q[j].z : fc.q[j].x, u ? fc.q[j].w : fc.q[j].y,
-                                             4 * p, sc[j].a[2 * g + p], sc[j].b[2 * g + p]);
+            const uint32_t d0 = u ? fc.q[j].z : fc.q[j].x, d1 = u ? fc.q[j].w : fc.q[j].y;
+            bf16x8_t b;
+            if constexpr (FMT == 5) {
+              const uint32_t h0 = u ? fc.qh[j].z : fc.qh[j].x, h1 = u ? fc.qh[j].w : fc.qh[j].y;
+              b = __builtin_bit_cast(
+                  bf16x8_t, dequant8_bf16_q5(q5_bytes(d0, h0, 4 * p, 2 * g + p),
+                                             q5_bytes(d1, h1, 4 * p, 2 * g + p),
+                                             sc[j].a[2 * g + p], sc[j].b[2 * g + p]));
+            } else {
+              b = dequant8_bf16(d0, d1, 4 * p, sc[j].a[2 * g + p], sc[j].b[2 * g + p]);
+            }
             acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.xa[2 * p + u], b, acc[j], 0, 0, 0);
           }
       __builtin_amdgcn_sched_barrier(0);
-      if (g < 3)
-        wait_copies<3 * C::XC + C::WC>();
-      else
-        wait_copies<3 * C::XC>();
+      wait_copies<C::wait_count(g)>();
       __builtin_amdgcn_sched_barrier(0);
       read_frag(i + 1, fn);
       if (g == 3) read_hdr((i >> 2) + 1, hd);
@@ -295,20 +319,31 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void k_gemm_q4k_stream(const 
 
 int gemm_stream_tiles(int64_t n) { return static_cast<int>((n + 63) / 64); }
 
-hipError_t launch_gemm_stream(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
-                              int64_t k, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_stream(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                         int64_t k, hipStream_t stream) {
   const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
   if (mi <= 8) {
-    hipLaunchKernelGGL((k_gemm_q4k_stream<1, 8>), dim3((ni + 31) / 32), dim3(256), 0, stream, w,
-                       x, y, mi, ni, ki);
+    hipLaunchKernelGGL((k_gemm_q4k_stream<1, 8, FMT>), dim3((ni + 31) / 32), dim3(256), 0,
+                       stream, w, x, y, mi, ni, ki);
   } else if (mi <= 16) {
-    hipLaunchKernelGGL((k_gemm_q4k_stream<1, 16>), dim3((ni + 31) / 32), dim3(256), 0, stream, w,
-                       x, y, mi, ni, ki);
+    hipLaunchKernelGGL((k_gemm_q4k_stream<1, 16, FMT>), dim3((ni + 31) / 32), dim3(256), 0,
+                       stream, w, x, y, mi, ni, ki);
   } else {
-    hipLaunchKernelGGL((k_gemm_q4k_stream<2, 32>), dim3((ni + 63) / 64), dim3(256), 0, stream, w,
-                       x, y, mi, ni, ki);
+    hipLaunchKernelGGL((k_gemm_q4k_stream<2, 32, FMT>), dim3((ni + 63) / 64), dim3(256), 0,
+                       stream, w, x, y, mi, ni, ki);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_stream(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                              int64_t k, hipStream_t stream) {
+  return launch_stream<4>(w, x, y, m, n, k, stream);
+}
+
+hipError_t launch_q5k_gemm_stream(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
+                                  int64_t n, int64_t k, hipStream_t stream) {
+  return launch_stream<5>(w, x, y, m, n, k, stream);
 }
 
 }  // namespace q4k

@@ -20,8 +20,7 @@ constexpr int kGemmBigTiles = 128;
 // use the mid-tile kernel; smaller grids split K over 128 x 128 tiles.
 constexpr int kGemmMidTiles = 192;
 // Batches of at most 32 rows with at least this many 64-row weight tiles use
-// the streaming kernel (Q4_K) or the 32 x 64 K-slice kernel (Q5_K); smaller
-// ones split K over 128-row tiles.
+// the streaming kernel; smaller ones split K over 128-row tiles.
 constexpr int kGemmSmallTiles = 128;
 // Batch-1 matrices of at most this many rows run 16 waves per workgroup.
 constexpr int64_t kGemvWideRows = 8192;
@@ -67,10 +66,13 @@ hipError_t launch_q5k_dequant_bf16(const uint8_t* w, uint16_t* out, int64_t n, i
 
 hipError_t launch_gemm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);
-// Q4_K GEMM for m <= 32 (k_gemm_stream.hip): one workgroup per 64 weight rows.
+// Q4_K and Q5_K GEMM for m <= 32 (k_gemm_stream.hip); gemm_stream_tiles(n)
+// counts its 64-row weight tiles.
 int gemm_stream_tiles(int64_t n);
 hipError_t launch_gemm_stream(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                               int64_t k, hipStream_t stream);
+hipError_t launch_q5k_gemm_stream(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
+                                  int64_t n, int64_t k, hipStream_t stream);
 
 // Q6_K (210-byte blocks): GEMV (passes of up to 4 x rows) and the dequant exports.
 hipError_t launch_q6k_gemv(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,

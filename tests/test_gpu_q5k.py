@@ -194,22 +194,24 @@ def test_q5k_gemv_split_batches(q4k, m, n, k):
     assert_within(y, yr, a, GEMV_TOL, "q5k split gemv m=%d %dx%d" % (m, n, k))
 
 
-# Grids that take the K-slice kernels on 176-byte records: m <= 32 with at
-# least 128 tiles of 32 x 64, and m > 32 with at least 192 tiles of 64 x 128,
-# else of 64 x 64 (ragged M and N tiles, one to several super-blocks).  The result is the dot
-# of the bf16 X with the bf16 weights of the dequant export, up to fp32
-# summation order.
-@pytest.mark.parametrize("m,n,k", [(1, 8192, 1024), (5, 8200, 512), (32, 8192, 768),
-                                   (330, 4000, 512), (384, 4096, 256), (256, 4096, 512),
-                                   (129, 6000, 256)])
-def test_q5k_gemm_kslice_bf16_weight_dot(q4k, m, n, k):
+# Grids that take the streaming kernel on 176-byte records (m <= 32 with at
+# least 128 weight tiles of 64 rows; X staged for 8, 16 or 32 rows, 1 to 9
+# super-blocks so that some waves have none or an odd count) and the K-slice
+# kernels (m > 32 with at least 192 tiles of 64 x 128, else of 64 x 64; ragged
+# M and N tiles).  The result is the dot of the bf16 X with the bf16 weights
+# of the dequant export, up to fp32 summation order.
+@pytest.mark.parametrize("m,n,k", [(1, 8192, 1024), (5, 8200, 512), (8, 8192, 256),
+                                   (9, 8200, 1280), (16, 8192, 2304), (17, 9000, 768),
+                                   (32, 8192, 768), (330, 4000, 512), (384, 4096, 256),
+                                   (256, 4096, 512), (129, 6000, 256)])
+def test_q5k_gemm_bf16_weight_dot(q4k, m, n, k):
     w = synth.q5k_weights(n, k, seed=m + 7)
     xb = synth.normal_bf16((m, k), seed=m + 7)
     Y = q4k.q5k_gemm(dev(w), dev_bf16(xb)).cpu().numpy().astype(np.float64)
     Wb = oracle.q5k_dequant_bf16(w, n, k)
     Wf = (Wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     Xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    assert_within(Y, Xf @ Wf.T, np.abs(Xf) @ np.abs(Wf.T), 1e-5, "q5k kslice %dx%dx%d" % (m, n, k))
+    assert_within(Y, Xf @ Wf.T, np.abs(Xf) @ np.abs(Wf.T), 1e-5, "q5k gemm %dx%dx%d" % (m, n, k))
     if m <= 32:
         Yr, A = oracle.q5k_gemm(w, xb, n, k)
-        assert_within(Y, Yr, A, GEMM_TOL, "q5k kslice %dx%dx%d vs oracle" % (m, n, k))
+        assert_within(Y, Yr, A, GEMM_TOL, "q5k gemm %dx%dx%d vs oracle" % (m, n, k))

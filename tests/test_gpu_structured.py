@@ -263,7 +263,8 @@ def test_q4k_gemm_structured(q4k, m, n, k):
     assert_within(Y[:, cols], Yr, A, GEMM_TOL, "q4k_gemm %dx%dx%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 130, 1024), (40, 300, 768), (512, 4096, 512)])
+@pytest.mark.parametrize("m,n,k", [(1, 130, 1024), (7, 8200, 256), (12, 8192, 1280),
+                                   (30, 8256, 768), (40, 300, 768), (512, 4096, 512)])
 def test_q5k_gemm_structured(q4k, m, n, k):
     w = tile(q5k_kinds(), n, k, seed=m + n)
     xb = synth.normal_bf16((m, k), seed=m + k)
