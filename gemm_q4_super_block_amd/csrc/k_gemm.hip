@@ -529,9 +529,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __re
 // (32 TI) x (32 NJ TI) output tiles with K split four ways inside the
 // workgroup, for grids that the 128 x 256 tiles cannot fill without splitting
 // K across workgroups (m=512, n=4096: TI=NJ=2, 256 tiles of 64 x 128; m=256,
-// n=4096: TI=2, NJ=1, 256 tiles of 64 x 64; m <= 32, n=14336: TI=1, NJ=2, 224
-// tiles of 32 x 64).  Splitting K across workgroups would need fp32 atomics (about one per
-// L2 channel per clock, ~25 us for the m=512, n=4096 output) or a second pass.
+// n=4096: TI=2, NJ=1, 256 tiles of 64 x 64; batches of at most 32 rows take
+// the streaming kernel of k_gemm_stream.hip).  Splitting K across workgroups
+// would need fp32 atomics (about one per L2 channel per clock: 29 us measured
+// for the 8 M adds of the m=512, n=4096 output split four ways) or a second
+// pass.
 //   * 4 TI waves = 4 K slices x TI N halves.  Wave (kq, wn) owns all 32 TI
 //     rows x 32 NJ columns of its half (TI x NJ accumulators) and, in every 64-wide
 //     K step, k = 32 p + 16 b + 8 h + (0..7) with p = kq / 2 (nibble parity),
