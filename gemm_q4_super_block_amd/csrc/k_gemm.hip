@@ -294,12 +294,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_q4k_128x256(const uint8_t* __re
   // The tile's first weight row, in 64 bits; offsets inside the tile's 256
   // rows stay below 2^32 (k <= 2^24, checked by the C ABI).
   const uint8_t* const wt = w + static_cast<size_t>(n0) * row_bytes;
-  const int sb_rot = (tn * 7) % nsb;
-  // Super-block of logical super-block S (indices past the end repeat the last).
-  auto phys_sb = [&](int S) {
-    const int e = min(S, nsb - 1) + sb_rot;
-    return e < nsb ? e : e - nsb;
-  };
+  // Super-block of step group S (indices past the end repeat the last).  Every
+  // tile walks K from super-block 0, so the tiles of one XCD that share X rows
+  // read the same K window of X at the same time and find it in their L2.
+  auto phys_sb = [&](int S) { return min(S, nsb - 1); };
 
   // X copy q of this wave fills tile rows 8 (4 wave + q) .. +7; lane ->
   // (row, LDS chunk lane % 8) holding X chunk (lane % 8) ^ swz(row).
@@ -611,11 +609,7 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   // The tile's first weight row, in 64 bits; offsets inside the tile stay
   // below 2^32 (k <= 2^24, checked by the C ABI).
   const uint8_t* const wt = w + static_cast<size_t>(n0) * row_bytes;
-  const int sb_rot = (tn * 7) % nsb;
-  auto phys_sb = [&](int S) {
-    const int e = min(S, nsb - 1) + sb_rot;
-    return e < nsb ? e : e - nsb;
-  };
+  auto phys_sb = [&](int S) { return min(S, nsb - 1); };  // K from super-block 0 (as above)
   // X copy of this wave: tile rows 8 wave .. +7.
   const uint16_t* xsrc;
   {
