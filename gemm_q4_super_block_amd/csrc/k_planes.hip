@@ -47,6 +47,7 @@
 //     exact weight rounded once) or its bf16 (nearest even).
 #include <hip/hip_runtime.h>
 
+#include "lds_copy.h"
 #include "q4k_device.h"
 #include "q4k_launch.h"
 
@@ -261,6 +262,118 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_planes(const uint8_t* __res
 }
 
 // One thread per unit of the matrix (8 per block, blocks in row-major order).
+// The same GEMV with each wave's weight rows staged through LDS: per K chunk
+// a wave copies the chunk's bytes of its RPW rows (one contiguous range per
+// row, from the 16-byte boundary at or below its start) straight into its own
+// part of LDS with 16-byte-per-lane copies, and the units are then read from
+// LDS exactly as the kernel above reads them from memory (the LDS copy keeps
+// each byte's address mod 16).  A row's records are fetched by a few wide,
+// contiguous loads instead of four to five small loads per unit.  The copied
+// range ends at most 15 bytes past the chunk, so the host takes this kernel
+// only when the matrix ends on a 16-byte boundary (n * k / 256 a multiple
+// of 8).
+template <int FMT>
+struct PlaneRows {
+  static constexpr int Units = (kPlaneChunk / 256 * Planes<FMT>::Bytes + 14 + 15) / 16;
+  static constexpr int Copies = (Units + 63) / 64;  // 16-byte-per-lane copies per row
+  static constexpr int Lds = Copies * 1024;          // LDS bytes per row
+};
+
+template <int FMT, int WAVES, int RPW, int MT>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_planes_lds(const uint8_t* __restrict__ w,
+                                                                const float* __restrict__ x,
+                                                                float* __restrict__ y, int n,
+                                                                int k, int mrows) {
+  using P = Planes<FMT>;
+  using RL = PlaneRows<FMT>;
+  __shared__ __attribute__((aligned(16))) float xs[MT][kPlaneChunk];
+  __shared__ __attribute__((aligned(16))) uint8_t wl[WAVES][RPW][RL::Lds];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = (blockIdx.x * WAVES + wave) * RPW;
+  const size_t row_bytes = static_cast<size_t>(k >> 8) * P::Bytes;
+  const uint8_t* rows[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+    rows[r] = w + static_cast<size_t>(min(row0 + r, n - 1)) * row_bytes;
+  float acc[MT][RPW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[i][r] = 0.0f;
+
+  for (int c0 = 0; c0 < k; c0 += kPlaneChunk) {
+    const int kc = min(kPlaneChunk, k - c0);  // a multiple of 256
+    const int units = kc >> 5;                // 8 per block
+    const int cbytes = (kc >> 8) * P::Bytes;
+    if (c0 > 0) __syncthreads();  // the previous chunk's reads of xs are done
+    // Row r's chunk: bytes [g0, g0 + cbytes) copied from a = g0 rounded down
+    // to 16; unit u of the copy lands at LDS offset 16 u (units past the
+    // range repeat its last unit).
+    int off[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const uint8_t* g0 = rows[r] + static_cast<size_t>(c0 >> 8) * P::Bytes;
+      const uint8_t* a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(g0) & ~uintptr_t(15));
+      off[r] = static_cast<int>(g0 - a);
+      const int nu = (off[r] + cbytes + 15) >> 4;
+      const uint32_t dst = lds_address(&wl[wave][r][0]);
+#pragma unroll
+      for (int q = 0; q < RL::Copies; ++q)
+        copy16_to_lds(a + 16 * min(64 * q + lane, nu - 1),
+                      __builtin_amdgcn_readfirstlane(dst + 1024 * q));
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i >= mrows) break;
+      for (int e = 4 * static_cast<int>(threadIdx.x); e < kc; e += 4 * 64 * WAVES)
+        *reinterpret_cast<float4*>(&xs[i][e]) =
+            *reinterpret_cast<const float4*>(x + static_cast<size_t>(i) * k + c0 + e);
+    }
+    wait_copies_barrier<0>();
+#pragma unroll
+    for (int t = 0; t < kPlaneUnitsPerLane; ++t) {
+      const int u = lane + 64 * t;
+      if (u >= units) continue;
+      const int bl = u >> 3, h = (u >> 2) & 1, c = u & 3;
+      PlaneUnit wu[RPW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        wu[r] = P::decode(P::load(&wl[wave][r][off[r] + bl * P::Bytes], h, c), h, c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float qf[RPW][8];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[r][e] = ubyte_f32(wu[r].q[j][e >> 2], e & 3) - P::Off;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          if (i >= mrows) break;
+          const float* p = &xs[i][256 * bl + 128 * h + 32 * j + 8 * c];
+          const float4 a = *reinterpret_cast<const float4*>(p);
+          const float4 b = *reinterpret_cast<const float4*>(p + 4);
+          const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf(qf[r][e], xv[e], dot);
+            acc[i][r] = fmaf(wu[r].dsc[j], dot, acc[i][r]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float v = wave_sum(acc[i][r]);
+      if (lane == 0 && i < mrows && row0 + r < n) y[static_cast<size_t>(i) * n + row0 + r] = v;
+    }
+}
+
 template <int FMT, bool BF16>
 __global__ __launch_bounds__(256) void k_dequant_planes(const uint8_t* __restrict__ w,
                                                         void* __restrict__ out, int64_t units) {
@@ -559,19 +672,32 @@ hipError_t launch_gemv_planes(const uint8_t* w, const float* x, float* y, int64_
   const int ni = static_cast<int>(n), ki = static_cast<int>(k);
   const int rows_per_wg = WAVES * RPW;
   const dim3 grid(static_cast<unsigned>((ni + rows_per_wg - 1) / rows_per_wg));
+  // Rows through LDS when the copies' 16-byte rounding stays inside the matrix.
+  const bool staged = (n * (k / 256)) % 8 == 0;
   for (int64_t i0 = 0; i0 < m; i0 += 4) {
     const int mm = static_cast<int>(m - i0 < 4 ? m - i0 : 4);
     const float* xs = x + i0 * k;
     float* ys = y + i0 * n;
-    if (mm == 1)
+    if (staged) {
+      if (mm == 1)
+        hipLaunchKernelGGL((k_gemv_planes_lds<FMT, WAVES, RPW, 1>), grid, dim3(64 * WAVES), 0,
+                           stream, w, xs, ys, ni, ki, mm);
+      else if (mm == 2)
+        hipLaunchKernelGGL((k_gemv_planes_lds<FMT, WAVES, RPW, 2>), grid, dim3(64 * WAVES), 0,
+                           stream, w, xs, ys, ni, ki, mm);
+      else
+        hipLaunchKernelGGL((k_gemv_planes_lds<FMT, WAVES, RPW, 4>), grid, dim3(64 * WAVES), 0,
+                           stream, w, xs, ys, ni, ki, mm);
+    } else if (mm == 1) {
       hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, 1>), grid, dim3(64 * WAVES), 0, stream,
                          w, xs, ys, ni, ki, mm);
-    else if (mm == 2)
+    } else if (mm == 2) {
       hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, 2>), grid, dim3(64 * WAVES), 0, stream,
                          w, xs, ys, ni, ki, mm);
-    else
+    } else {
       hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, 4>), grid, dim3(64 * WAVES), 0, stream,
                          w, xs, ys, ni, ki, mm);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
