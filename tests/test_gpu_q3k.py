@@ -78,6 +78,11 @@ def assert_within(got, ref, scale, what):
     (64, 512, 5, 7),        # two passes: 4 + 1
     (50, 4352, 8, 8),       # two full passes, x past one chunk
     (17, 256, 2, 9),        # a pass of 2
+    # rows staged through LDS (n * k / 256 a multiple of 8) that start at
+    # varying offsets mod 16: two chunks, the last one block wide; a batch
+    (8, 4352, 1, 10),
+    (24, 8448, 3, 11),
+    (40, 1280, 2, 12),
 ])
 def test_q3k_gemv(q4k, n, k, m, seed):
     w = synth.q3k_weights(n, k, seed=seed)

@@ -225,7 +225,8 @@ def test_q5k_gemv_structured(q4k, m, n, k):
 
 # ------------------------------------------------------------------ Q6_K / Q3_K GEMV
 
-@pytest.mark.parametrize("m,n,k", [(1, 100, 1024), (2, 33, 768), (4, 40, 4352), (6, 17, 512)])
+@pytest.mark.parametrize("m,n,k", [(1, 100, 1024), (2, 33, 768), (4, 40, 4352), (6, 17, 512),
+                                   (1, 8, 4352), (3, 40, 1280)])
 def test_q6k_gemv_structured(q4k, m, n, k):
     w = tile(q6k_kinds(), n, k, seed=m + n)
     x = synth.normal_f32((m, k), seed=m + k)
@@ -235,7 +236,8 @@ def test_q6k_gemv_structured(q4k, m, n, k):
     assert_within(y, yr, a, GEMV_TOL, "q6k_gemv m=%d %dx%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 100, 1024), (3, 40, 768), (5, 17, 4352)])
+@pytest.mark.parametrize("m,n,k", [(1, 100, 1024), (3, 40, 768), (5, 17, 4352), (1, 8, 4352),
+                                   (2, 24, 8448)])
 def test_q3k_gemv_structured(q4k, m, n, k):
     w = tile(q3k_kinds(), n, k, seed=m + n)
     x = synth.normal_f32((m, k), seed=m + k)
