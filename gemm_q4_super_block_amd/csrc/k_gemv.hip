@@ -37,6 +37,7 @@
 
 #include <atomic>
 
+#include "lds_copy.h"
 #include "q4k_device.h"
 #include "q4k_launch.h"
 
@@ -354,6 +355,93 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
   gemv_body<MT, R, GLU, NWV, XREG, FMT>(w, w2, x, y, m, n, k);
 }
 
+// Batch-1 GEMV for k <= 4096 (one K step) and at most kGemvWideRows rows:
+// the arithmetic of gemv_body<1, 1, false, 16> (same loads, the same
+// per-lane order of every rounding, so the results are bit-identical), with
+// the generality a single row per wave does not need taken out: no row-set
+// or chunk loops, and x staged by one direct global -> LDS copy per thread
+// (issued before the weight loads) instead of loads and LDS stores.  The
+// LDS keeps x in 16-byte units, unit u at position u ^ ((u >> 4) & 15): the
+// 16 lanes of a quarter-wave read units 64 b + 16 g + c with 4 b + g running
+// over 16 values, which puts them in 16 different bank groups.
+__global__ __launch_bounds__(1024) void k_gemv_decode(const uint8_t* __restrict__ w,
+                                                      const float* __restrict__ x,
+                                                      float* __restrict__ y, int n, int k) {
+  __shared__ __attribute__((aligned(1024))) float xs[4096];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int b = lane >> 2;
+  const int g = lane & 3;
+  const int nsb = k >> 8;
+  const int row = blockIdx.x * 16 + wave;
+  const bool active = b < nsb;
+  // x: LDS unit p <- x unit p ^ ((p >> 4) & 15) (units past k / 4 repeat the last; unused).
+  {
+    const int u = min(t ^ ((t >> 4) & 15), (k >> 2) - 1);
+    const uint32_t dst = lds_address(xs) + static_cast<uint32_t>(wave) * 1024u;
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(x + 4 * u), "s"(__builtin_amdgcn_readfirstlane(dst))
+        : "memory", "m0");
+  }
+  // Weights of this lane: header and the 32 quant bytes of group g of block b.
+  const size_t row_bytes = static_cast<size_t>(nsb) * kBlockBytes;
+  const uint8_t* p = w + static_cast<size_t>(min(row, n - 1)) * row_bytes +
+                     static_cast<size_t>(min(b, nsb - 1)) * kBlockBytes;
+  const uint4 hd = load16(p);
+  const uint4 qa = load16(p + 16 + 32 * g);
+  const uint4 qb = load16(p + 32 + 32 * g);
+  // The x copy was issued before the three weight loads: it has landed once
+  // at most three loads are in flight.
+  asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
+
+  const int kb = active ? b : 0;
+  const int xkey = (4 * kb + g) & 15;
+  const float* xbase = xs + 4 * (64 * kb + 16 * g);
+  auto xunit = [&](int c) { return *reinterpret_cast<const f4_t*>(xbase + 4 * (c ^ xkey)); };
+  const GroupScales s = group_scales(hd, g);
+  float pl = 0.0f, ph = 0.0f;
+  f4_t xl_n = xunit(0), xh_n = xunit(8);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const f4_t xl = xl_n, xh = xh_n;
+    if (c < 7) {
+      xl_n = xunit(c + 1);
+      xh_n = xunit(c + 9);
+    }
+    const uint32_t v = c < 4 ? word(qa, c) : word(qb, c - 4);
+    const uint32_t lo = v & 0x0F0F0F0Fu;
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+    const f2_t l01 = fp8x2_lo(lo), l23 = fp8x2_hi(lo);
+    const f2_t h01 = fp8x2_lo(hi), h23 = fp8x2_hi(hi);
+    const float wl0 = __builtin_fmaf(s.a_lo, l01.x, -s.b_lo);
+    const float wl1 = __builtin_fmaf(s.a_lo, l01.y, -s.b_lo);
+    const float wl2 = __builtin_fmaf(s.a_lo, l23.x, -s.b_lo);
+    const float wl3 = __builtin_fmaf(s.a_lo, l23.y, -s.b_lo);
+    const float wh0 = __builtin_fmaf(s.a_hi, h01.x, -s.b_hi);
+    const float wh1 = __builtin_fmaf(s.a_hi, h01.y, -s.b_hi);
+    const float wh2 = __builtin_fmaf(s.a_hi, h23.x, -s.b_hi);
+    const float wh3 = __builtin_fmaf(s.a_hi, h23.y, -s.b_hi);
+    pl = __builtin_fmaf(wl0, xl.x, pl);
+    pl = __builtin_fmaf(wl1, xl.y, pl);
+    pl = __builtin_fmaf(wl2, xl.z, pl);
+    pl = __builtin_fmaf(wl3, xl.w, pl);
+    ph = __builtin_fmaf(wh0, xh.x, ph);
+    ph = __builtin_fmaf(wh1, xh.y, ph);
+    ph = __builtin_fmaf(wh2, xh.z, ph);
+    ph = __builtin_fmaf(wh3, xh.w, ph);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float acc = 0.0f;
+  acc += active ? pl + ph : 0.0f;
+  const float v = wave_sum(acc);
+  if (lane == 0 && row < n) y[row] = v;
+}
+
 // Independent batch-1 GEMVs of one shape in one persistent launch: y[l] =
 // W[l] x[l] for l < layers (k <= kGemvLayersMaxK).  The work mapping of the
 // batch-1 GEMV above (lane = super-block slot x quant group, one row per
@@ -608,8 +696,14 @@ hipError_t launch_gemv_passes(const uint8_t* w, const float* x, float* y, int64_
     // workgroup (x staged once per 16 waves).  Taller ones take 4 waves and,
     // within one K step (k <= 4096), keep x in registers across their rows;
     // past one K step, 8 waves.
-    if (n <= kGemvWideRows)
+    if (n <= kGemvWideRows) {
+      if (FMT == 4 && ki <= 4096) {
+        hipLaunchKernelGGL(k_gemv_decode, dim3((ni + 15) / 16), dim3(1024), 0, stream, w, x, y,
+                           ni, ki);
+        return hipGetLastError();
+      }
       return launch<1, kGemvRowsPerWave, false, 16, false, FMT>(w, w, x, y, mm, ni, ki, stream);
+    }
     if (k <= 4096)
       return launch<1, kGemvRowsPerWave, false, 4, true, FMT>(w, w, x, y, mm, ni, ki, stream);
     return launch<1, kGemvRowsPerWave, false, 8, false, FMT>(w, w, x, y, mm, ni, ki, stream);
