@@ -747,7 +747,9 @@ __global__ __launch_bounds__(256 * TI, 1) void k_gemm_q4k_kslice(const uint8_t* 
   read_q(0, 0, Q0);
   read_q(0, 1, Q1);
   read_x(0, A0);
-  wait_copies_barrier<8 + 2 * CW>();
+  // The end of step -1: every copy of step -8 and before has landed, X(1)
+  // among them (step 0 reads it).  After X(1) came X(2..8), W(1) and W(2).
+  wait_copies_barrier<7 + 2 * CW>();
   scales_load(0, sa, sb);
   bf16x8_t B0[NJ], B1[NJ];
   dequant(Q0, 0, sa[0], sb[0], B0);
