@@ -531,7 +531,7 @@ def main():
     if head:
         out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": head["hbm_frac"], "traffic": traffic("gemv_4096x4096"),
-                           "kernel": "k_gemv_q4k<1, 1, false, 16, false, 4>",
+                           "kernel": "k_gemv_decode",
                            "bytes_per_launch": 9469952, **timing(head)}
     if gemm:
         out["roofline_gemm"] = {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS,
@@ -631,6 +631,8 @@ def _template_args(name, kernel):
 def dispatch_workload(name, threads, lds, hint=""):
     if "k_gemv_layers" in name:
         return "gemv_layers_%dx4096x4096" % LAYERS
+    if "k_gemv_decode" in name:
+        return "gemv_4096x4096"
     gv = _template_args(name, "k_gemv_q4k")
     if gv:
         # <MT, R, GLU, NWV, XREG, FMT>

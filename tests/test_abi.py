@@ -123,6 +123,7 @@ def test_shipped_launch_shapes_are_pinned():
     launch = open(os.path.join(src, "q4k_launch.h")).read()
     assert re.search(r"kGemvRowsPerWave = 1;", launch)
     assert re.search(r"kGemvWideRows = 8192;", launch)
+    assert re.search(r"kDecodeWaves = 8;", launch)
     assert re.search(r"kGateUpRowsPerWave = 1;", launch)
     gemm = open(os.path.join(src, "k_gemm.hip")).read()
     assert re.search(r"kBN = 128;", gemm) and re.search(r"kBK = 64;", gemm)

@@ -30,6 +30,7 @@ CASES = [
     ("k_gemv_planes<3, 8, 2, 1>", 4096 // 16 * 512, 16384, "", "q3k_gemv_4096x4096"),
     ("k_gemv_split<1, 2, 4>", 0, 0, "", "sweep_gemv_14336x4096_split"),
     ("k_gemv_layers", 256 * 1024, 0, "", "gemv_layers_8x4096x4096"),
+    ("k_gemv_decode", 256 * 1024, 16384, "", "gemv_4096x4096"),
     ("k_w8a8_gemm<1, 1, 2, 1>", 48 * 16 * 256, 32768, "", "w8a8_linear_1024x3072x3072"),
     ("k_w8a8_gemm<2, 2, 2, 1>", 24 * 64 * 256, 65536, "", "w8a8_linear_8192x3072x3072"),
     ("k_w8a8_quantize_rows<8>", 1024 * 64, 0, "", "w8a8_quantize_1024x3072"),
