@@ -33,6 +33,12 @@
 //     fp8 value q * 2^-9), two per instruction, and each weight is formed once
 //     whatever MT.
 //   * lanes reduce with DPP and two cross-row swizzles; lane 0 stores.
+//   * batch 1 with k <= 16384 -- matrices of up to 8192 rows, and the gate/up
+//     pair of the MLP at any d_ff -- takes k_gemv_decode: the same per-lane
+//     arithmetic with one row per wave, every K step's weights issued at once
+//     and x staged by direct global -> LDS copies.  The gate and up rows of a
+//     row index go to two waves of one workgroup, which read the one staged x;
+//     the gate wave forms h from u passed through LDS.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -355,97 +361,133 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
   gemv_body<MT, R, GLU, NWV, XREG, FMT>(w, w2, x, y, m, n, k);
 }
 
-// Batch-1 GEMV for k <= 4096 (one K step) and at most kGemvWideRows rows:
-// the arithmetic of gemv_body<1, 1, false, 16> (same loads, the same
-// per-lane order of every rounding, so the results are bit-identical), with
-// the generality a single row per wave does not need taken out: no row-set
-// or chunk loops, and x staged by direct global -> LDS copies (issued before
-// the weight loads) instead of loads and LDS stores.  NW waves (rows) per
-// workgroup; 8 measured fastest at 4096 x 4096 (4.7 us against 4.9 for 4 and
-// 5.0 for 16), two workgroups per CU each staging its own copy of x.  The
-// LDS keeps x in 16-byte units, unit u at position u ^ ((u >> 4) & 15): the
-// 16 lanes of a quarter-wave read units 64 b + 16 g + c with 4 b + g running
-// over 16 values, which puts them in 16 different bank groups.
-template <int NW>
+// Batch-1 GEMV for k <= 4096 NS (NS K steps of 4096) and at most
+// kGemvWideRows rows: the arithmetic of gemv_body<1, 1, false, 16> (same
+// loads, the same per-lane order of every rounding, step partials added in
+// step order, so the results are bit-identical), with the generality a
+// single row per wave does not need taken out: no row-set or chunk loops,
+// every step's weight loads issued at once, and x staged by direct global ->
+// LDS copies (issued before the weight loads) instead of loads and LDS
+// stores.  NW waves (rows) per workgroup; 8 measured fastest at 4096 x 4096
+// (4.7 us against 4.9 for 4 and 5.0 for 16), two workgroups per CU each
+// staging its own copy of x (from L2).  The LDS holds x in 16-byte units with
+// one spare unit after every 16 (unit 16 G + r at position 17 G + r, the
+// layout xs_index gives the general kernel): the 16 lanes of a quarter-wave
+// read units 16 G + c for 16 consecutive G, which fall in 16 different bank
+// groups, and a lane's 16 units of a step sit at immediate offsets from one
+// address.  The staging copies fill the positions in order, each lane
+// fetching the unit its position holds.
+//
+// GLU: the gate/up pair of the MLP.  Waves 2 i and 2 i + 1 take row i of the
+// workgroup in W_gate (w) and W_up (w2), both reading the one staged x, and
+// y = h = silu(g) * u from the two dots (u passed through LDS).
+template <int NW, int NS, bool GLU>
 __global__ __launch_bounds__(64 * NW) void k_gemv_decode(const uint8_t* __restrict__ w,
+                                                         const uint8_t* __restrict__ w2,
                                                          const float* __restrict__ x,
                                                          float* __restrict__ y, int n, int k) {
-  __shared__ __attribute__((aligned(1024))) float xs[4096];
+  constexpr int XPOS = 17 * 64 * NS;  // LDS positions: 17 per 16 x units
+  constexpr int RW = GLU ? NW / 2 : NW;  // rows per workgroup
+  __shared__ __attribute__((aligned(1024))) float xs[4 * XPOS];
+  __shared__ float up[GLU ? RW : 1];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   const int b = lane >> 2;
   const int g = lane & 3;
   const int nsb = k >> 8;
-  const int row = blockIdx.x * NW + wave;
-  const bool active = b < nsb;
-  // x: LDS unit p <- x unit p ^ ((p >> 4) & 15) (units past k / 4 repeat the
-  // last; unused); 16 / NW copies per thread.
+  const int row = blockIdx.x * RW + (GLU ? wave >> 1 : wave);
+  const bool is_up = GLU && (wave & 1);
+  // x: copy q of this wave fills positions 64 (wave + NW q) .. + 63, lane l
+  // position p = 17 grp + r, r = p mod 17 (kept as the copies advance by
+  // 64 NW positions); spare positions and units past k / 4 take the last unit
+  // of their group or of x (never read).
+  {
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    int grp = (64 * wave + lane) / 17;
+    int r = 64 * wave + lane - 17 * grp;
 #pragma unroll
-  for (int q = 0; q < 16 / NW; ++q) {
-    const int p = t + 64 * NW * q;
-    const int u = min(p ^ ((p >> 4) & 15), (k >> 2) - 1);
-    const uint32_t dst = lds_address(xs) + static_cast<uint32_t>(wave + NW * q) * 1024u;
-    asm volatile(
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, off"
-        :
-        : "v"(x + 4 * u), "s"(__builtin_amdgcn_readfirstlane(dst))
-        : "memory", "m0");
-  }
-  // Weights of this lane: header and the 32 quant bytes of group g of block b.
-  const size_t row_bytes = static_cast<size_t>(nsb) * kBlockBytes;
-  const uint8_t* p = w + static_cast<size_t>(min(row, n - 1)) * row_bytes +
-                     static_cast<size_t>(min(b, nsb - 1)) * kBlockBytes;
-  const uint4 hd = load16(p);
-  const uint4 qa = load16(p + 16 + 32 * g);
-  const uint4 qb = load16(p + 32 + 32 * g);
-  // The x copies were issued before the three weight loads: they have landed
-  // once at most three loads are in flight.
-  asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
-
-  const int kb = active ? b : 0;
-  const int xkey = (4 * kb + g) & 15;
-  const float* xbase = xs + 4 * (64 * kb + 16 * g);
-  auto xunit = [&](int c) { return *reinterpret_cast<const f4_t*>(xbase + 4 * (c ^ xkey)); };
-  const GroupScales s = group_scales(hd, g);
-  float pl = 0.0f, ph = 0.0f;
-  f4_t xl_n = xunit(0), xh_n = xunit(8);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const f4_t xl = xl_n, xh = xh_n;
-    if (c < 7) {
-      xl_n = xunit(c + 1);
-      xh_n = xunit(c + 9);
+    for (int q = 0; q < (XPOS + 64 * NW - 1) / (64 * NW); ++q) {
+      const int base = 64 * (wu + NW * q);
+      if (base < XPOS) {
+        const int u = min(16 * grp + min(r, 15), (k >> 2) - 1);
+        copy16_to_lds(x + 4 * u, lds_address(xs) + 16u * static_cast<uint32_t>(base));
+      }
+      r += (64 * NW) % 17;
+      grp += (64 * NW) / 17;
+      if (r >= 17) {
+        r -= 17;
+        ++grp;
+      }
     }
-    const uint32_t v = c < 4 ? word(qa, c) : word(qb, c - 4);
-    const uint32_t lo = v & 0x0F0F0F0Fu;
-    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
-    const f2_t l01 = fp8x2_lo(lo), l23 = fp8x2_hi(lo);
-    const f2_t h01 = fp8x2_lo(hi), h23 = fp8x2_hi(hi);
-    const float wl0 = __builtin_fmaf(s.a_lo, l01.x, -s.b_lo);
-    const float wl1 = __builtin_fmaf(s.a_lo, l01.y, -s.b_lo);
-    const float wl2 = __builtin_fmaf(s.a_lo, l23.x, -s.b_lo);
-    const float wl3 = __builtin_fmaf(s.a_lo, l23.y, -s.b_lo);
-    const float wh0 = __builtin_fmaf(s.a_hi, h01.x, -s.b_hi);
-    const float wh1 = __builtin_fmaf(s.a_hi, h01.y, -s.b_hi);
-    const float wh2 = __builtin_fmaf(s.a_hi, h23.x, -s.b_hi);
-    const float wh3 = __builtin_fmaf(s.a_hi, h23.y, -s.b_hi);
-    pl = __builtin_fmaf(wl0, xl.x, pl);
-    pl = __builtin_fmaf(wl1, xl.y, pl);
-    pl = __builtin_fmaf(wl2, xl.z, pl);
-    pl = __builtin_fmaf(wl3, xl.w, pl);
-    ph = __builtin_fmaf(wh0, xh.x, ph);
-    ph = __builtin_fmaf(wh1, xh.y, ph);
-    ph = __builtin_fmaf(wh2, xh.z, ph);
-    ph = __builtin_fmaf(wh3, xh.w, ph);
-    __builtin_amdgcn_sched_barrier(0);
   }
+  // Weights of this lane, step st: header and the 32 quant bytes of group g
+  // of block 16 st + b (lanes past the last block read the last one and add
+  // nothing).
+  const size_t row_bytes = static_cast<size_t>(nsb) * kBlockBytes;
+  const uint8_t* const wr = (is_up ? w2 : w) + static_cast<size_t>(min(row, n - 1)) * row_bytes;
+  uint4 hd[NS], qa[NS], qb[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const uint8_t* p = wr + static_cast<size_t>(min(16 * st + b, nsb - 1)) * kBlockBytes;
+    hd[st] = load16(p);
+    qa[st] = load16(p + 16 + 32 * g);
+    qb[st] = load16(p + 32 + 32 * g);
+  }
+  // The x copies were issued before the 3 NS weight loads: they have landed
+  // once at most 3 NS loads are in flight.
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(3 * NS) : "memory");
+
   float acc = 0.0f;
-  acc += active ? pl + ph : 0.0f;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const bool active = 16 * st + b < nsb;
+    const int kb = active ? 16 * st + b : 0;
+    // units 16 (4 kb + g) + c: c < 8 low-nibble weights, c >= 8 high
+    const f4_t* xg = reinterpret_cast<const f4_t*>(xs) + 17 * (4 * kb + g);
+    const GroupScales s = group_scales(hd[st], g);
+    float pl = 0.0f, ph = 0.0f;
+    f4_t xl_n = xg[0], xh_n = xg[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const f4_t xl = xl_n, xh = xh_n;
+      if (c < 7) {
+        xl_n = xg[c + 1];
+        xh_n = xg[c + 9];
+      }
+      const uint32_t v = c < 4 ? word(qa[st], c) : word(qb[st], c - 4);
+      const uint32_t lo = v & 0x0F0F0F0Fu;
+      const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+      const f2_t l01 = fp8x2_lo(lo), l23 = fp8x2_hi(lo);
+      const f2_t h01 = fp8x2_lo(hi), h23 = fp8x2_hi(hi);
+      const float wl0 = __builtin_fmaf(s.a_lo, l01.x, -s.b_lo);
+      const float wl1 = __builtin_fmaf(s.a_lo, l01.y, -s.b_lo);
+      const float wl2 = __builtin_fmaf(s.a_lo, l23.x, -s.b_lo);
+      const float wl3 = __builtin_fmaf(s.a_lo, l23.y, -s.b_lo);
+      const float wh0 = __builtin_fmaf(s.a_hi, h01.x, -s.b_hi);
+      const float wh1 = __builtin_fmaf(s.a_hi, h01.y, -s.b_hi);
+      const float wh2 = __builtin_fmaf(s.a_hi, h23.x, -s.b_hi);
+      const float wh3 = __builtin_fmaf(s.a_hi, h23.y, -s.b_hi);
+      pl = __builtin_fmaf(wl0, xl.x, pl);
+      pl = __builtin_fmaf(wl1, xl.y, pl);
+      pl = __builtin_fmaf(wl2, xl.z, pl);
+      pl = __builtin_fmaf(wl3, xl.w, pl);
+      ph = __builtin_fmaf(wh0, xh.x, ph);
+      ph = __builtin_fmaf(wh1, xh.y, ph);
+      ph = __builtin_fmaf(wh2, xh.z, ph);
+      ph = __builtin_fmaf(wh3, xh.w, ph);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    acc += active ? pl + ph : 0.0f;
+  }
   const float v = wave_sum(acc);
-  if (lane == 0 && row < n) y[row] = v;
+  if constexpr (GLU) {
+    if (is_up && lane == 0) up[wave >> 1] = v;
+    __syncthreads();
+    if (!is_up && lane == 0 && row < n) y[row] = silu(v) * up[wave >> 1];
+  } else {
+    if (lane == 0 && row < n) y[row] = v;
+  }
 }
 
 // Independent batch-1 GEMVs of one shape in one persistent launch: y[l] =
@@ -691,6 +733,23 @@ hipError_t launch_layers(const LayerPtrs& p, int layers, int n, int k, hipStream
   return hipGetLastError();
 }
 
+// The decode kernel for k <= 16384: one to four K steps.
+template <int NW, bool GLU>
+hipError_t launch_decode(const uint8_t* w, const uint8_t* w2, const float* x, float* y, int n,
+                         int k, hipStream_t stream) {
+  constexpr int RW = GLU ? NW / 2 : NW;
+  const dim3 grid((n + RW - 1) / RW), block(64 * NW);
+  if (k <= 4096)
+    hipLaunchKernelGGL((k_gemv_decode<NW, 1, GLU>), grid, block, 0, stream, w, w2, x, y, n, k);
+  else if (k <= 2 * 4096)
+    hipLaunchKernelGGL((k_gemv_decode<NW, 2, GLU>), grid, block, 0, stream, w, w2, x, y, n, k);
+  else if (k <= 3 * 4096)
+    hipLaunchKernelGGL((k_gemv_decode<NW, 3, GLU>), grid, block, 0, stream, w, w2, x, y, n, k);
+  else
+    hipLaunchKernelGGL((k_gemv_decode<NW, 4, GLU>), grid, block, 0, stream, w, w2, x, y, n, k);
+  return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t launch_gemv_passes(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                               int64_t k, hipStream_t stream) {
@@ -698,16 +757,14 @@ hipError_t launch_gemv_passes(const uint8_t* w, const float* x, float* y, int64_
   const int mm = static_cast<int>(m);
   const int ni = static_cast<int>(n), ki = static_cast<int>(k);
   if (mm == 1) {
-    // One row per wave; matrices with few rows per CU take 16 waves per
-    // workgroup (x staged once per 16 waves).  Taller ones take 4 waves and,
-    // within one K step (k <= 4096), keep x in registers across their rows;
-    // past one K step, 8 waves.
+    // One row per wave.  Q4_K matrices of up to kGemvWideRows rows and
+    // k <= 16384 take the decode kernel (one x staging per workgroup of
+    // kDecodeWaves rows); the other formats there take the general kernel at
+    // 16 waves per workgroup.  Taller matrices take 4 waves and, within one K
+    // step (k <= 4096), keep x in registers across their rows; past one K
+    // step, 8 waves.
     if (n <= kGemvWideRows) {
-      if (FMT == 4 && ki <= 4096) {
-        hipLaunchKernelGGL(k_gemv_decode<kDecodeWaves>, dim3((ni + kDecodeWaves - 1) / kDecodeWaves),
-                           dim3(64 * kDecodeWaves), 0, stream, w, x, y, ni, ki);
-        return hipGetLastError();
-      }
+      if (FMT == 4 && ki <= 4 * 4096) return launch_decode<kDecodeWaves, false>(w, w, x, y, ni, ki, stream);
       return launch<1, kGemvRowsPerWave, false, 16, false, FMT>(w, w, x, y, mm, ni, ki, stream);
     }
     if (k <= 4096)
@@ -748,6 +805,9 @@ hipError_t launch_gemv_layers(const uint8_t* const* w, const float* const* x, fl
 
 hipError_t launch_gateup_swiglu(const uint8_t* w_gate, const uint8_t* w_up, const float* x,
                                 float* h, int64_t d_model, int64_t d_ff, hipStream_t stream) {
+  if (d_model <= 4 * 4096)
+    return launch_decode<kDecodeGluWaves, true>(w_gate, w_up, x, h, static_cast<int>(d_ff),
+                                                static_cast<int>(d_model), stream);
   return launch<1, kGateUpRowsPerWave, true, 8>(w_gate, w_up, x, h, 1, static_cast<int>(d_ff),
                                                 static_cast<int>(d_model), stream);
 }

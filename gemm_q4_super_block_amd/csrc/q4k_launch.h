@@ -23,9 +23,12 @@ constexpr int kGemmMidTiles = 192;
 // the streaming kernel; smaller ones split K over 128-row tiles.
 constexpr int kGemmSmallTiles = 128;
 // Batch-1 matrices of at most this many rows run 16 waves per workgroup
-// (k <= 4096 on Q4_K: the decode kernel, kDecodeWaves waves).
+// (k <= 16384 on Q4_K: the decode kernel, kDecodeWaves waves, one row each).
 constexpr int64_t kGemvWideRows = 8192;
 constexpr int kDecodeWaves = 8;
+// Waves per workgroup of the MLP's gate/up decode kernel (a gate and an up
+// wave per row) for d_model <= 16384.
+constexpr int kDecodeGluWaves = 8;
 // Q4_K and Q5_K GEMV batches of at least this many rows (up to 32) take the
 // split-bf16 MFMA kernel (k_gemv_split.hip) instead of the fp32 FMA passes
 // (which handle 1 to kGemvSplitMinM - 1 rows in one pass).

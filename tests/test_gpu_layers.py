@@ -52,9 +52,10 @@ def test_layers_match_the_oracle(q4k, layers, n, k, shared):
     _check(q4k, ws, xs, n, k, "%d layers %dx%d" % (layers, n, k))
 
 
-def test_layers_equal_separate_gemvs(q4k):
-    # the same per-row arithmetic as q4k_gemv: bit-identical outputs
-    n, k, layers = 1000, 1280, 5
+@pytest.mark.parametrize("n,k", [(1000, 1280), (257, 9216), (300, 14336)])
+def test_layers_equal_separate_gemvs(q4k, n, k):
+    # the same per-row arithmetic as q4k_gemv (one to four K steps): bit-identical outputs
+    layers = 5
     ws = [torch.from_numpy(synth.q4k_weights(n, k, seed=300 + l)).cuda() for l in range(layers)]
     xs = [torch.from_numpy(synth.normal_f32(k, seed=400 + l)).cuda() for l in range(layers)]
     ys = q4k.gemv_layers(ws, xs)
