@@ -33,8 +33,8 @@
 //     fp8 value q * 2^-9), two per instruction, and each weight is formed once
 //     whatever MT.
 //   * lanes reduce with DPP and two cross-row swizzles; lane 0 stores.
-//   * batch 1 with k <= 16384 -- matrices of up to 8192 rows, and the gate/up
-//     pair of the MLP at any d_ff -- takes k_gemv_decode: the same per-lane
+//   * batch 1 with k <= 16384 -- the GEMV at any row count, and the gate/up
+//     pair of the MLP -- takes k_gemv_decode: the same per-lane
 //     arithmetic with one row per wave, every K step's weights issued at once
 //     and x staged by direct global -> LDS copies.  The gate and up rows of a
 //     row index go to two waves of one workgroup, which read the one staged x;
@@ -77,19 +77,16 @@ struct WRegs {
 };
 
 // MT activation rows per pass, R weight rows per wave (times NW = 2 weight
-// matrices for the gate/up pair), NWV waves per workgroup.  XREG (batch 1,
-// k <= 4096: one K step, so a lane meets the same 64 x values in every row):
-// each lane holds its x slice in registers, read from LDS once while the
-// first weights are in flight.  FMT: 4 (Q4_K) or 5 (Q5_K: a lane also loads
+// matrices for the gate/up pair), NWV waves per workgroup.  FMT: 4 (Q4_K) or
+// 5 (Q5_K: a lane also loads
 // the block's 32 high-bit bytes and widens its 5-bit quant bytes exactly with
 // v_cvt_f32_ubyte, so its scale is d*sc without the 2^9 of the fp8 path).
-template <int MT, int R, bool GLU, int NWV, bool XREG, int FMT>
+template <int MT, int R, bool GLU, int NWV, int FMT>
 __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ w,
                                           const uint8_t* __restrict__ w2,
                                           const float* __restrict__ x, float* __restrict__ y,
                                           int m, int n, int k) {
   static_assert(!GLU || MT == 1, "the gate/up pair runs at batch 1");
-  static_assert(!XREG || MT == 1, "x in registers at batch 1 only");
   constexpr int NW = GLU ? 2 : 1;
   constexpr int NT = 64 * NWV;
   extern __shared__ float smem[];
@@ -122,7 +119,6 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ w,
 #pragma unroll
       for (int i = 0; i < MT; ++i) acc[u][r][i] = 0.0f;
 
-  f4_t xr[XREG ? 16 : 1];  // x[64g .. 64g+63] of super-block b (XREG)
   for (int c0 = 0; c0 < k; c0 += kXChunk<MT>) {
     const int kc = min(kXChunk<MT>, k - c0);
     const int s_begin = c0 >> 12;
@@ -184,7 +180,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ w,
       // read at use (their many accumulators leave no registers to spare).
       // A scheduling fence per slice keeps the compiler from hoisting all the
       // reads of a step (and spilling).
-      constexpr bool kAhead = MT == 1 && !XREG;
+      constexpr bool kAhead = MT == 1;
       f4_t xl_n[MT], xh_n[MT];
       if constexpr (kAhead) {
         xl_n[0] = *reinterpret_cast<const f4_t*>(xs + xo);
@@ -195,10 +191,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ w,
         f4_t xl[MT], xh[MT];
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          if constexpr (XREG) {
-            xl[i] = xr[c];
-            xh[i] = xr[8 + c];
-          } else if constexpr (kAhead) {
+          if constexpr (kAhead) {
             xl[i] = xl_n[i];
             xh[i] = xh_n[i];
             if (c < 7) {
@@ -330,17 +323,6 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ w,
       store_x16(idx, v);
     }
     __syncthreads();
-    if constexpr (XREG) {
-      // One K step: super-block b of the chunk (lanes past the last block read
-      // block 0 and add nothing).
-      const int kb_local = b < kb_count ? b : 0;
-      const int xo = xs_index(kb_local * kQK + 64 * g);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        xr[c] = *reinterpret_cast<const f4_t*>(xs + xo + 4 * c);
-        xr[8 + c] = *reinterpret_cast<const f4_t*>(xs + xo + 32 + 4 * c);
-      }
-    }
 
     for (int j = 0; j < jobs; j += 2) {
       if (j + 1 < jobs) issue(j + 1, bufB);
@@ -352,17 +334,17 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ w,
   }
 }
 
-template <int MT, int R, bool GLU, int NWV, bool XREG, int FMT = 4>
+template <int MT, int R, bool GLU, int NWV, int FMT = 4>
 __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict__ w,
                                                        const uint8_t* __restrict__ w2,
                                                        const float* __restrict__ x,
                                                        float* __restrict__ y, int m, int n,
                                                        int k) {
-  gemv_body<MT, R, GLU, NWV, XREG, FMT>(w, w2, x, y, m, n, k);
+  gemv_body<MT, R, GLU, NWV, FMT>(w, w2, x, y, m, n, k);
 }
 
-// Batch-1 GEMV for k <= 4096 NS (NS K steps of 4096) and at most
-// kGemvWideRows rows: the arithmetic of gemv_body<1, 1, false, 16> (same
+// Batch-1 GEMV for k <= 4096 NS (NS K steps of 4096): the arithmetic of
+// gemv_body<1, 1, false, 16> (same
 // loads, the same per-lane order of every rounding, step partials added in
 // step order, so the results are bit-identical), with the generality a
 // single row per wave does not need taken out: no row-set or chunk loops,
@@ -381,7 +363,10 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv_q4k(const uint8_t* __restrict
 // GLU: the gate/up pair of the MLP.  Waves 2 i and 2 i + 1 take row i of the
 // workgroup in W_gate (w) and W_up (w2), both reading the one staged x, and
 // y = h = silu(g) * u from the two dots (u passed through LDS).
-template <int NW, int NS, bool GLU>
+//
+// FMT 5: Q5_K blocks, with the two 16-byte loads of the high-bit plane per
+// step and the quant bytes widened as gemv_body does for that format.
+template <int NW, int NS, bool GLU, int FMT>
 __global__ __launch_bounds__(64 * NW) void k_gemv_decode(const uint8_t* __restrict__ w,
                                                          const uint8_t* __restrict__ w2,
                                                          const float* __restrict__ x,
@@ -424,19 +409,26 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_decode(const uint8_t* __restri
   // Weights of this lane, step st: header and the 32 quant bytes of group g
   // of block 16 st + b (lanes past the last block read the last one and add
   // nothing).
-  const size_t row_bytes = static_cast<size_t>(nsb) * kBlockBytes;
+  constexpr int kBB = block_bytes<FMT>();
+  constexpr int kQOff = FMT == 5 ? kQ5QuantOffset : 16;
+  constexpr int kLoads = FMT == 5 ? 5 : 3;  // 16-byte weight loads per step
+  const size_t row_bytes = static_cast<size_t>(nsb) * kBB;
   const uint8_t* const wr = (is_up ? w2 : w) + static_cast<size_t>(min(row, n - 1)) * row_bytes;
-  uint4 hd[NS], qa[NS], qb[NS];
+  uint4 hd[NS], qa[NS], qb[NS], h0[FMT == 5 ? NS : 1], h1[FMT == 5 ? NS : 1];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    const uint8_t* p = wr + static_cast<size_t>(min(16 * st + b, nsb - 1)) * kBlockBytes;
+    const uint8_t* p = wr + static_cast<size_t>(min(16 * st + b, nsb - 1)) * kBB;
     hd[st] = load16(p);
-    qa[st] = load16(p + 16 + 32 * g);
-    qb[st] = load16(p + 32 + 32 * g);
+    qa[st] = load16(p + kQOff + 32 * g);
+    qb[st] = load16(p + kQOff + 16 + 32 * g);
+    if constexpr (FMT == 5) {
+      h0[st] = load16(p + kQ5HighOffset);
+      h1[st] = load16(p + kQ5HighOffset + 16);
+    }
   }
-  // The x copies were issued before the 3 NS weight loads: they have landed
-  // once at most 3 NS loads are in flight.
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(3 * NS) : "memory");
+  // The x copies were issued before the kLoads NS weight loads: they have
+  // landed once at most kLoads NS loads are in flight.
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kLoads * NS) : "memory");
 
   float acc = 0.0f;
 #pragma unroll
@@ -445,7 +437,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_decode(const uint8_t* __restri
     const int kb = active ? 16 * st + b : 0;
     // units 16 (4 kb + g) + c: c < 8 low-nibble weights, c >= 8 high
     const f4_t* xg = reinterpret_cast<const f4_t*>(xs) + 17 * (4 * kb + g);
-    const GroupScales s = group_scales(hd[st], g);
+    GroupScales s = group_scales(hd[st], g);
+    if constexpr (FMT == 5) {  // the quants are exact integers, not q * 2^-9
+      s.a_lo *= 1.0f / kNibbleUnscale;
+      s.a_hi *= 1.0f / kNibbleUnscale;
+    }
     float pl = 0.0f, ph = 0.0f;
     f4_t xl_n = xg[0], xh_n = xg[8];
 #pragma unroll
@@ -456,10 +452,23 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_decode(const uint8_t* __restri
         xh_n = xg[c + 9];
       }
       const uint32_t v = c < 4 ? word(qa[st], c) : word(qb[st], c - 4);
-      const uint32_t lo = v & 0x0F0F0F0Fu;
-      const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
-      const f2_t l01 = fp8x2_lo(lo), l23 = fp8x2_hi(lo);
-      const f2_t h01 = fp8x2_lo(hi), h23 = fp8x2_hi(hi);
+      f2_t l01, l23, h01, h23;
+      if constexpr (FMT == 5) {
+        const uint32_t hw = c < 4 ? word(h0[st], c) : word(h1[st], c - 4);
+        const uint32_t lo = q5_bytes(v, hw, 0, 2 * g);
+        const uint32_t hi = q5_bytes(v, hw, 4, 2 * g + 1);
+        l01 = f2_t{ubyte_f32(lo, 0), ubyte_f32(lo, 1)};
+        l23 = f2_t{ubyte_f32(lo, 2), ubyte_f32(lo, 3)};
+        h01 = f2_t{ubyte_f32(hi, 0), ubyte_f32(hi, 1)};
+        h23 = f2_t{ubyte_f32(hi, 2), ubyte_f32(hi, 3)};
+      } else {
+        const uint32_t lo = v & 0x0F0F0F0Fu;
+        const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+        l01 = fp8x2_lo(lo);
+        l23 = fp8x2_hi(lo);
+        h01 = fp8x2_lo(hi);
+        h23 = fp8x2_hi(hi);
+      }
       const float wl0 = __builtin_fmaf(s.a_lo, l01.x, -s.b_lo);
       const float wl1 = __builtin_fmaf(s.a_lo, l01.y, -s.b_lo);
       const float wl2 = __builtin_fmaf(s.a_lo, l23.x, -s.b_lo);
@@ -694,11 +703,11 @@ hipError_t gemv_grid(K kern, std::atomic<int>* resident, int n, int k, int* grid
   return hipSuccess;
 }
 
-template <int MT, int R, bool GLU, int NWV, bool XREG = false, int FMT = 4>
+template <int MT, int R, bool GLU, int NWV, int FMT = 4>
 hipError_t launch(const uint8_t* w, const uint8_t* w2, const float* x, float* y, int m, int n,
                   int k, hipStream_t stream) {
   static std::atomic<int> resident[kMaxDevices];  // workgroups per CU, LDS aside
-  const auto kern = &k_gemv_q4k<MT, R, GLU, NWV, XREG, FMT>;
+  const auto kern = &k_gemv_q4k<MT, R, GLU, NWV, FMT>;
   int grid = 0;
   size_t lds = 0;
   const hipError_t e = gemv_grid<MT, R, GLU, NWV>(kern, resident, n, k, &grid, &lds);
@@ -734,19 +743,19 @@ hipError_t launch_layers(const LayerPtrs& p, int layers, int n, int k, hipStream
 }
 
 // The decode kernel for k <= 16384: one to four K steps.
-template <int NW, bool GLU>
+template <int NW, bool GLU, int FMT>
 hipError_t launch_decode(const uint8_t* w, const uint8_t* w2, const float* x, float* y, int n,
                          int k, hipStream_t stream) {
   constexpr int RW = GLU ? NW / 2 : NW;
   const dim3 grid((n + RW - 1) / RW), block(64 * NW);
   if (k <= 4096)
-    hipLaunchKernelGGL((k_gemv_decode<NW, 1, GLU>), grid, block, 0, stream, w, w2, x, y, n, k);
+    hipLaunchKernelGGL((k_gemv_decode<NW, 1, GLU, FMT>), grid, block, 0, stream, w, w2, x, y, n, k);
   else if (k <= 2 * 4096)
-    hipLaunchKernelGGL((k_gemv_decode<NW, 2, GLU>), grid, block, 0, stream, w, w2, x, y, n, k);
+    hipLaunchKernelGGL((k_gemv_decode<NW, 2, GLU, FMT>), grid, block, 0, stream, w, w2, x, y, n, k);
   else if (k <= 3 * 4096)
-    hipLaunchKernelGGL((k_gemv_decode<NW, 3, GLU>), grid, block, 0, stream, w, w2, x, y, n, k);
+    hipLaunchKernelGGL((k_gemv_decode<NW, 3, GLU, FMT>), grid, block, 0, stream, w, w2, x, y, n, k);
   else
-    hipLaunchKernelGGL((k_gemv_decode<NW, 4, GLU>), grid, block, 0, stream, w, w2, x, y, n, k);
+    hipLaunchKernelGGL((k_gemv_decode<NW, 4, GLU, FMT>), grid, block, 0, stream, w, w2, x, y, n, k);
   return hipGetLastError();
 }
 
@@ -757,22 +766,18 @@ hipError_t launch_gemv_passes(const uint8_t* w, const float* x, float* y, int64_
   const int mm = static_cast<int>(m);
   const int ni = static_cast<int>(n), ki = static_cast<int>(k);
   if (mm == 1) {
-    // One row per wave.  Q4_K matrices of up to kGemvWideRows rows and
-    // k <= 16384 take the decode kernel (one x staging per workgroup of
-    // kDecodeWaves rows); the other formats there take the general kernel at
-    // 16 waves per workgroup.  Taller matrices take 4 waves and, within one K
-    // step (k <= 4096), keep x in registers across their rows; past one K
-    // step, 8 waves.
-    if (n <= kGemvWideRows) {
-      if (FMT == 4 && ki <= 4 * 4096) return launch_decode<kDecodeWaves, false>(w, w, x, y, ni, ki, stream);
-      return launch<1, kGemvRowsPerWave, false, 16, false, FMT>(w, w, x, y, mm, ni, ki, stream);
-    }
-    if (k <= 4096)
-      return launch<1, kGemvRowsPerWave, false, 4, true, FMT>(w, w, x, y, mm, ni, ki, stream);
-    return launch<1, kGemvRowsPerWave, false, 8, false, FMT>(w, w, x, y, mm, ni, ki, stream);
+    // One row per wave.  k <= 16384 takes the decode kernel (one x staging
+    // per workgroup of kDecodeWaves rows; Q4_K 14336 x 4096: 9.6 us against
+    // 11.3-11.9 for the general kernel below).  Past that, matrices of up to
+    // kGemvWideRows rows take the general kernel at 16 waves per workgroup;
+    // taller ones 8 waves.
+    if (ki <= 4 * 4096) return launch_decode<kDecodeWaves, false, FMT>(w, w, x, y, ni, ki, stream);
+    if (n <= kGemvWideRows)
+      return launch<1, kGemvRowsPerWave, false, 16, FMT>(w, w, x, y, mm, ni, ki, stream);
+    return launch<1, kGemvRowsPerWave, false, 8, FMT>(w, w, x, y, mm, ni, ki, stream);
   }
-  if (mm == 2) return launch<2, 2, false, 4, false, FMT>(w, w, x, y, mm, ni, ki, stream);
-  return launch<4, 2, false, 4, false, FMT>(w, w, x, y, mm, ni, ki, stream);
+  if (mm == 2) return launch<2, 2, false, 4, FMT>(w, w, x, y, mm, ni, ki, stream);
+  return launch<4, 2, false, 4, FMT>(w, w, x, y, mm, ni, ki, stream);
 }
 
 }  // namespace
@@ -806,7 +811,7 @@ hipError_t launch_gemv_layers(const uint8_t* const* w, const float* const* x, fl
 hipError_t launch_gateup_swiglu(const uint8_t* w_gate, const uint8_t* w_up, const float* x,
                                 float* h, int64_t d_model, int64_t d_ff, hipStream_t stream) {
   if (d_model <= 4 * 4096)
-    return launch_decode<kDecodeGluWaves, true>(w_gate, w_up, x, h, static_cast<int>(d_ff),
+    return launch_decode<kDecodeGluWaves, true, 4>(w_gate, w_up, x, h, static_cast<int>(d_ff),
                                                 static_cast<int>(d_model), stream);
   return launch<1, kGateUpRowsPerWave, true, 8>(w_gate, w_up, x, h, 1, static_cast<int>(d_ff),
                                                 static_cast<int>(d_model), stream);

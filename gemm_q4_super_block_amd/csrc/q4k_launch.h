@@ -22,9 +22,10 @@ constexpr int kGemmMidTiles = 192;
 // Batches of at most 32 rows with at least this many 64-row weight tiles use
 // the streaming kernel; smaller ones split K over 128-row tiles.
 constexpr int kGemmSmallTiles = 128;
-// Batch-1 matrices of at most this many rows run 16 waves per workgroup
-// (k <= 16384 on Q4_K: the decode kernel, kDecodeWaves waves, one row each).
+// Batch-1 GEMVs outside the decode kernel with at most this many rows run 16
+// waves per workgroup.
 constexpr int64_t kGemvWideRows = 8192;
+// Waves (rows) per workgroup of the batch-1 decode kernel (Q4_K, k <= 16384).
 constexpr int kDecodeWaves = 8;
 // Waves per workgroup of the MLP's gate/up decode kernel (a gate and an up
 // wave per row) for d_model <= 16384.

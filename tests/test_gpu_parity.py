@@ -128,12 +128,11 @@ def test_gemv_decode_4096(q4k, seed):
     assert_within(y, yr[0], a[0], GEMV_TOL, "gemv 4096x4096 seed %d" % seed)
 
 
-# Batch 1 runs three launch shapes: up to 8192 rows and k <= 16384 the decode
-# kernel (8 rows per workgroup; one to four K steps of 4096, ragged last steps
-# of one block (8448) and of 49 blocks (12544), the largest k, rows not a
-# multiple of 8), taller matrices with k <= 4096 (x held in registers; 8200 x
-# 768 leaves 13 of the 16 super-block lanes idle, 9001 x 4096 has a ragged last
-# row set) and taller ones past one K step (8193 x 4352).
+# Batch 1 at k <= 16384 runs the decode kernel (8 rows per workgroup; one to
+# four K steps of 4096, ragged last steps of one block (8448) and of 49 blocks
+# (12544), the largest k, rows not a multiple of 8, tall matrices: 8200 x 768
+# leaves 13 of the 16 super-block lanes idle).  The general kernel's batch-1
+# shapes are covered through Q5_K, which runs them at every size.
 @pytest.mark.parametrize("n,k", [(1, 256), (17, 256), (257, 768), (100, 3840), (33, 4352),
                                  (64, 14336), (1000, 1280), (50, 8448), (5, 9216), (7, 12544),
                                  (4100, 16384), (8192, 2304), (8200, 768), (9001, 4096),
