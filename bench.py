@@ -631,20 +631,32 @@ def _template_args(name, kernel):
 def dispatch_workload(name, threads, lds, hint=""):
     if "k_gemv_layers" in name:
         return "gemv_layers_%dx4096x4096" % LAYERS
-    if "k_gemv_decode" in name:
-        return "gemv_4096x4096"
-    gv = _template_args(name, "k_gemv_q4k")
-    if gv:
-        # <MT, R, GLU, NWV, XREG, FMT>
-        mt, glu, nwv, fmt = gv[0], gv[2], gv[3], gv[5] if len(gv) > 5 else "4"
+    dc = _template_args(name, "k_gemv_decode")
+    if dc:
+        # <NW, NS, GLU, FMT>: 8 rows per workgroup of 64 NW threads, NS K steps of 4096
+        ns, glu, fmt = dc[1], dc[2], dc[3]
+        rows = threads // 64
         if glu == "true":
             return "swiglu_mlp_gateup_14336x4096"
         if fmt == "5":
-            return "q5k_gemv_4096x4096" if mt == "1" else "q5k_other"
-        if mt == "1" and nwv == "16":
-            return "swiglu_mlp_down_4096x14336" if hint == "mlp" else "gemv_4096x4096"
-        if mt == "1":
+            return "q5k_gemv_4096x4096" if rows == 4096 and ns == "1" else "q5k_other"
+        if ns == "4" and rows == 4096:
+            return "swiglu_mlp_down_4096x14336"
+        if ns == "1" and rows == 4096:
+            return "gemv_4096x4096"
+        if ns == "1" and rows == 14336:
             return "sweep_gemv_14336x4096_m1"
+        return "gemv_other"
+    gv = _template_args(name, "k_gemv_q4k")
+    if gv:
+        # <MT, R, GLU, NWV, FMT>
+        mt, glu, fmt = gv[0], gv[2], gv[4] if len(gv) > 4 else "4"
+        if glu == "true":
+            return "swiglu_mlp_gateup_other"
+        if fmt == "5":
+            return "q5k_other"
+        if mt == "1":
+            return "gemv_other"
         return "sweep_gemv_14336x4096_batched"
     dq = _template_args(name, "k_dequant_q4k")
     if dq:

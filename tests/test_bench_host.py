@@ -15,9 +15,14 @@ NS = "void q4k::(anonymous namespace)::"
 
 # (kernel with template arguments, total work-items of the launch, LDS bytes, hint) -> workload
 CASES = [
-    ("k_gemv_q4k<1, 1, false, 16, false, 4>", 4096 // 16 * 1024, 0, "", "gemv_4096x4096"),
-    ("k_gemv_q4k<1, 1, false, 16, false, 4>", 4096 // 16 * 1024, 0, "mlp",
-     "swiglu_mlp_down_4096x14336"),
+    ("k_gemv_decode<8, 1, false, 4>", 4096 // 8 * 512, 17408, "", "gemv_4096x4096"),
+    ("k_gemv_decode<8, 4, false, 4>", 4096 // 8 * 512, 69632, "mlp", "swiglu_mlp_down_4096x14336"),
+    ("k_gemv_decode<8, 1, true, 4>", 14336 // 4 * 512, 17920, "mlp",
+     "swiglu_mlp_gateup_14336x4096"),
+    ("k_gemv_decode<8, 1, false, 4>", 14336 // 8 * 512, 17408, "", "sweep_gemv_14336x4096_m1"),
+    ("k_gemv_decode<8, 1, false, 5>", 4096 // 8 * 512, 17408, "", "q5k_gemv_4096x4096"),
+    ("k_gemv_q4k<2, 2, false, 4, 4>", 196608, 0, "", "sweep_gemv_14336x4096_batched"),
+    ("k_gemv_q4k<1, 1, true, 8, 4>", 4096, 0, "", "swiglu_mlp_gateup_other"),
     ("k_gemm_q4k_kslice<2, 2, 4>", 131072, 163840, "", "gemm_512x4096x4096"),
     ("k_gemm_q4k_kslice<2, 2, 5>", 131072, 157696, "", "q5k_gemm_512x4096x4096"),
     ("k_gemm_q4k_kslice<1, 2, 4>", 224 * 256, 81920, "", "sweep_gemm_14336x4096"),
@@ -30,7 +35,6 @@ CASES = [
     ("k_gemv_planes<3, 8, 2, 1>", 4096 // 16 * 512, 16384, "", "q3k_gemv_4096x4096"),
     ("k_gemv_split<1, 2, 4>", 0, 0, "", "sweep_gemv_14336x4096_split"),
     ("k_gemv_layers", 256 * 1024, 0, "", "gemv_layers_8x4096x4096"),
-    ("k_gemv_decode", 256 * 1024, 16384, "", "gemv_4096x4096"),
     ("k_w8a8_gemm<1, 1, 2, 1>", 48 * 16 * 256, 32768, "", "w8a8_linear_1024x3072x3072"),
     ("k_w8a8_gemm<2, 2, 2, 1>", 24 * 64 * 256, 65536, "", "w8a8_linear_8192x3072x3072"),
     ("k_w8a8_quantize_rows<8>", 1024 * 64, 0, "", "w8a8_quantize_1024x3072"),
