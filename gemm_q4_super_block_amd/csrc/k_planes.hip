@@ -35,14 +35,22 @@
 //     OFF is an exact small integer, so a zero weight adds exactly zero; the
 //     offset is not applied to a separate sum of x, whose rounding would not
 //     cancel against that of sum q x when the weights do.
-//   * GEMV: 8 waves per workgroup, 2 rows per wave (16 rows per workgroup;
-//     measured against 4x4, 8x4, 16x1, 4x2 and 8x1, it was 8-14% faster than
-//     4x4 on 4096- and 14336-row matrices).  Per 4096-wide chunk of x a lane
-//     owns units lane and lane + 64; it issues the chunk's weight loads first,
-//     then x is staged once per workgroup in LDS and each lane copies its
-//     units' x values and 8-sums into registers, reused for both rows.
-//     Batches run in passes of up to 4 x rows: each unit's quants are widened
-//     once per pass and serve every x row.
+//   * (q - OFF) is widened by one sign-extending byte convert: the quant
+//     field with its top bit flipped is its two's-complement value, and
+//     shifted to the top of its byte it reads as (q - OFF) * SCALE (SCALE =
+//     4 for the 6-bit, 32 for the 3-bit fields), with SCALE taken off d sc.
+//     Scaling by a power of two commutes with every rounding, so the sums
+//     and the dequant export are what they would be unscaled.  Against an
+//     unsigned convert and a subtraction per weight this is ~20% fewer VALU
+//     instructions, and the batch-1 GEMVs are bound by them (4096 x 4096:
+//     Q6_K 6.3-6.4 us against 8.0, Q3_K 6.2 against 7.4, with the shape
+//     below).
+//   * GEMV at batch 1: one row per wave, 4 waves per workgroup; x staged by
+//     direct global -> LDS copies issued before the weight copies.  Passes of
+//     2 to 4 x rows: 8 waves, 2 rows per wave, x staged by loads.  Per
+//     4096-wide chunk of x a lane owns units lane and lane + 64; it issues
+//     the chunk's weight loads first.  Each unit's quants are widened once
+//     per pass and serve every x row (and both rows' dots).
 //   * Dequant export: one thread per unit, fp32 = (d sc) * (q - OFF) (the
 //     exact weight rounded once) or its bf16 (nearest even).
 #include <hip/hip_runtime.h>
@@ -56,6 +64,7 @@ namespace {
 
 constexpr int kPlaneChunk = 4096;  // x elements staged per pass (16 KiB)
 constexpr int kPlaneUnitsPerLane = kPlaneChunk / 32 / 64;
+constexpr int kPlaneDecodeWaves = 4;  // waves (rows) per workgroup of the batch-1 GEMV
 
 // Up to four dwords read from the dword boundary at or below p (p = the
 // field's address, s = p mod 4 in {0, 2}); the last one only when s = 2.
@@ -76,12 +85,22 @@ __device__ __forceinline__ void align_field(const uint32_t (&f)[N + 1], uint32_t
   for (int i = 0; i < N; ++i) v[i] = __builtin_amdgcn_alignbyte(f[i + 1], f[i], s);
 }
 
-// The decoded unit: quants q[j][e / 4] (four values per dword, weight e in
-// byte e % 4, offset by OFF) and the four scales d * sc.
+// The decoded unit: quants q[j][e / 4] (four per dword, weight e in byte
+// e % 4) as the signed bytes (q - OFF) * SCALE, and the four scales
+// d * sc / SCALE.  (q - OFF) is the quant field read as a two's-complement
+// number after flipping its top bit; shifted to the top of its byte, one
+// sign-extending byte convert per weight widens it, and SCALE (a power of
+// two) comes off the scale exactly, so d sc (q - OFF) and every sum of its
+// products are what they would be unscaled.
 struct PlaneUnit {
   uint32_t q[4][2];
   float dsc[4];
 };
+
+// Byte i of v as a signed integer, exactly as a float.
+__device__ __forceinline__ float sbyte_f32(uint32_t v, int i) {
+  return static_cast<float>(static_cast<int8_t>((v >> (8 * i)) & 0xFFu));
+}
 
 template <int FMT>
 struct Planes;
@@ -90,6 +109,7 @@ template <>
 struct Planes<6> {
   static constexpr int Bytes = 210;
   static constexpr float Off = 32.0f;
+  static constexpr float Scale = 4.0f;  // 6-bit fields: (q ^ 32) << 2
   struct Raw {
     uint32_t lo[3], hi[3], qh[3], sc[3];
     uint32_t d, s;
@@ -113,17 +133,18 @@ struct Planes<6> {
     PlaneUnit u;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      u.q[0][e] = (L[e] & 0x0F0F0F0Fu) | ((Q[e] << 4) & 0x30303030u);
-      u.q[1][e] = (H[e] & 0x0F0F0F0Fu) | ((Q[e] << 2) & 0x30303030u);
-      u.q[2][e] = ((L[e] >> 4) & 0x0F0F0F0Fu) | (Q[e] & 0x30303030u);
-      u.q[3][e] = ((H[e] >> 4) & 0x0F0F0F0Fu) | ((Q[e] >> 2) & 0x30303030u);
+      u.q[0][e] = (((L[e] & 0x0F0F0F0Fu) | ((Q[e] << 4) & 0x30303030u)) ^ 0x20202020u) << 2;
+      u.q[1][e] = (((H[e] & 0x0F0F0F0Fu) | ((Q[e] << 2) & 0x30303030u)) ^ 0x20202020u) << 2;
+      u.q[2][e] = ((((L[e] >> 4) & 0x0F0F0F0Fu) | (Q[e] & 0x30303030u)) ^ 0x20202020u) << 2;
+      u.q[3][e] = ((((H[e] >> 4) & 0x0F0F0F0Fu) | ((Q[e] >> 2) & 0x30303030u)) ^ 0x20202020u) << 2;
     }
     const float d = half_bits_to_float(r.d);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int b = 2 * j + (c >> 1);  // scale byte of the half: sub-block 8h + 2j + c/2
       const uint32_t word = b < 4 ? S[0] : S[1];
-      u.dsc[j] = d * static_cast<float>(static_cast<int8_t>((word >> (8 * (b & 3))) & 0xFFu));
+      u.dsc[j] = d * static_cast<float>(static_cast<int8_t>((word >> (8 * (b & 3))) & 0xFFu)) *
+                 (1.0f / Scale);
     }
     (void)h;
     return u;
@@ -134,6 +155,7 @@ template <>
 struct Planes<3> {
   static constexpr int Bytes = 110;
   static constexpr float Off = 4.0f;
+  static constexpr float Scale = 32.0f;  // 3-bit fields: (q ^ 4) << 5
   struct Raw {
     uint32_t hm[3], qs[3], sc[4];
     uint32_t d, s;
@@ -157,8 +179,8 @@ struct Planes<3> {
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        u.q[j][e] = ((Qs[e] >> (2 * j)) & 0x03030303u) |
-                    (((Hm[e] >> (4 * h + j)) & 0x01010101u) << 2);
+        u.q[j][e] = ((((Qs[e] >> (2 * j)) & 0x03030303u) |
+                     (((Hm[e] >> (4 * h + j)) & 0x01010101u) << 2)) ^ 0x04040404u) << 5;
     const float d = half_bits_to_float(r.d);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -167,7 +189,7 @@ struct Planes<3> {
       const int b = 2 * j + (c >> 1);
       const uint32_t low4 = ((b < 4 ? S[0] : S[1]) >> (8 * (b & 3) + 4 * h)) & 15u;
       const uint32_t top2 = (S[2] >> (8 * (b & 3) + 2 * (2 * h + (j >> 1)))) & 3u;
-      u.dsc[j] = d * static_cast<float>(static_cast<int>(low4 | (top2 << 4)) - 32);
+      u.dsc[j] = d * static_cast<float>(static_cast<int>(low4 | (top2 << 4)) - 32) * (1.0f / Scale);
     }
     return u;
   }
@@ -233,7 +255,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_planes(const uint8_t* __res
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qf[r][e] = ubyte_f32(wu[r].q[j][e >> 2], e & 3) - P::Off;
+          for (int e = 0; e < 8; ++e) qf[r][e] = sbyte_f32(wu[r].q[j][e >> 2], e & 3);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
           if (i >= mrows) break;
@@ -307,6 +329,17 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_planes_lds(const uint8_t* _
     const int units = kc >> 5;                // 8 per block
     const int cbytes = (kc >> 8) * P::Bytes;
     if (c0 > 0) __syncthreads();  // the previous chunk's reads of xs are done
+    if constexpr (MT == 1) {
+      // x by direct copies, issued first: 16-byte unit p of the chunk to LDS
+      // unit p (units past the chunk repeat its last; never read).
+#pragma unroll
+      for (int q = 0; q < kPlaneChunk / 4 / (64 * WAVES); ++q) {
+        const int p = 64 * (wave + WAVES * q) + lane;
+        copy16_to_lds(x + c0 + 4 * min(p, (kc >> 2) - 1),
+                      __builtin_amdgcn_readfirstlane(lds_address(&xs[0][0]) +
+                                                     1024u * static_cast<uint32_t>(wave + WAVES * q)));
+      }
+    }
     // Row r's chunk: bytes [g0, g0 + cbytes) copied from a = g0 rounded down
     // to 16; unit u of the copy lands at LDS offset 16 u (units past the
     // range repeat its last unit).
@@ -323,12 +356,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_planes_lds(const uint8_t* _
         copy16_to_lds(a + 16 * min(64 * q + lane, nu - 1),
                       __builtin_amdgcn_readfirstlane(dst + 1024 * q));
     }
+    if constexpr (MT > 1) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      if (i >= mrows) break;
-      for (int e = 4 * static_cast<int>(threadIdx.x); e < kc; e += 4 * 64 * WAVES)
-        *reinterpret_cast<float4*>(&xs[i][e]) =
-            *reinterpret_cast<const float4*>(x + static_cast<size_t>(i) * k + c0 + e);
+      for (int i = 0; i < MT; ++i) {
+        if (i >= mrows) break;
+        for (int e = 4 * static_cast<int>(threadIdx.x); e < kc; e += 4 * 64 * WAVES)
+          *reinterpret_cast<float4*>(&xs[i][e]) =
+              *reinterpret_cast<const float4*>(x + static_cast<size_t>(i) * k + c0 + e);
+      }
     }
     wait_copies_barrier<0>();
 #pragma unroll
@@ -346,7 +381,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_planes_lds(const uint8_t* _
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qf[r][e] = ubyte_f32(wu[r].q[j][e >> 2], e & 3) - P::Off;
+          for (int e = 0; e < 8; ++e) qf[r][e] = sbyte_f32(wu[r].q[j][e >> 2], e & 3);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
           if (i >= mrows) break;
@@ -389,7 +424,7 @@ __global__ __launch_bounds__(256) void k_dequant_planes(const uint8_t* __restric
   for (int j = 0; j < 4; ++j) {
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = u.dsc[j] * (ubyte_f32(u.q[j][e >> 2], e & 3) - P::Off);
+    for (int e = 0; e < 8; ++e) v[e] = u.dsc[j] * sbyte_f32(u.q[j][e >> 2], e & 3);
     if constexpr (BF16) {
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + base + 32 * j) =
           uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
@@ -666,39 +701,41 @@ hipError_t launch_gemm_planes(const uint8_t* w, const uint16_t* x, float* y, int
   return launch_gemm_planes_tiles<FMT, 4, 1, 1, 4>(w, x, y, mi, ni, ki, stream);
 }
 
-template <int FMT, int WAVES = 8, int RPW = 2>
+// One pass of up to MT x rows: the LDS-staged kernel when the copies'
+// 16-byte rounding stays inside the matrix, else the direct one.
+template <int FMT, int WAVES, int RPW, int MT>
+hipError_t launch_gemv_planes_pass(const uint8_t* w, const float* x, float* y, int n, int k,
+                                   int mm, bool staged, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n + WAVES * RPW - 1) / (WAVES * RPW)));
+  if (staged)
+    hipLaunchKernelGGL((k_gemv_planes_lds<FMT, WAVES, RPW, MT>), grid, dim3(64 * WAVES), 0, stream,
+                       w, x, y, n, k, mm);
+  else
+    hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, MT>), grid, dim3(64 * WAVES), 0, stream, w,
+                       x, y, n, k, mm);
+  return hipGetLastError();
+}
+
+// Batch 1: one row per wave, kPlaneDecodeWaves waves per workgroup.  Passes of
+// 2 to 4 x rows: two rows per wave, 8 waves (each unit widened once serves
+// both rows' dots for every x row).
+template <int FMT>
 hipError_t launch_gemv_planes(const uint8_t* w, const float* x, float* y, int64_t m, int64_t n,
                               int64_t k, hipStream_t stream) {
   const int ni = static_cast<int>(n), ki = static_cast<int>(k);
-  const int rows_per_wg = WAVES * RPW;
-  const dim3 grid(static_cast<unsigned>((ni + rows_per_wg - 1) / rows_per_wg));
-  // Rows through LDS when the copies' 16-byte rounding stays inside the matrix.
   const bool staged = (n * (k / 256)) % 8 == 0;
   for (int64_t i0 = 0; i0 < m; i0 += 4) {
     const int mm = static_cast<int>(m - i0 < 4 ? m - i0 : 4);
     const float* xs = x + i0 * k;
     float* ys = y + i0 * n;
-    if (staged) {
-      if (mm == 1)
-        hipLaunchKernelGGL((k_gemv_planes_lds<FMT, WAVES, RPW, 1>), grid, dim3(64 * WAVES), 0,
-                           stream, w, xs, ys, ni, ki, mm);
-      else if (mm == 2)
-        hipLaunchKernelGGL((k_gemv_planes_lds<FMT, WAVES, RPW, 2>), grid, dim3(64 * WAVES), 0,
-                           stream, w, xs, ys, ni, ki, mm);
-      else
-        hipLaunchKernelGGL((k_gemv_planes_lds<FMT, WAVES, RPW, 4>), grid, dim3(64 * WAVES), 0,
-                           stream, w, xs, ys, ni, ki, mm);
-    } else if (mm == 1) {
-      hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, 1>), grid, dim3(64 * WAVES), 0, stream,
-                         w, xs, ys, ni, ki, mm);
-    } else if (mm == 2) {
-      hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, 2>), grid, dim3(64 * WAVES), 0, stream,
-                         w, xs, ys, ni, ki, mm);
-    } else {
-      hipLaunchKernelGGL((k_gemv_planes<FMT, WAVES, RPW, 4>), grid, dim3(64 * WAVES), 0, stream,
-                         w, xs, ys, ni, ki, mm);
-    }
-    const hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (mm == 1)
+      e = launch_gemv_planes_pass<FMT, kPlaneDecodeWaves, 1, 1>(w, xs, ys, ni, ki, mm, staged,
+                                                                stream);
+    else if (mm == 2)
+      e = launch_gemv_planes_pass<FMT, 8, 2, 2>(w, xs, ys, ni, ki, mm, staged, stream);
+    else
+      e = launch_gemv_planes_pass<FMT, 8, 2, 4>(w, xs, ys, ni, ki, mm, staged, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
