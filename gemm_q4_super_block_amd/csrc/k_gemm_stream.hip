@@ -78,28 +78,6 @@ struct Stream {
   static_assert((XSlots - 2) * XC + WC <= 63, "vmcnt range");
 };
 
-// Direct global -> LDS copy of 16 bytes per lane from sbase + voff (sbase
-// uniform, in SGPRs; voff a per-lane 32-bit byte offset) to lds_uniform + 16
-// lane.  M0 is saved and restored around the copy.
-__device__ __forceinline__ void copy16_to_lds_so(uint32_t voff, const void* sbase,
-                                                 uint32_t lds_uniform) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds_uniform)
-      : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // Sub-block scales of one super-block header: a = d sc 2^9 (Q5_K: d sc),
 // b = dmin m for sub-blocks 0..7.
 struct SbScales {

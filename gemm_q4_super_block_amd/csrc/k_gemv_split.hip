@@ -31,6 +31,7 @@
 //     through LDS at the end.
 #include <hip/hip_runtime.h>
 
+#include "lds_copy.h"
 #include "q4k_device.h"
 #include "q4k_launch.h"
 
@@ -83,14 +84,30 @@ __device__ __forceinline__ void weights8(uint2 q, uint2 h, int bit, float a, flo
   }
 }
 
-template <int MT, int NT, int WV, int FMT>
+// STAGED: a wave's super-blocks of the 16 NT weight rows reach LDS by direct
+// copies (each row's record contiguous, in a wave-private two-slot ring one
+// super-block ahead) and the lanes read their header and quant bytes from
+// there.  Loaded straight from memory instead, each load instruction touches
+// 16 rows' 16 or 32 bytes, one record (row_bytes) apart.
+template <int MT, int NT, int WV, int FMT, bool STAGED>
 __global__ __launch_bounds__(64 * WV) void k_gemv_split(const uint8_t* __restrict__ w,
                                                         const float* __restrict__ x,
                                                         float* __restrict__ y, int m, int n,
                                                         int k) {
-  __shared__ __attribute__((aligned(16))) float red[WV][MT][NT][4][64];
+  constexpr int BB = block_bytes<FMT>();
+  constexpr int WUnits = 16 * NT * BB / 16;  // 16-byte units of one super-block of the rows
+  constexpr int WC = (WUnits + 63) / 64;     // copies of them per wave
+  constexpr int WSlot = WUnits * 16;
+  constexpr int RedBytes = WV * MT * NT * 4 * 64 * 4;
+  constexpr int RingBytes = STAGED ? WV * 2 * WSlot : 0;
+  constexpr int SmemBytes = RingBytes > RedBytes ? RingBytes : RedBytes;
+  static_assert(SmemBytes <= 160 * 1024, "LDS budget of one workgroup");
+  static_assert(WC + 16 * MT <= 63, "vmcnt range");
+  // The weight rings, and after the K loop the partial tiles (over them).
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SmemBytes];
+  auto red = reinterpret_cast<float (*)[MT][NT][4][64]>(smem);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, kg = lane >> 4;
   const int nb = k >> 8;
   const int n0 = blockIdx.x * 16 * NT;
@@ -136,11 +153,56 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_split(const uint8_t* __restric
     }
   };
 
+  // Staged: copy i of a super-block fills units min(64 i, WUnits - 64) + lane
+  // of the slot, unit U = part U % (BB / 16) of row U / (BB / 16) (rows past n
+  // read row n - 1; the last copy repeats some units of the one before, with
+  // the same data and place).
+  const uint32_t row_bytes = static_cast<uint32_t>(nb) * BB;
+  const uint8_t* const wt = w + static_cast<size_t>(n0) * row_bytes;
+  uint32_t woff[STAGED ? WC : 1];
+  if constexpr (STAGED) {
+#pragma unroll
+    for (int i = 0; i < WC; ++i) {
+      const int U = min(64 * i, WUnits - 64) + lane;
+      const int r = U / (BB / 16);
+      woff[i] = static_cast<uint32_t>(min(r, n - 1 - n0)) * row_bytes + (U - r * (BB / 16)) * 16;
+    }
+  }
+  uint8_t* const ring = smem + (STAGED ? wave * 2 * WSlot : 0);
+  auto copy_w = [&](int b, int slot) {
+    const uint8_t* base = wt + static_cast<size_t>(min(b, nb - 1)) * BB;
+    const uint32_t dst = lds_address(ring) + slot * WSlot;
+#pragma unroll
+    for (int i = 0; i < WC; ++i) copy16_to_lds_so(woff[i], base, dst + min(64 * i, WUnits - 64) * 16);
+  };
+  auto read_w = [&](int slot, WBlock& wb) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint8_t* p = ring + slot * WSlot + (16 * t + nl) * BB;
+      wb.hd[t] = *reinterpret_cast<const uint4*>(p);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        wb.q[t][g] = *reinterpret_cast<const uint2*>(p + kQOff + 32 * g + 8 * kg);
+      if constexpr (FMT == 5) wb.qh[t] = *reinterpret_cast<const uint2*>(p + kQ5HighOffset + 8 * kg);
+    }
+  };
+
   WBlock cur, nxt;
   int b = wave;
-  if (b < nb) load_w(b, cur);
-  for (; b < nb; b += WV) {
-    if (b + WV < nb) load_w(b + WV, nxt);
+  int slot = 0;
+  if constexpr (STAGED) {
+    if (b < nb) copy_w(b, 0);
+  } else {
+    if (b < nb) load_w(b, cur);
+  }
+  for (; b < nb; b += WV, slot ^= 1) {
+    // Staged: the next super-block's copies (past the end the last one again,
+    // so every pass issues the same number) ahead of this one's x loads.
+    if constexpr (STAGED) {
+      copy_w(b + WV, slot ^ 1);
+    } else {
+      if (b + WV < nb) load_w(b + WV, nxt);
+    }
     // x of the whole super-block, this lane's 8 k of each of its 8 sub-blocks:
     // issued together so that one L2 round trip serves the four quant groups.
     float4 xr[MT][8][2];
@@ -152,6 +214,11 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_split(const uint8_t* __restric
         xr[t][sb][0] = *reinterpret_cast<const float4*>(p);
         xr[t][sb][1] = *reinterpret_cast<const float4*>(p + 4);
       }
+    if constexpr (STAGED) {
+      // Issued after this super-block's copies: the next copies and the x loads.
+      wait_copies<WC + 16 * MT>();
+      read_w(slot, cur);
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // x of sub-blocks 2g (s = 0) and 2g + 1 (s = 1), split into bf16 hi + lo
@@ -196,8 +263,11 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_split(const uint8_t* __restric
         }
       }
     }
-    cur = nxt;
+    if constexpr (!STAGED) cur = nxt;
   }
+  (void)slot;
+  if constexpr (STAGED) wait_copies<0>();
+  __syncthreads();  // every wave is done with its ring before the tiles go over it
 
   // Sum the waves' partial tiles: wave v finishes the (t, nt) tiles with
   // (t * NT + nt) % WV == v and stores them.  Tile register r holds batch row
@@ -238,11 +308,16 @@ namespace {
 // rows); smaller ones 16-row tiles on 8 waves (256 at 4096 rows), so that
 // the grid still covers the CUs.
 constexpr int kSplitTallRows = 8192;
+constexpr bool kSplitStaged = true;
 
 template <int MT, int NT, int WV, int FMT>
 void launch_split_tiles(const uint8_t* w, const float* x, float* y, int m, int n, int k,
                         hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemv_split<MT, NT, WV, FMT>), dim3((n + 16 * NT - 1) / (16 * NT)),
+  // Q4_K's 64-row tiles stage their weights through LDS (Q5_K's 176-byte
+  // records would need 176 KiB of rings; the 16-row tiles of two batch tiles
+  // run out of registers).
+  constexpr bool kStaged = FMT == 4 && NT == 4 && kSplitStaged;
+  hipLaunchKernelGGL((k_gemv_split<MT, NT, WV, FMT, kStaged>), dim3((n + 16 * NT - 1) / (16 * NT)),
                      dim3(64 * WV), 0, stream, w, x, y, m, n, k);
 }
 

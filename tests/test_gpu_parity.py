@@ -436,11 +436,14 @@ def test_gemm_long_k(q4k):
 # x each split into bf16 hi + lo (three MFMAs per tile).  Edges: one
 # super-block (only the first of the four K-split waves has work), a block
 # count not divisible by four, single and ragged 16-row weight tiles, batch
-# sizes around the 16-row MFMA tile, matrices past 8192 rows (two weight
-# tiles per workgroup, ragged), and x spanning six decades.
+# sizes around the 16-row MFMA tile, matrices past 8192 rows (64-row
+# weight tiles staged through LDS: ragged rows, fewer super-blocks than the
+# eight K-split waves, a block count not divisible by eight, one and two
+# batch tiles), and x spanning six decades.
 @pytest.mark.parametrize("m,n,k", [(5, 1, 256), (6, 1, 256), (15, 17, 256), (16, 33, 1280),
                                    (17, 16, 4352), (32, 15, 768), (7, 4096, 4096),
-                                   (24, 500, 2048), (5, 8200, 512), (20, 8192, 256)])
+                                   (24, 500, 2048), (5, 8200, 512), (20, 8192, 256),
+                                   (8, 8250, 1280), (12, 16384, 2048), (32, 9000, 4352)])
 def test_gemv_split_edges(q4k, m, n, k):
     w = synth.q4k_weights(n, k, seed=m + n)
     x = synth.normal_f32((m, k), seed=m + n)

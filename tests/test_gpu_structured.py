@@ -182,13 +182,14 @@ def tile(kinds, n, k, seed):
 
 # ------------------------------------------------------------------ Q4_K GEMV
 
-# Batch 1 in its three launch shapes (<= 8192 rows; taller with x in
-# registers; taller past one K step), the FMA passes (2..4) and the split-bf16
-# MFMA kernel (5..32 rows, one and two weight tiles per workgroup).
+# Batch 1 (the decode kernel at one and two K steps, any row count), the FMA
+# passes (2..4) and the split-bf16 MFMA kernel (5..32 rows, one and two batch
+# tiles; 64-row weight tiles staged through LDS from 8192 rows).
 @pytest.mark.parametrize("m,n,k", [(1, 200, 1024), (1, 8200, 512), (1, 8195, 4352),
                                    (2, 150, 768), (3, 97, 1024), (4, 64, 2304),
                                    (5, 130, 1024), (8, 8200, 256), (16, 77, 768),
-                                   (17, 64, 512), (32, 300, 1280)])
+                                   (17, 64, 512), (32, 300, 1280), (12, 8256, 1280),
+                                   (30, 8200, 768)])
 def test_q4k_gemv_structured(q4k, m, n, k):
     w = tile(q4k_kinds(), n, k, seed=m + n)
     x = synth.normal_f32((m, k), seed=m + k)
