@@ -686,9 +686,11 @@ def dispatch_workload(name, threads, lds, hint=""):
         return "read_probe"
     if "k_gemv_split" in name:
         return "sweep_gemv_14336x4096_split"
-    gp = _template_args(name, "k_gemv_planes")
+    gp = _template_args(name, "k_gemv_planes") or _template_args(name, "k_gemv_planes_lds")
     if gp:
-        return ("q%sk_gemv_4096x4096" % gp[0]) if threads == 4096 // 16 * 512 else "planes_other"
+        # <FMT, WAVES, RPW, MT>: one wave per RPW weight rows
+        rows = threads // 64 * int(gp[2])
+        return ("q%sk_gemv_4096x4096" % gp[0]) if rows == 4096 and gp[3] == "1" else "planes_other"
     if "k_dequant_planes" in name:
         return "planes_dequant"
     pg = _template_args(name, "k_gemm_planes")

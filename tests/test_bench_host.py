@@ -32,7 +32,9 @@ CASES = [
     ("k_gemm_planes<6, 4, 1, 1, 4>", 128 * 2 * 256, 36864, "", "q6k_gemm_512x4096x4096"),
     ("k_gemm_planes<3, 4, 1, 1, 4>", 128 * 2 * 256, 36864, "", "q3k_gemm_512x4096x4096"),
     ("k_gemv_planes<6, 8, 2, 1>", 4096 // 16 * 512, 16384, "", "q6k_gemv_4096x4096"),
-    ("k_gemv_planes<3, 8, 2, 1>", 4096 // 16 * 512, 16384, "", "q3k_gemv_4096x4096"),
+    ("k_gemv_planes_lds<6, 4, 1, 1>", 4096 // 4 * 256, 32768, "", "q6k_gemv_4096x4096"),
+    ("k_gemv_planes_lds<3, 4, 1, 1>", 4096 // 4 * 256, 24576, "", "q3k_gemv_4096x4096"),
+    ("k_gemv_planes_lds<3, 8, 2, 4>", 4096 // 16 * 512, 90112, "", "planes_other"),
     ("k_gemv_split<1, 2, 4>", 0, 0, "", "sweep_gemv_14336x4096_split"),
     ("k_gemv_layers", 256 * 1024, 0, "", "gemv_layers_8x4096x4096"),
     ("k_w8a8_gemm<1, 1, 2, 1>", 48 * 16 * 256, 32768, "", "w8a8_linear_1024x3072x3072"),
