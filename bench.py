@@ -550,7 +550,7 @@ def main():
         out["roofline_w8a8"] = {"bound": "mfma", "achieved": w8["tops"], "peak": INT8_PEAK_TOPS,
                                 "unit": "TOP/s", "frac": w8["mfma_frac"],
                                 "traffic": traffic("w8a8_linear_%dx%dx%d" % (W8A8_M[0], W8A8_N, W8A8_K)),
-                                "kernel": "k_w8a8_gemm<1, 1, 2, 1>",
+                                "kernel": "k_w8a8_gemm<1, 3, 3, 1>",
                                 "op_per_launch": 2 * W8A8_M[0] * W8A8_N * W8A8_K, **timing(w8)}
     print(json.dumps(out))
 
@@ -703,10 +703,10 @@ def dispatch_workload(name, threads, lds, hint=""):
     wg = _template_args(name, "k_w8a8_gemm")
     if wg:
         # <TI, TJ, S, OUT>: (64 TI) x (64 TJ) tiles of the 3072-wide output, 256 threads each
-        # (64 x 64 at M = 1024, 128 x 128 at M = 8192)
-        if wg == ("1", "1", "2", "1") and threads == (3072 // 64) * (1024 // 64) * 256:
+        # (64 x 192 at M = 1024, 128 x 192 at M = 8192)
+        if wg == ("1", "3", "3", "1") and threads == (3072 // 192) * (1024 // 64) * 256:
             return "w8a8_linear_1024x3072x3072"
-        if wg == ("2", "2", "2", "1") and threads == (3072 // 128) * (8192 // 128) * 256:
+        if wg == ("2", "3", "2", "1") and threads == (3072 // 192) * (8192 // 128) * 256:
             return "w8a8_linear_8192x3072x3072"
         return "w8a8_other"
     if "k_w8a8_quantize_rows" in name:

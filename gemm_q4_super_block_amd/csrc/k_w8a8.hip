@@ -18,8 +18,9 @@
 //     X and W rows (128 bytes each) from global memory straight into LDS
 //     (global_load_lds_dwordx4) through a ring of S slots, S - 1 steps ahead.
 //     LDS rows keep the XOR-swizzled chunk order of lds_copy.h.  The shipped
-//     tiles, 64 x 64 (small grids) and 128 x 128, with S = 2 hold 32 and
-//     64 KiB; two or more workgroups share a CU.
+//     tiles: 64 x 64 (S = 2, 32 KiB) and 64 x 192 (S = 3, 96 KiB) for small
+//     grids, 128 x 192 and 128 x 128 (S = 2, 80 and 64 KiB, two workgroups
+//     per CU) for large ones.
 //   * MFMA slice u (0..3) of a step, lane half h, covers k = 32 u + 16 h +
 //     (0..15) for both operands (the MFMA sums over k, so any common
 //     assignment is the same contraction): one conflict-free ds_read_b128 per
@@ -92,8 +93,7 @@ __device__ __forceinline__ uint32_t swap_lane_pairs(uint32_t v) {
 // (32 TI) x (32 TJ) outputs as TI x TJ accumulators of v_mfma_i32_32x32x32_i8.
 // K advances 128 per step; the tile's X and W rows of a step are copied
 // straight into LDS slot s % S, S - 1 steps ahead, and a step's fragments are
-// read slice by slice while the MFMAs of the previous slice run.  With S = 2
-// and 128 x 128 tiles a workgroup holds 64 KiB of LDS, so two run on each CU.
+// read slice by slice while the MFMAs of the previous slice run.
 template <int TI, int TJ, int S, int OUT>
 __global__ __launch_bounds__(256, 2) void k_w8a8_gemm(
     const int8_t* __restrict__ x, const int8_t* __restrict__ w, const float* __restrict__ xs,
@@ -402,19 +402,33 @@ hipError_t launch_tiles(const int8_t* x, const int8_t* w, const float* xs, const
 
 namespace {
 
-// Tile shape per grid (3072 x 3072 weights): where 128 x 128 tiles would not
-// give every CU one (M = 512 / 1024: 96 / 192 tiles), 64 x 64 tiles (warm L2:
-// 13.0 / 18.2 us against 20.6 / 22.4; cold inputs at M = 1024: 23.7 against
-// 28.7); otherwise 128 x 128, whose operands are re-read least (cold inputs
-// at M = 8192: 106.5 us against 131 for 64 x 128, which was 1-4% faster on
-// warm ones).
+// Tile shape per grid.  The loop is bound by the L2 read requests a CU can
+// keep in flight (about 70 128-byte lines; counters: the TCP waits on L2 data
+// half its cycles while the MFMA pipe is 30% busy), so the wider the tile,
+// the fewer requests per MAC.  N-wide 192 tiles are used where they pad N no
+// more than 128-wide ones do.  3072 x 3072 weights, warm timings:
+//   * grids up to 256 tiles of 128 x 128 (M = 512 / 1024): 64 x 192 tiles
+//     with a three-slot ring (96 KiB, one workgroup per CU) where they still
+//     give every CU one (M = 1024: 23.5 us against 25.9 for 64 x 64 and 27
+//     for 64 x 128), else 64 x 64 (two slots, several per CU);
+//   * larger grids: 128 x 192 with two slots (80 KiB, two workgroups per CU;
+//     M = 8192: 99 us against 111 for 128 x 128, which remains for other N).
+//     Tiles that leave one workgroup per CU lose even with fewer requests
+//     (256 x 192: 110 us; 256 x 128 three slots: 122; 128 x 128 three or four
+//     slots: 134), as do 64-byte K steps, which halve the request size.
 template <int OUT>
 hipError_t launch_w8a8(const int8_t* x, const int8_t* w, const float* xs, const float* ws,
                        const float* bias, void* out, int64_t m, int64_t n, int64_t k,
                        hipStream_t stream) {
   const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
   const int64_t tiles128 = ((m + 127) / 128) * ((n + 127) / 128);
-  if (tiles128 <= 256) return launch_tiles<1, 1, 2, OUT>(x, w, xs, ws, bias, out, mi, ni, ki, stream);
+  const bool n192 = (n + 191) / 192 * 192 <= (n + 127) / 128 * 128;
+  if (tiles128 <= 256) {
+    if (n192 && ((m + 63) / 64) * ((n + 191) / 192) >= 256)
+      return launch_tiles<1, 3, 3, OUT>(x, w, xs, ws, bias, out, mi, ni, ki, stream);
+    return launch_tiles<1, 1, 2, OUT>(x, w, xs, ws, bias, out, mi, ni, ki, stream);
+  }
+  if (n192) return launch_tiles<2, 3, 2, OUT>(x, w, xs, ws, bias, out, mi, ni, ki, stream);
   return launch_tiles<2, 2, 2, OUT>(x, w, xs, ws, bias, out, mi, ni, ki, stream);
 }
 

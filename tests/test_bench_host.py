@@ -37,8 +37,9 @@ CASES = [
     ("k_gemv_planes_lds<3, 8, 2, 4>", 4096 // 16 * 512, 90112, "", "planes_other"),
     ("k_gemv_split<1, 2, 4>", 0, 0, "", "sweep_gemv_14336x4096_split"),
     ("k_gemv_layers", 256 * 1024, 0, "", "gemv_layers_8x4096x4096"),
-    ("k_w8a8_gemm<1, 1, 2, 1>", 48 * 16 * 256, 32768, "", "w8a8_linear_1024x3072x3072"),
-    ("k_w8a8_gemm<2, 2, 2, 1>", 24 * 64 * 256, 65536, "", "w8a8_linear_8192x3072x3072"),
+    ("k_w8a8_gemm<1, 3, 3, 1>", 16 * 16 * 256, 98304, "", "w8a8_linear_1024x3072x3072"),
+    ("k_w8a8_gemm<2, 3, 2, 1>", 16 * 64 * 256, 81920, "", "w8a8_linear_8192x3072x3072"),
+    ("k_w8a8_gemm<2, 2, 2, 1>", 24 * 64 * 256, 65536, "", "w8a8_other"),
     ("k_w8a8_quantize_rows<8>", 1024 * 64, 0, "", "w8a8_quantize_1024x3072"),
     ("k_zero_planes", 524544, 0, "", "split_k_zero_fill"),
     ("k_zero_f32", 524544, 0, "", "split_k_zero_fill"),

@@ -55,10 +55,12 @@ def run_linear(q4k, case, bias=True):
     (256, 384, 1024, 1),    # several tiles, eight steps
     (130, 200, 384, 2),     # ragged M and N tiles
     (1, 1, 256, 3),         # a single output
-    (64, 1024, 512, 4),     # one row of 64 x 64 tiles (the tile of every grid up to 256 tiles of 128 x 128)
+    (64, 1024, 512, 4),     # one row of 64 x 64 tiles (small grids)
     (257, 129, 640, 5),     # ragged, odd step count
     (96, 3072, 3072, 6),    # the pages' K and N, small M
     (2100, 2000, 256, 7),   # 128 x 128 tiles (more than 256 of them), ragged
+    (1030, 3072, 256, 8),   # 64 x 192 tiles, three-slot ring (a small grid that fills the CUs), ragged M
+    (2200, 1900, 256, 9),   # 128 x 192 tiles (a large grid), ragged M and N
 ])
 def test_linear_acc_and_fused_epilogue_bit_exact(q4k, m, n, k, seed):
     case = synth.w8a8_case(m, n, k, seed)
