@@ -693,6 +693,10 @@ def dispatch_workload(name, threads, lds, hint=""):
         return ("q%sk_gemv_4096x4096" % gp[0]) if rows == 4096 and gp[3] == "1" else "planes_other"
     if "k_dequant_planes" in name:
         return "planes_dequant"
+    pl = _template_args(name, "k_gemm_planes_lds")
+    if pl:
+        # <FMT>: 128 x 128 tiles of 8 waves, split K in two at M = 512 (32 x 4 x 2 workgroups)
+        return ("q%sk_gemm_512x4096x4096" % pl[0]) if threads == 32 * 4 * 2 * 512 else "planes_other"
     pg = _template_args(name, "k_gemm_planes")
     if pg:
         # <FMT, WAVES_M, WAVES_N, TI, TJ>: 128 x 128 tiles, split K in two at M = 512

@@ -453,60 +453,66 @@ constexpr int kPBN = 128;      // weight rows per tile
 constexpr int kPBK = 64;       // weights per K step
 constexpr int kPLds = 72;      // bf16 per LDS row: 64 + 8 pad
 
-template <int FMT>
+// A tile-fill thread's share of a 64-k step: the 32 weights l = 0..31 of
+// group j of half h (ND = 8 dwords per field), or the 16 weights l = 16 part
+// + (0..15) (ND = 4).
+template <int FMT, int ND = 8>
 struct PlaneFill {
-  uint32_t lo[9], hi[9];  // low-bit field (ql / qs), high-bit field (qh / hmask)
-  uint32_t sc[4];         // the scale bytes of the half (Q6_K: 8) or all 12 (Q3_K)
+  uint32_t lo[ND + 1], hi[ND + 1];  // low-bit field (ql / qs), high-bit field (qh / hmask)
+  uint32_t sc[4];                   // the scale bytes of the half (Q6_K: 8) or all 12 (Q3_K)
   uint32_t d, s;
 };
 
-template <int FMT>
-__device__ __forceinline__ void plane_fill_load(const uint8_t* blk, int sp, int f,
-                                                PlaneFill<FMT>& r) {
+template <int FMT, int ND = 8>
+__device__ __forceinline__ void plane_fill_load(const uint8_t* blk, int sp, int f, int part,
+                                                PlaneFill<FMT, ND>& r) {
   const int h = sp >> 1, j = 2 * (sp & 1) + f;
+  const int lb = ND == 8 ? 0 : 16 * part;
   r.s = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(blk) & 3u);
   if constexpr (FMT == 6) {
-    load_field<8>(blk + 64 * h + 32 * (j & 1), r.s, r.lo);
-    load_field<8>(blk + 128 + 32 * h, r.s, r.hi);
+    load_field<ND>(blk + 64 * h + 32 * (j & 1) + lb, r.s, r.lo);
+    load_field<ND>(blk + 128 + 32 * h + lb, r.s, r.hi);
     uint32_t t[3];
     load_field<2>(blk + 192 + 8 * h, r.s, t);
     r.sc[0] = t[0]; r.sc[1] = t[1]; r.sc[2] = t[2]; r.sc[3] = 0u;
     r.d = *reinterpret_cast<const uint16_t*>(blk + 208);
   } else {
-    load_field<8>(blk + 32 + 32 * h, r.s, r.lo);
-    load_field<8>(blk, r.s, r.hi);
+    load_field<ND>(blk + 32 + 32 * h + lb, r.s, r.lo);
+    load_field<ND>(blk + lb, r.s, r.hi);
     load_field<3>(blk + 96, r.s, r.sc);
     r.d = *reinterpret_cast<const uint16_t*>(blk + 108);
   }
 }
 
-// 32 bf16 weights (l = 0..31 of group j of half h) into out[16] (pairs).
-template <int FMT>
-__device__ __forceinline__ void plane_fill_decode(const PlaneFill<FMT>& r, int sp, int f,
-                                                  uint32_t (&out)[16]) {
+// The thread's bf16 weights as pairs: 32 (l = 0..31 of group j of half h)
+// into out[16], or 16 (l = 16 part + (0..15)) into out[8].
+template <int FMT, int ND = 8>
+__device__ __forceinline__ void plane_fill_decode(const PlaneFill<FMT, ND>& r, int sp, int f,
+                                                  int part, uint32_t (&out)[2 * ND]) {
   const int h = sp >> 1, j = 2 * (sp & 1) + f;
-  uint32_t L[8], H[8];
-  align_field<8>(r.lo, r.s, L);
-  align_field<8>(r.hi, r.s, H);
+  constexpr int NCB = ND / 4;  // sub-blocks of 16 weights the thread covers
+  uint32_t L[ND], H[ND];
+  align_field<ND>(r.lo, r.s, L);
+  align_field<ND>(r.hi, r.s, H);
   const float d = half_bits_to_float(r.d);
-  float dsc[2];
+  float dsc[NCB];
   if constexpr (FMT == 6) {
     uint32_t S[2];
     align_field<2>(*reinterpret_cast<const uint32_t(*)[3]>(r.sc), r.s, S);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int b = 2 * j + cb;  // sub-block 8h + 2j + cb
-      dsc[cb] = d * static_cast<float>(static_cast<int8_t>(((b < 4 ? S[0] : S[1]) >> (8 * (b & 3))) & 0xFFu));
+    for (int c = 0; c < NCB; ++c) {
+      const int b = 2 * j + (ND == 8 ? c : part);  // sub-block 8h + 2j + l / 16
+      dsc[c] = d * static_cast<float>(static_cast<int8_t>(((b < 4 ? S[0] : S[1]) >> (8 * (b & 3))) & 0xFFu));
     }
   } else {
     uint32_t S[3];
     align_field<3>(r.sc, r.s, S);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int b = 2 * j + cb;
+    for (int c = 0; c < NCB; ++c) {
+      const int b = 2 * j + (ND == 8 ? c : part);
       const uint32_t low4 = ((b < 4 ? S[0] : S[1]) >> (8 * (b & 3) + 4 * h)) & 15u;
       const uint32_t top2 = (S[2] >> (8 * (b & 3) + 2 * (2 * h + (j >> 1)))) & 3u;
-      dsc[cb] = d * static_cast<float>(static_cast<int>(low4 | (top2 << 4)) - 32);
+      dsc[c] = d * static_cast<float>(static_cast<int>(low4 | (top2 << 4)) - 32);
     }
   }
   // Per dword: the low bits shifted to bits 0.. of each byte, the high bits
@@ -523,11 +529,13 @@ __device__ __forceinline__ void plane_fill_decode(const PlaneFill<FMT>& r, int s
   // (d sc) OFF is exact and the FMA rounds the exact weight once, as the
   // subtract-then-multiply form does.
   const float off = Planes<FMT>::Off;
-  const float nb0 = -(dsc[0] * off), nb1 = -(dsc[1] * off);
+  float nbs[NCB];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {  // dword e: weights l = 4e .. 4e + 3
+  for (int c = 0; c < NCB; ++c) nbs[c] = -(dsc[c] * off);
+#pragma unroll
+  for (int e = 0; e < ND; ++e) {  // dword e: weights 4e .. 4e + 3 of the thread's run
     const uint32_t q = ((L[e] >> lshift) & lmask) | (__builtin_amdgcn_alignbit(H[e], H[e], hrot) & hmask);
-    const float sv = dsc[e >> 2], nb = e < 4 ? nb0 : nb1;
+    const float sv = dsc[e >> 2], nb = nbs[e >> 2];
     out[2 * e] = pack_bf16x2(__builtin_fmaf(sv, ubyte_f32(q, 0), nb), __builtin_fmaf(sv, ubyte_f32(q, 1), nb));
     out[2 * e + 1] = pack_bf16x2(__builtin_fmaf(sv, ubyte_f32(q, 2), nb), __builtin_fmaf(sv, ubyte_f32(q, 3), nb));
   }
@@ -575,7 +583,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_planes(const uint8_t* __restric
   // Loads past the last step re-read the last step (results unused).
   auto load_w = [&](int s, PlaneFill<FMT>& r) {
     const int sc = min(s, s_end - 1);
-    plane_fill_load<FMT>(f_base + static_cast<size_t>(sc >> 2) * BB, sc & 3, f_hh, r);
+    plane_fill_load<FMT>(f_base + static_cast<size_t>(sc >> 2) * BB, sc & 3, f_hh, 0, r);
   };
   auto load_x = [&](int s, uint4 (&xr)[TI][4]) {
     const int sc = min(s, s_end - 1);
@@ -588,7 +596,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_planes(const uint8_t* __restric
   };
   auto store_w = [&](int buf, int s, const PlaneFill<FMT>& r) {
     uint32_t v[16];
-    plane_fill_decode<FMT>(r, s & 3, f_hh, v);
+    plane_fill_decode<FMT>(r, s & 3, f_hh, 0, v);
     uint16_t* dst = &ws[buf][f_row * kPLds + 32 * f_hh];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -670,6 +678,261 @@ __global__ __launch_bounds__(256) void k_zero_planes(float* __restrict__ y, size
   }
 }
 
+// ------------------------------------------------- GEMM, operands staged in LDS
+// The tile kernel above issues, per thread and 64-k step, about 22 dword
+// loads of its row's fields and 4 X loads that touch each 128-byte line of
+// X twice: counters at m = 512, n = k = 4096 (Q6_K) show the texture
+// addresser busy 67% of the time and 0.09 L2 requests per clock per CU,
+// i.e. the launch is bound by its memory instructions.  Here both operands
+// reach LDS by direct 16-byte copies, and the tile fill reads its fields
+// from LDS:
+//   * X: per 64-k step the tile's 128 rows x 128 bytes (16 copies, 4 per
+//     wave) into a 3-slot ring, two steps ahead, rows XOR-swizzled by 16-byte
+//     chunk (lds_copy.h) so a fragment read is conflict-free.
+//   * weights: per super-block each of the 128 rows' record as the U 16-byte
+//     units from the 16-byte boundary at or below its start (Q6_K: 14, Q3_K:
+//     8), into a 2-slot ring, copied at the last step of the super-block
+//     before the one that needs it.  Unit u of row r lands at LDS unit
+//     PITCH r + u of the slot (PITCH = U + 1, odd, so the rows a wave's fill
+//     reads at once fall in different banks; with PITCH = U the 128-byte
+//     rows of Q3_K all but shared their banks: 79 against 51 us at m = 512,
+//     n = k = 4096 with four waves), so a record keeps its address mod 16
+//     and its fields are read as in global memory.  Every wave issues the same number
+//     of copies; the pad unit of each row and the lanes past the last row
+//     re-read a unit of the matrix into LDS that no fill reads.  A unit past
+//     the 16-byte boundary at or above the record's end re-reads the one
+//     before it, so no copy leaves the matrix, whose byte size must be a
+//     multiple of 16 (the launcher checks).
+//   * eight waves, two per SIMD, so that one wave's fill arithmetic and LDS
+//     waits run beside the other's MFMAs: the fill (thread t: row t / 4, the
+//     16 weights 16 (t % 4) .. +15 of the step) decodes step s + 1 into the
+//     other bf16 tile during step s, with the arithmetic above, and wave w
+//     runs step s's MFMAs for rows 32 (w % 4) .. +31 and columns
+//     64 (w / 4) .. +63 (four waves, one per SIMD, each filling 32 weights
+//     and running all 128 columns: 10% slower).
+//   * where the time goes (m = 512, n = k = 4096, Q6_K, 51 us; timing-only
+//     copies of the kernel): the copies and barriers alone with the zero
+//     fill and the split-K atomics take 34 us, of which the atomics about 8
+//     and the zero fill 5.6; the fill adds about 12 us and the MFMAs about
+//     10, with little overlap (separate copy-only waves did not change it).
+//   * waits: at the end of step s the copies of X(s + 1) (issued at step
+//     s - 1) and everything before them have landed; the weight copies of a
+//     super-block are older than the X copies of the step before its first
+//     fill, so one count per phase covers both.
+template <int FMT>
+struct PlaneStage {
+  static constexpr int BB = Planes<FMT>::Bytes;
+  static constexpr int U = FMT == 6 ? 14 : 8;  // 16-byte units per row and super-block
+  static constexpr int PITCH = U + 1;          // LDS units per row
+  static constexpr int Waves = 8, Threads = 64 * Waves;
+  static constexpr int WC = (kPBN * PITCH + 64 * Waves - 1) / (64 * Waves);  // weight copies per wave per super-block
+  static constexpr int XC = kPBN * 128 / 1024 / Waves;  // X copies per wave per step
+  static constexpr int XSlots = 3, WSlots = 2;
+  static constexpr int XSlot = kPBN * 128;
+  static constexpr int WSlot = WC * Waves * 1024;  // every copy's 1 KiB, the rows' PITCH units first
+  static constexpr int TOff = XSlots * XSlot + WSlots * WSlot;
+  static constexpr int TSlot = kPBN * kPLds * 2;
+  static constexpr int Lds = TOff + 2 * TSlot;
+  static_assert((BB + 14 + 15) / 16 <= U, "U units cover a record at any 16-byte offset");
+  static_assert(WC * Waves * 64 >= kPBN * PITCH, "the weight copies of a super-block cover the tile");
+  static_assert(XC * Waves * 1024 == kPBN * 128, "the X copies of a step cover the tile");
+  static_assert(Lds <= 160 * 1024, "LDS budget of one workgroup");
+};
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int FMT>
+__global__ __launch_bounds__(512, 1) void k_gemm_planes_lds(const uint8_t* __restrict__ w,
+                                                            const uint16_t* __restrict__ x,
+                                                            float* __restrict__ y, int m, int n,
+                                                            int k, int sb_per_split,
+                                                            int atomic_out) {
+  using P = PlaneStage<FMT>;
+  typedef float f16v_t __attribute__((ext_vector_type(16)));
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[P::Lds];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int half = lane >> 5;
+  const int c32 = lane & 31;
+  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * kPBN;
+  const int nb = k >> 8;
+  const int sb0 = blockIdx.z * sb_per_split;
+  const int nsb = min(nb, sb0 + sb_per_split) - sb0;
+  if (nsb <= 0) return;  // uniform over the workgroup, before any barrier
+  const int nst = 4 * nsb;
+  const size_t row_bytes = static_cast<size_t>(nb) * P::BB;
+
+  // X copy q of this wave: tile rows 8 (XC wave + q) .. +7, lane -> (row lane
+  // / 8, LDS chunk lane % 8) holding global chunk (lane % 8) ^ swz(row).  Rows
+  // past m re-read row m - 1 (not stored).
+  const uint16_t* xsrc[P::XC];
+#pragma unroll
+  for (int q = 0; q < P::XC; ++q) {
+    const int row = 8 * (P::XC * wave + q) + (lane >> 3);
+    xsrc[q] = x + static_cast<size_t>(min(m0 + row, m - 1)) * k + 256 * static_cast<size_t>(sb0) +
+              8 * ((lane & 7) ^ swz(row));
+  }
+  // Weight copy i of this wave: LDS unit Ui = 64 (WC wave + i) + lane of the
+  // slot = unit Ui % PITCH of tile row Ui / PITCH (rows past n re-read row
+  // n - 1; the pad unit and the rows past the tile re-read a unit of a
+  // record, clamped below).
+  const uint8_t* wsrc[P::WC];
+  uint32_t wunit[P::WC];
+#pragma unroll
+  for (int i = 0; i < P::WC; ++i) {
+    const int ui = 64 * (P::WC * wave + i) + lane;
+    const int r = ui / P::PITCH;
+    wunit[i] = static_cast<uint32_t>(ui - r * P::PITCH);
+    wsrc[i] = w + static_cast<size_t>(min(n0 + r, n - 1)) * row_bytes +
+              static_cast<size_t>(sb0) * P::BB;
+  }
+  const uint32_t lds0 = lds_address(smem);
+  // Steps and super-blocks past the end re-read the last one (into slots no
+  // later step reads).
+  auto copy_x = [&](int s) {
+    const int sc = min(s, nst - 1);
+    const uint32_t slot = lds0 + (s % P::XSlots) * P::XSlot;
+#pragma unroll
+    for (int q = 0; q < P::XC; ++q)
+      copy16_to_lds(xsrc[q] + static_cast<size_t>(sc) * kPBK,
+                    __builtin_amdgcn_readfirstlane(slot + (P::XC * wave + q) * 1024));
+  };
+  auto copy_w = [&](int S) {
+    const int sc = min(S, nsb - 1);
+    const uint32_t slot = lds0 + P::XSlots * P::XSlot + (S % P::WSlots) * P::WSlot;
+#pragma unroll
+    for (int i = 0; i < P::WC; ++i) {
+      const uintptr_t rec = reinterpret_cast<uintptr_t>(wsrc[i]) + static_cast<uintptr_t>(sc) * P::BB;
+      const uintptr_t last = ((rec + P::BB + 15) & ~static_cast<uintptr_t>(15)) - 16;
+      uintptr_t a = (rec & ~static_cast<uintptr_t>(15)) + 16 * wunit[i];
+      a = a < last ? a : last;
+      copy16_to_lds(reinterpret_cast<const void*>(a),
+                    __builtin_amdgcn_readfirstlane(slot + (P::WC * wave + i) * 1024));
+    }
+  };
+
+  // Fill thread: row t / 4, weights 32 f_hh + 16 part + (0..15) of a step.
+  const int f_row = t >> 2, f_hh = (t >> 1) & 1, part = t & 1;
+  const uint32_t f_mis = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>(w + static_cast<size_t>(min(n0 + f_row, n - 1)) * row_bytes +
+                                  static_cast<size_t>(sb0) * P::BB) & 15u);
+  auto fill = [&](int s) {
+    const int S = s >> 2, sp = s & 3;
+    const uint32_t off = (f_mis + static_cast<uint32_t>(S * P::BB)) & 15u;
+    const uint8_t* blk = smem + P::XSlots * P::XSlot + (S % P::WSlots) * P::WSlot +
+                         f_row * (P::PITCH * 16) + off;
+    PlaneFill<FMT, 4> r;
+    plane_fill_load<FMT, 4>(blk, sp, f_hh, part, r);
+    uint32_t v[8];
+    plane_fill_decode<FMT, 4>(r, sp, f_hh, part, v);
+    uint16_t* dst = reinterpret_cast<uint16_t*>(smem + P::TOff + (s & 1) * P::TSlot) +
+                    f_row * kPLds + 32 * f_hh + 16 * part;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<uint4*>(dst + 8 * q) =
+          make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  };
+
+  const int wm = wave & 3, wn = wave >> 2;
+  f16v_t acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+  // Wave: tile rows 32 wm .. +31, columns 64 wn .. +63.  Lane half h takes
+  // k = 32 h + 8 kk + (0..7) of the step in slice kk, for X and weights alike.
+  auto mfma_step = [&](int s) {
+    const uint8_t* xb = smem + (s % P::XSlots) * P::XSlot;
+    const uint16_t* tb = reinterpret_cast<const uint16_t*>(smem + P::TOff + (s & 1) * P::TSlot);
+    const int xr = 32 * wm + c32;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8_t a =
+          *reinterpret_cast<const bf16x8_t*>(xb + xr * 128 + (((4 * half + kk) ^ swz(xr)) << 4));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
+            tb + (64 * wn + 32 * j + c32) * kPLds + 32 * half + 8 * kk);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+      }
+    }
+  };
+
+  // Prologue: W(0), X(0), X(1), W(1); W(0) and X(0) land; step 0 is filled.
+  copy_w(0);
+  copy_x(0);
+  copy_x(1);
+  copy_w(1);
+  wait_copies_barrier<P::XC + P::WC>();
+  fill(0);
+  lds_barrier();
+  // Step s (phase p = s % 4 of its super-block): X(s + 2) into the slot of
+  // step s - 1, at phase 3 the weights of super-block S + 2 into the slot of
+  // S; fill step s + 1; MFMAs of step s.  Younger than X(s + 1) at the end:
+  // this step's X copies, and the weight copies of a phase-3 step (this one
+  // at p = 3, the one before at p = 0).
+  auto step = [&](int s, int p) {
+    copy_x(s + 2);
+    if (p == 3) copy_w((s >> 2) + 2);
+    if (s + 1 < nst) fill(s + 1);
+    mfma_step(s);
+    if (p == 0 || p == 3)
+      wait_copies_barrier<P::XC + P::WC>();
+    else
+      wait_copies_barrier<P::XC>();
+  };
+  for (int s = 0; s < nst; s += 4) {
+    step(s, 0);
+    step(s + 1, 1);
+    step(s + 2, 2);
+    step(s + 3, 3);
+  }
+  wait_copies<0>();  // the re-read copies past the end land before the LDS is released
+
+  // Accumulator r of a 32x32 tile holds row 8 (r / 4) + 4 half + r % 4, column lane % 32.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + 64 * wn + 32 * j + c32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + 32 * wm + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (row < m && col < n) {
+        float* dst = y + static_cast<size_t>(row) * n + col;
+        if (atomic_out)
+          unsafeAtomicAdd(dst, acc[j][r]);
+        else
+          *dst = acc[j][r];
+      }
+    }
+  }
+}
+
+template <int FMT>
+hipError_t launch_gemm_planes_staged(const uint8_t* w, const uint16_t* x, float* y, int m, int n,
+                                     int k, hipStream_t stream) {
+  const int tiles_m = (m + 127) / 128, tiles_n = (n + kPBN - 1) / kPBN;
+  const int nb = k / 256;
+  // Split K (whole super-blocks) until the grid reaches one workgroup per CU.
+  int splits = 1;
+  while (tiles_m * tiles_n * splits * 2 <= 256 && splits * 2 <= nb / 2) splits *= 2;
+  const int per = (nb + splits - 1) / splits;
+  splits = (nb + per - 1) / per;
+  if (splits > 1) {
+    const size_t count = static_cast<size_t>(m) * n;
+    hipLaunchKernelGGL(k_zero_planes, dim3(static_cast<unsigned>((count / 4 + 256) / 256)), dim3(256),
+                       0, stream, y, count);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_gemm_planes_lds<FMT>), dim3(tiles_n, tiles_m, splits),
+                     dim3(PlaneStage<FMT>::Threads), 0,
+                     stream, w, x, y, m, n, k, per, splits > 1 ? 1 : 0);
+  return hipGetLastError();
+}
+
 template <int FMT, int WAVES_M, int WAVES_N, int TI, int TJ>
 hipError_t launch_gemm_planes_tiles(const uint8_t* w, const uint16_t* x, float* y, int m, int n,
                                     int k, hipStream_t stream) {
@@ -698,6 +961,11 @@ hipError_t launch_gemm_planes(const uint8_t* w, const uint16_t* x, float* y, int
                               int64_t k, hipStream_t stream) {
   const int mi = static_cast<int>(m), ni = static_cast<int>(n), ki = static_cast<int>(k);
   if (mi <= 32) return launch_gemm_planes_tiles<FMT, 1, 4, 1, 1>(w, x, y, mi, ni, ki, stream);
+  // The staged kernel's weight copies round each record out to 16-byte
+  // boundaries, which stay inside the matrix when its byte size is a
+  // multiple of 16.
+  if ((n * (k / 256) * Planes<FMT>::Bytes) % 16 == 0)
+    return launch_gemm_planes_staged<FMT>(w, x, y, mi, ni, ki, stream);
   return launch_gemm_planes_tiles<FMT, 4, 1, 1, 4>(w, x, y, mi, ni, ki, stream);
 }
 

@@ -29,8 +29,9 @@ CASES = [
     ("k_gemm_q4k_stream<1, 8>", 448 * 256, 57344, "", "sweep_gemm_14336x4096"),
     ("k_gemm_q4k_stream<2, 32>", 224 * 256, 155648, "", "sweep_gemm_14336x4096"),
     ("k_gemm_q4k_128x256", 57344, 155648, "", "gemm_512x14336x4096"),
+    ("k_gemm_planes_lds<6>", 32 * 4 * 2 * 512, 151552, "", "q6k_gemm_512x4096x4096"),
+    ("k_gemm_planes_lds<3>", 32 * 4 * 2 * 512, 135168, "", "q3k_gemm_512x4096x4096"),
     ("k_gemm_planes<6, 4, 1, 1, 4>", 128 * 2 * 256, 36864, "", "q6k_gemm_512x4096x4096"),
-    ("k_gemm_planes<3, 4, 1, 1, 4>", 128 * 2 * 256, 36864, "", "q3k_gemm_512x4096x4096"),
     ("k_gemv_planes<6, 8, 2, 1>", 4096 // 16 * 512, 16384, "", "q6k_gemv_4096x4096"),
     ("k_gemv_planes_lds<6, 4, 1, 1>", 4096 // 4 * 256, 32768, "", "q6k_gemv_4096x4096"),
     ("k_gemv_planes_lds<3, 4, 1, 1>", 4096 // 4 * 256, 24576, "", "q3k_gemv_4096x4096"),

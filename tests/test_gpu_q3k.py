@@ -114,9 +114,12 @@ def _dev_bf16(bits):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 128, 256), (8, 520, 1024), (32, 384, 768), (64, 200, 512),
-                                   (130, 257, 1280)])
+                                   (130, 257, 1280), (130, 264, 1280), (300, 136, 2048)])
 def test_q3k_gemm_full_output(q4k, m, n, k):
-    # split-K grids (small tiles) and full ones, ragged tiles, odd block counts per row
+    # split-K grids (small tiles) and full ones, ragged tiles, odd block counts per row; for m > 32
+    # the operands go through LDS by copies when n * k / 256 is a multiple of 8 (64 x 200, 130 x
+    # 264 with 5 super-blocks split 3 + 2, 300 x 136 split four ways), else the tile kernel loads
+    # them (130 x 257)
     w = synth.q3k_weights(n, k, seed=m + n)
     xb = synth.normal_bf16((m, k), seed=m + n)
     y = q4k.q3k_gemm(dev(w), _dev_bf16(xb)).cpu().numpy()

@@ -279,7 +279,8 @@ def test_q5k_gemm_structured(q4k, m, n, k):
 
 
 @pytest.mark.parametrize("fmt,m,n,k", [("q6k", 1, 100, 1024), ("q6k", 64, 257, 768),
-                                       ("q3k", 1, 100, 1024), ("q3k", 64, 257, 768)])
+                                       ("q6k", 64, 264, 768), ("q3k", 1, 100, 1024),
+                                       ("q3k", 64, 257, 768), ("q3k", 64, 264, 768)])
 def test_plane_gemm_structured(q4k, fmt, m, n, k):
     kinds = q6k_kinds() if fmt == "q6k" else q3k_kinds()
     w = tile(kinds, n, k, seed=m + n)
