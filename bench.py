@@ -542,8 +542,9 @@ def main():
     if mlp:
         out["roofline_mlp"] = {"bound": "hbm", "achieved": mlp["gbs"], "peak": HBM_PEAK_GBS,
                                "unit": "GB/s", "frac": mlp["hbm_frac"],
-                               "kernels": "k_gemv_q4k<1, 1, true, 8, false, 4> (gate/up + SwiGLU), "
-                                          "k_gemv_q4k<1, 1, false, 16, false, 4> (down)",
+                               "traffic": mlp_traffic(),
+                               "kernels": "k_gemv_decode<8, 1, true, 4> (gate/up + SwiGLU), "
+                                          "k_gemv_decode<8, 4, false, 4> (down)",
                                "bytes_per_launch": 3 * q4k_bytes(D_FF, D_MODEL) + 4 * D_MODEL
                                + 2 * 4 * D_FF + 4 * D_MODEL, **timing(mlp)}
     if w8:
@@ -615,6 +616,13 @@ def traffic(name):
         except (OSError, ValueError):
             continue
     return None
+
+
+def mlp_traffic():
+    """The SwiGLU MLP's HBM bytes per call: its two launches' counter figures added, or None."""
+    parts = [traffic("swiglu_mlp_gateup_%dx%d" % (D_FF, D_MODEL)),
+             traffic("swiglu_mlp_down_%dx%d" % (D_MODEL, D_FF))]
+    return None if None in parts else sum(parts)
 
 
 def _template_args(name, kernel):
