@@ -169,8 +169,11 @@ def test_graph_sibling_formats_and_w8a8_replay(q4k):
                          ("q3k", synth.q3k_weights, q4k.q3k_dequantize_f32)):
         w = dev(gen(256, 512, seed=3))
         add("%s dequant" % fmt, lambda w=w, dq=dq: [dq(w)])
-    x8, xs, w8, ws, b = (dev(a) for a in synth.w8a8_case(256, 512, 1024, seed=5))
-    add("w8a8_linear", lambda: [q4k.w8a8_linear(x8, xs, w8, ws, b)])
+    # the INT8 layer's tile shapes: 64 x 64, 64 x 192 (three-slot ring), 128 x 192
+    for m8, n8, k8 in ((256, 512, 1024), (1030, 3072, 256), (2200, 1920, 256)):
+        x8, xs, w8, ws, b = (dev(a) for a in synth.w8a8_case(m8, n8, k8, seed=5))
+        add("w8a8_linear %dx%dx%d" % (m8, n8, k8),
+            lambda x8=x8, xs=xs, w8=w8, ws=ws, b=b: [q4k.w8a8_linear(x8, xs, w8, ws, b)])
     xq = dev_bf16(synth.normal_bf16((64, 1024), seed=5))
     add("w8a8_quantize_rows", lambda: list(q4k.w8a8_quantize_rows(xq)))
 
