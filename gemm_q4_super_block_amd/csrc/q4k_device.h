@@ -198,23 +198,27 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// Sum of a float over the 64 lanes of a wave (every lane gets the total).
-// Within a row of 16 lanes: DPP quad_perm xor-1 and xor-2, then row_ror 4
-// and 8; across the four rows: two lane swizzles through the LDS crossbar.
-template <int kCtrl>
+// Sum of a float over the 64 lanes of a wave (every lane gets the total; all
+// 64 lanes must be active).  Within a row of 16 lanes: DPP quad_perm xor-1 and
+// xor-2, then row_ror 4 and 8; across the four rows: two DPP row broadcasts,
+// then lane 63's total is read into every lane (the two lane swizzles through
+// the LDS crossbar this replaces cost two LDS round trips and their lane
+// arithmetic per sum).
+template <int kCtrl, int kRowMask = 0xF>
 __device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                               kRowMask, 0xF, false));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
   v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
   v += dpp_mov<0x124>(v);  // row_ror 4
-  v += dpp_mov<0x128>(v);  // row_ror 8
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  v += dpp_mov<0x128>(v);  // row_ror 8: every lane holds its row's sum
+  v += dpp_mov<0x142, 0xA>(v);  // row_bcast 15: rows 1 and 3 add the last lane of rows 0 and 2
+  v += dpp_mov<0x143, 0xC>(v);  // row_bcast 31: rows 2 and 3 add lane 31 (rows 0 + 1)
+  // Lane 63 holds (row 3 + row 2) + (row 1 + row 0); every lane returns it.
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 }  // namespace q4k
