@@ -1,4 +1,4 @@
-"""A Q4_K weight matrix larger than 4 GiB through the GEMV and GEMM kernels.
+"""Q4_K and Q6_K weight matrices larger than 4 GiB through the GEMV and GEMM kernels.
 
 The pages warn of 32-bit offsets on large tensors ("Writing an ESIMD Fused
 Kernel From Reverse-Engineered Assembly", "The ABI Adapter and the int32
@@ -69,5 +69,60 @@ def test_gemm_rows_past_4gib(big, m):
     xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
     y = lib.gemm(wd, xt).cpu().numpy()
     yr, a = oracle.gemm_cols(base, xb, PERIOD, K, rows % PERIOD)
+    err = np.abs(y[:, rows] - yr)
+    assert np.all(err <= 1e-2 * a), "worst %g" % (err / (1e-2 * a)).max()
+
+
+# ---- Q6_K (210-byte records) past 4 GiB: the plane GEMV and the plane GEMM whose operands
+# are copied into LDS (the copies' 16-byte-aligned record spans, row pointers in 64 bits).
+N6 = 1_300_000
+ROW_BYTES_6 = K // 256 * 210
+FIRST_ROW_PAST_4G_6 = (1 << 32) // ROW_BYTES_6 + 1
+
+
+@pytest.fixture(scope="module")
+def big6():
+    if torch.cuda.device_count() == 0:
+        pytest.skip("no GPU")
+    import gemm_q4_super_block_amd as lib
+    lib.load_library()
+    torch.cuda.set_device(0)
+    base = synth.q6k_weights(PERIOD, K, seed=12)
+    wd = torch.empty((N6, ROW_BYTES_6), dtype=torch.uint8, device="cuda")
+    bd = torch.from_numpy(base).cuda()
+    for r0 in range(0, N6, PERIOD):
+        r1 = min(N6, r0 + PERIOD)
+        wd[r0:r1].copy_(bd[: r1 - r0])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, FIRST_ROW_PAST_4G_6 - 1, FIRST_ROW_PAST_4G_6, N6 - 1],
+                                     np.random.default_rng(6).integers(FIRST_ROW_PAST_4G_6, N6, 12)]))
+    yield lib, wd, base, rows
+    del wd, bd
+    torch.cuda.empty_cache()
+
+
+def test_q6k_matrix_is_past_4gib(big6):
+    _, wd, _, _ = big6
+    assert wd.numel() > (1 << 32)
+    assert FIRST_ROW_PAST_4G_6 * ROW_BYTES_6 >= (1 << 32) > (FIRST_ROW_PAST_4G_6 - 1) * ROW_BYTES_6
+    assert (N6 * (K // 256)) % 8 == 0  # the GEMM takes the LDS-staged kernel
+
+
+def test_q6k_gemv_rows_past_4gib(big6):
+    lib, wd, base, rows = big6
+    x = synth.normal_f32((1, K), seed=21)
+    y = lib.q6k_gemv(wd, torch.from_numpy(x).cuda()).cpu().numpy().reshape(1, -1)
+    yr, a = oracle.q6k_gemv_rows(base, x, PERIOD, K, rows % PERIOD)
+    err = np.abs(y[:, rows] - yr)
+    assert np.all(err <= 1e-4 * a), "worst %g" % (err / (1e-4 * a)).max()
+
+
+def test_q6k_gemm_rows_past_4gib(big6):
+    lib, wd, base, rows = big6
+    m = 64
+    xb = synth.normal_bf16((m, K), seed=22)
+    xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    y = lib.q6k_gemm(wd, xt).cpu().numpy()
+    yr, a = oracle.q6k_gemm_cols(base, xb, PERIOD, K, rows % PERIOD)
     err = np.abs(y[:, rows] - yr)
     assert np.all(err <= 1e-2 * a), "worst %g" % (err / (1e-2 * a)).max()
