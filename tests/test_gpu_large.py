@@ -1,4 +1,4 @@
-"""Q4_K and Q6_K weight matrices larger than 4 GiB through the GEMV and GEMM kernels.
+"""Q4_K, Q6_K and int8 weight matrices larger than 4 GiB through the GEMV and GEMM kernels.
 
 The pages warn of 32-bit offsets on large tensors ("Writing an ESIMD Fused
 Kernel From Reverse-Engineered Assembly", "The ABI Adapter and the int32
@@ -126,3 +126,34 @@ def test_q6k_gemm_rows_past_4gib(big6):
     yr, a = oracle.q6k_gemm_cols(base, xb, PERIOD, K, rows % PERIOD)
     err = np.abs(y[:, rows] - yr)
     assert np.all(err <= 1e-2 * a), "worst %g" % (err / (1e-2 * a)).max()
+
+
+# ---- INT8 W8A8 weights past 4 GiB (int8 [n, k], the 128 x 192 tiles), bit for bit.
+N8 = 1_105_920  # a multiple of 128 and of 192
+FIRST_ROW_PAST_4G_8 = (1 << 32) // K + 1
+
+
+def test_w8a8_rows_past_4gib():
+    if torch.cuda.device_count() == 0:
+        pytest.skip("no GPU")
+    import gemm_q4_super_block_amd as lib
+    lib.load_library()
+    torch.cuda.set_device(0)
+    m = 64
+    x, xs, w, ws, b = synth.w8a8_case(m, PERIOD, K, seed=13)
+    wd = torch.empty((N8, K), dtype=torch.int8, device="cuda")
+    bd = torch.from_numpy(w).cuda()
+    for r0 in range(0, N8, PERIOD):
+        r1 = min(N8, r0 + PERIOD)
+        wd[r0:r1].copy_(bd[: r1 - r0])
+    assert wd.numel() > (1 << 32)
+    wsd = torch.from_numpy(np.resize(ws, N8)).cuda()
+    b_d = torch.from_numpy(np.resize(b, N8)).cuda()
+    y = lib.w8a8_linear(torch.from_numpy(x).cuda(), torch.from_numpy(xs).cuda(), wd, wsd, b_d)
+    rows = np.unique(np.concatenate([[0, FIRST_ROW_PAST_4G_8 - 1, FIRST_ROW_PAST_4G_8, N8 - 1],
+                                     np.random.default_rng(8).integers(FIRST_ROW_PAST_4G_8, N8, 12)]))
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)[:, rows]
+    ref = oracle.w8a8_linear_cols(x, xs, w, ws, b, rows % PERIOD)
+    del wd, bd, wsd, b_d, y
+    torch.cuda.empty_cache()
+    assert np.array_equal(got, ref), "%d of %d outputs differ" % ((got != ref).sum(), got.size)
