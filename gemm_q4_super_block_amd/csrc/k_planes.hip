@@ -686,7 +686,7 @@ __global__ __launch_bounds__(256) void k_zero_planes(float* __restrict__ y, size
 // i.e. the launch is bound by its memory instructions.  Here both operands
 // reach LDS by direct 16-byte copies, and the tile fill reads its fields
 // from LDS:
-//   * X: per 64-k step the tile's 128 rows x 128 bytes (16 copies, 4 per
+//   * X: per 64-k step the tile's 128 rows x 128 bytes (16 copies, 2 per
 //     wave) into a 3-slot ring, two steps ahead, rows XOR-swizzled by 16-byte
 //     chunk (lds_copy.h) so a fragment read is conflict-free.
 //   * weights: per super-block each of the 128 rows' record as the U 16-byte
@@ -697,12 +697,12 @@ __global__ __launch_bounds__(256) void k_zero_planes(float* __restrict__ y, size
 //     reads at once fall in different banks; with PITCH = U the 128-byte
 //     rows of Q3_K all but shared their banks: 79 against 51 us at m = 512,
 //     n = k = 4096 with four waves), so a record keeps its address mod 16
-//     and its fields are read as in global memory.  Every wave issues the same number
-//     of copies; the pad unit of each row and the lanes past the last row
-//     re-read a unit of the matrix into LDS that no fill reads.  A unit past
-//     the 16-byte boundary at or above the record's end re-reads the one
-//     before it, so no copy leaves the matrix, whose byte size must be a
-//     multiple of 16 (the launcher checks).
+//     and its fields are read as in global memory.  Every wave issues the
+//     same number of copies; the pad unit of each row and the lanes past the
+//     last row re-read a unit of the matrix into LDS that no fill reads.  A
+//     unit past the 16-byte boundary at or above the record's end re-reads
+//     the one before it, so no copy leaves the matrix, whose byte size must
+//     be a multiple of 16 (the launcher checks).
 //   * eight waves, two per SIMD, so that one wave's fill arithmetic and LDS
 //     waits run beside the other's MFMAs: the fill (thread t: row t / 4, the
 //     16 weights 16 (t % 4) .. +15 of the step) decodes step s + 1 into the
