@@ -527,17 +527,29 @@ __device__ __forceinline__ void plane_fill_decode(const PlaneFill<FMT, ND>& r, i
   constexpr uint32_t hmask = FMT == 6 ? 0x30303030u : 0x04040404u;
   // (d sc) (q - OFF) = fma(d sc, q, -(d sc) OFF): OFF is a power of two, so
   // (d sc) OFF is exact and the FMA rounds the exact weight once, as the
-  // subtract-then-multiply form does.
+  // subtract-then-multiply form does.  Q3_K's quants (0..7) are widened two
+  // at a time as fp8 bytes (q 2^-9 exactly), with 2^9 folded into d sc.
   const float off = Planes<FMT>::Off;
-  float nbs[NCB];
+  float svs[NCB], nbs[NCB];
 #pragma unroll
-  for (int c = 0; c < NCB; ++c) nbs[c] = -(dsc[c] * off);
+  for (int c = 0; c < NCB; ++c) {
+    nbs[c] = -(dsc[c] * off);
+    svs[c] = FMT == 3 ? dsc[c] * kNibbleUnscale : dsc[c];
+  }
 #pragma unroll
   for (int e = 0; e < ND; ++e) {  // dword e: weights 4e .. 4e + 3 of the thread's run
     const uint32_t q = ((L[e] >> lshift) & lmask) | (__builtin_amdgcn_alignbit(H[e], H[e], hrot) & hmask);
-    const float sv = dsc[e >> 2], nb = nbs[e >> 2];
-    out[2 * e] = pack_bf16x2(__builtin_fmaf(sv, ubyte_f32(q, 0), nb), __builtin_fmaf(sv, ubyte_f32(q, 1), nb));
-    out[2 * e + 1] = pack_bf16x2(__builtin_fmaf(sv, ubyte_f32(q, 2), nb), __builtin_fmaf(sv, ubyte_f32(q, 3), nb));
+    const float sv = svs[e >> 2], nb = nbs[e >> 2];
+    f2_t q01, q23;
+    if constexpr (FMT == 3) {
+      q01 = fp8x2_lo(q);
+      q23 = fp8x2_hi(q);
+    } else {
+      q01 = f2_t{ubyte_f32(q, 0), ubyte_f32(q, 1)};
+      q23 = f2_t{ubyte_f32(q, 2), ubyte_f32(q, 3)};
+    }
+    out[2 * e] = pack_bf16x2(__builtin_fmaf(sv, q01.x, nb), __builtin_fmaf(sv, q01.y, nb));
+    out[2 * e + 1] = pack_bf16x2(__builtin_fmaf(sv, q23.x, nb), __builtin_fmaf(sv, q23.y, nb));
   }
 }
 
